@@ -1,0 +1,116 @@
+"""Pins for oracle/moe.py (CPU only): packing against a brute-force bucket
+sort, the GEMM against an exact rational triple loop and against the dense
+product of the compensated activation (Eq. (6) applied to X~ of Eq. (21)),
+SwiGLU against scipy's logistic function, combine against a loop."""
+
+from fractions import Fraction
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import synth
+from oracle import formats as F
+from oracle import moe as M
+from oracle import nvfp4 as Q
+from oracle import rac as R
+
+
+def test_pack_bruteforce():
+    rng = np.random.default_rng(0)
+    for t, e, topk in [(5, 3, 2), (37, 16, 4), (64, 128, 8), (1, 1, 1)]:
+        ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+        off, row_token, pos = M.pack_routes(ids, e)
+        buckets = [[] for _ in range(e)]
+        for tt in range(t):
+            for s in range(topk):
+                buckets[ids[tt, s]].append((tt, s))
+        flat = [p for b in buckets for p in b]
+        assert list(off) == list(np.cumsum([0] + [len(b) for b in buckets]))
+        assert list(row_token) == [tt for tt, _ in flat]
+        for p, (tt, s) in enumerate(flat):
+            assert pos[tt * topk + s] == p
+    # empty experts and all-to-one routing
+    off, row_token, pos = M.pack_routes(np.zeros((4, 1), np.int32), 3)
+    assert list(off) == [0, 4, 4, 4] and list(row_token) == [0, 1, 2, 3]
+
+
+def _tiny_problem(seed, rows_a, k_dim, n, e, k, routing_rows):
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((rows_a, k_dim)).astype(np.float32))
+    out = R.rac_quantize(F.bf16_to_f64(x), k)
+    w = synth.weights(rng, e, n, k_dim, std=0.5)
+    wp, ws, wt, _ = Q.weight_qdq(w)
+    return x, out, (wp, ws, wt)
+
+
+def test_gemm_dense_exact_rational_triple_loop():
+    x, out, w = _tiny_problem(1, 3, 32, 4, 1, 16, None)
+    a = (out["nib"], out["scale"], out["ts"])
+    r = (out["r_nib"], out["r_scale"], out["r_ts"])
+    y, bound = M.grouped_gemm(a, r, out["sel"], w, [0, 3])
+    ad = Q.dequantize(*a)
+    rd = Q.dequantize(*r)
+    wd = Q.dequantize(w[0][0], w[1][0], w[2][0])
+    for p in range(3):
+        for nn in range(4):
+            acc = sum(Fraction(float(ad[p, j])) * Fraction(float(wd[nn, j])) for j in range(32))
+            acc += sum(Fraction(float(rd[p, i])) * Fraction(float(wd[nn, out["sel"][i]]))
+                       for i in range(16))
+            assert abs(Fraction(float(y[p, nn])) - acc) <= abs(acc) * Fraction(1, 2 ** 50)
+
+
+def test_gemm_equals_product_of_compensated_activation():
+    """Eq. (21) then Eq. (6): W X~ computed densely equals the split formula."""
+    x, out, w = _tiny_problem(2, 24, 64, 12, 1, 16, None)
+    a = (out["nib"], out["scale"], out["ts"])
+    r = (out["r_nib"], out["r_scale"], out["r_ts"])
+    y, bound = M.grouped_gemm(a, r, out["sel"], w, [0, 24])
+    xt = R.compensated(out, 64)
+    wd = Q.dequantize(w[0][0], w[1][0], w[2][0])
+    ref = xt @ wd.T
+    assert np.all(np.abs(y - ref) <= 1e-13 * bound)
+    assert np.all(bound >= np.abs(y) * (1 - 1e-12))
+
+
+def test_grouped_equals_per_expert_dense():
+    rng = np.random.default_rng(3)
+    t, e, topk, h, n = 40, 5, 2, 32, 8
+    ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    off, row_token, pos = M.pack_routes(ids, e)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((t, h)).astype(np.float32))
+    out = R.rac_quantize(F.bf16_to_f64(x), 16)
+    wp, ws, wt, _ = Q.weight_qdq(synth.weights(rng, e, n, h, std=0.3))
+    a = (out["nib"], out["scale"], out["ts"])
+    r = (out["r_nib"], out["r_scale"], out["r_ts"])
+    y, bound = M.grouped_gemm(a, r, out["sel"], (wp, ws, wt), off, row_token)
+    xt = R.compensated(out, h)
+    for p in range(len(row_token)):
+        ex = int(np.searchsorted(off, p, side="right") - 1)
+        wd = Q.dequantize(wp[ex], ws[ex], wt[ex])
+        assert np.all(np.abs(y[p] - wd @ xt[row_token[p]]) <= 1e-13 * bound[p])
+
+
+def test_swiglu_against_scipy_and_torch_rounding():
+    rng = np.random.default_rng(4)
+    y1 = rng.standard_normal((7, 16)) * 4
+    h = M.swiglu(y1)
+    g, u = y1[:, :8], y1[:, 8:]
+    ref = g * expit(g) * u
+    got = F.bf16_to_f64(h)
+    ulp = np.exp2(np.floor(np.log2(np.abs(ref))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp / 2 * (1 + 1e-9))
+
+
+def test_combine_loop():
+    rng = np.random.default_rng(5)
+    t, topk, n = 6, 3, 4
+    y2 = rng.standard_normal((t * topk, n))
+    pos = rng.permutation(t * topk).astype(np.int32)
+    w = rng.random((t, topk)).astype(np.float32)
+    out = M.combine(y2, pos, w, t, topk)
+    for tt in range(t):
+        acc = np.zeros(n)
+        for s in range(topk):
+            acc = acc + np.float64(w[tt, s]) * y2[pos[tt * topk + s]]
+        assert np.array_equal(out[tt], acc)
