@@ -1,0 +1,180 @@
+/*
+ * quads.h -- C ABI of the QUADS rollout hot path on MI355X (gfx950).
+ *
+ * The method is "QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE via
+ * QUantization-error Alignment across Dual Sides" (arXiv 2607.15810): NVFP4
+ * activation quantization (section 2.2, "FP4" paragraph; Eq. (9)), Residual
+ * Activation Compensation (section 3.3, Eq. (20)-(24)) and the W4A4 product
+ * (Eq. (6), (21)), here for MoE expert layers.
+ *
+ * Conventions shared by every call
+ *  - Pointers are device pointers unless stated.  bf16 tensors are passed as
+ *    uint16_t bit patterns.  Every tensor is dense and row-major.  Every
+ *    pointer must be 16-byte aligned.
+ *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronizes with the host, allocates memory or keeps
+ *    a pointer after it returns.  Scalars produced on the device (tensor
+ *    scales, selected channels, expert offsets) stay on the device.
+ *  - Scratch memory is caller-owned: `ws` must hold at least the bytes the
+ *    matching *_ws() query returns for the same sizes (NULL is allowed when
+ *    that is 0).  Calls that share a workspace must be ordered on one stream.
+ *  - Argument checks run on the host before any launch.  A failed check
+ *    returns QUADS_EINVAL (null or misaligned pointer, bad enum),
+ *    QUADS_ESHAPE (a size rule below) or QUADS_EWORKSPACE; nothing is
+ *    launched then.  A failed launch returns QUADS_EHIP; quads_status_string
+ *    then describes the HIP error of the calling thread.
+ *  - Inputs must be finite.  Size-0 tensors (M, T or rows = 0) are a no-op
+ *    that returns QUADS_OK (tensor scales are still written as 0 where an
+ *    output scale is requested).
+ *
+ * NVFP4 layout (arXiv 2607.15810, section 2.2 "FP4")
+ *  - Element: 4-bit E2M1 code, bit 3 = sign, bits 2..0 = magnitude code
+ *    0..7 for 0, 0.5, 1, 1.5, 2, 3, 4, 6.  Two codes per byte; the even
+ *    channel is the low nibble.  `nib` of a [rows, K] tensor is [rows, K/2].
+ *  - Block scale: one OCP E4M3FN byte (max 448, section 2.2 "FP8") per 16
+ *    consecutive channels of a row; `scale` is [rows, K/16].
+ *  - Tensor scale: one fp32.  Value of an element = v * s_b * s_t.
+ *  - Quantization: s_t = RN32(max|x| / 2688); s_b = min(448, RNE_E4M3(
+ *    amax_block / (6 s_t))); code = RNE_E2M1(|x| / (s_b s_t)) saturating at
+ *    6, ties to even, sign bit copied from x; s_t = 0 or s_b = 0 give
+ *    magnitude 0.  RNE is taken on the exact real quotient.
+ */
+#ifndef QUADS_H
+#define QUADS_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    QUADS_OK = 0,
+    QUADS_EINVAL = -1,
+    QUADS_ESHAPE = -2,
+    QUADS_EWORKSPACE = -3,
+    QUADS_EHIP = -4
+} quads_status;
+
+typedef enum { QUADS_OUT_F32 = 0, QUADS_OUT_BF16 = 1 } quads_out_dtype;
+typedef enum { QUADS_EPI_NONE = 0, QUADS_EPI_SWIGLU = 1 } quads_epilogue;
+
+/* Human-readable text for a status code (thread-local detail for QUADS_EHIP). */
+const char* quads_status_string(int status);
+
+/* Library version string, e.g. "quads-mi355x 0.1 gfx950". Host pointer. */
+const char* quads_version(void);
+
+/*
+ * NVFP4 activation quantization, Q_A of Eq. (9) (section 3.1) with the
+ * format of section 2.2.
+ *   x       bf16 [M, K], K % 16 == 0
+ *   ts_in   NULL: dynamic tensor scale from max|x|;  else a device fp32 used
+ *           as s_t (must be finite and >= 0; blocks then saturate at 448 and
+ *           codes at 6)
+ *   nib     out uint8 [M, K/2];  scale out uint8 [M, K/16]
+ *   ts_out  out fp32 [1]: the tensor scale used
+ */
+size_t quads_nvfp4_quantize_ws(int64_t M, int64_t K);
+int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* ts_in,
+                         uint8_t* nib, uint8_t* scale, float* ts_out,
+                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Residual Activation Compensation (section 3.3).
+ *   x        bf16 [M, K], K % 16 == 0;  k % 16 == 0, 0 <= k <= K
+ *   nib, scale, ts    main NVFP4 of x, identical to quads_nvfp4_quantize
+ *                     with a dynamic tensor scale
+ *   sel      out int32 [k]: S of Eq. (24), the k channels with the largest
+ *            score s_j = sum_t r_tj^2 (Eq. (23) squared), ties to the lower
+ *            index, ascending.  r = RN32(x - DQ(Q(x))) is the negated error
+ *            of Eq. (20).  The sum runs in fp64 in a fixed order: tokens in
+ *            groups of 64 summed in order from +0, then those sums in groups
+ *            of 64, and so on.
+ *   r_nib, r_scale, r_ts  out: NVFP4 of the gathered residual R[t,i] =
+ *            r[t, sel[i]] ([M, k/2], [M, k/16], fp32 [1]), quantized like x
+ *            with its own dynamic tensor scale.  Then
+ *            X~ = DQ(x) + scatter_sel(DQ(R)) is Eq. (21).
+ *   score_out  NULL or out fp64 [K]: the channel scores
+ * With k == 0 no residual output is written except r_ts = 0 (r_nib,
+ * r_scale and sel may then be NULL).
+ */
+size_t quads_rac_quantize_ws(int64_t M, int64_t K, int32_t k);
+int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                       uint8_t* nib, uint8_t* scale, float* ts,
+                       int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                       double* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Shared NVFP4 weight QDQ, Q_W of Eq. (7) / QDQ_W of Eq. (12): each expert
+ * matrix W_e [N, K] (rows = output features, blocks along K) is quantized
+ * with its own dynamic tensor scale.
+ *   w       bf16 [E, N, K], K % 16 == 0, E >= 1
+ *   w_nib   out [E, N, K/2];  w_scale out [E, N, K/16];  w_ts out fp32 [E]
+ *   w_dq    NULL or out bf16 [E, N, K]: RNE_bf16 of the exact v*s_b*s_t
+ */
+size_t quads_nvfp4_weight_qdq_ws(int64_t E, int64_t N, int64_t K);
+int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                           uint8_t* w_nib, uint8_t* w_scale, float* w_ts, uint16_t* w_dq,
+                           void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Token-to-expert packing: stable counting sort of the (token, slot) pairs
+ * by expert id.  Packed order: experts ascending, then t*topk + slot
+ * ascending.
+ *   topk_ids  int32 [T, topk], every id in [0, E)
+ *   offsets   out int32 [E+1]: rows of expert e are offsets[e] .. offsets[e+1]-1
+ *   row_token out int32 [T*topk]: token feeding each packed row
+ *   pos       out int32 [T*topk]: packed row of (t, slot) at index t*topk+slot
+ */
+size_t quads_moe_pack_ws(int64_t T, int32_t topk, int32_t E);
+int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                   int32_t* offsets, int32_t* row_token, int32_t* pos,
+                   void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped W4A4 GEMM with the RAC compensation term in the same accumulator
+ * (Eq. (6) applied to X~ of Eq. (21)).  For packed row p of expert e and
+ * output feature n:
+ *   Y[p,n] = s_tA s_tW[e] sum_{j<K} a[row(p), j] w_e[n, j]
+ *          + s_tR s_tW[e] sum_{i<k} r[row(p), i] w_e[n, sel[i]]
+ * with a, r, w the exact v*s_b values (computed on bf16/fp16-exact MFMA
+ * operands, fp32 accumulation).
+ *   a_nib, a_scale, a_ts   activation NVFP4 [Ta, K/2], [Ta, K/16], fp32 [1]
+ *   row_token  NULL: row(p) = p (Ta = rows);  else int32 [rows], row(p) =
+ *              row_token[p] < Ta
+ *   r_nib, r_scale, r_ts, sel, k   second pass (quads_rac_quantize layout);
+ *              k == 0 gives plain W4A4 and these may be NULL
+ *   w_nib, w_scale, w_ts   weights [E, N, K/2], [E, N, K/16], fp32 [E]
+ *   offsets    int32 [E+1] with offsets[0] = 0, offsets[E] = rows,
+ *              non-decreasing; NULL only when E == 1 (all rows, expert 0)
+ *   epilogue   QUADS_EPI_NONE: out [rows, N];
+ *              QUADS_EPI_SWIGLU: N even, gate = features [0, N/2), up =
+ *              [N/2, N), out bf16 [rows, N/2] = RNE_bf16(silu(g) * u)
+ *   out_dtype  QUADS_OUT_F32 or QUADS_OUT_BF16 (SWIGLU requires BF16)
+ */
+size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int32_t E, int64_t N);
+int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
+                        const int32_t* row_token, int64_t rows, int64_t K,
+                        const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
+                        const int32_t* sel, int32_t k,
+                        const uint8_t* w_nib, const uint8_t* w_scale, const float* w_ts,
+                        const int32_t* offsets, int32_t E, int64_t N,
+                        int epilogue, int out_dtype, void* out,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * MoE combine: out[t, n] = sum over slots in order of topk_w[t, slot] *
+ * y[pos[t*topk + slot], n], accumulated in fp32.
+ *   y        [T*topk, N], fp32 (y_dtype QUADS_OUT_F32) or bf16 (QUADS_OUT_BF16)
+ *   topk_w   fp32 [T, topk];  out fp32 [T, N];  N % 8 == 0
+ */
+int quads_moe_combine(const void* y, int y_dtype, const int32_t* pos, const float* topk_w,
+                      int64_t T, int32_t topk, int64_t N, float* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QUADS_H */

@@ -1,0 +1,213 @@
+// Shared device helpers and host-side argument checks for the QUADS kernels.
+//
+// NVFP4 arithmetic follows arXiv 2607.15810, section 2.2 ("FP4" and "FP8"
+// paragraphs): E2M1 element codes with magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6;
+// one OCP E4M3FN scale byte per 16 elements; one fp32 tensor scale.  Every
+// rounding is round-to-nearest-even of the exact real value; the helpers
+// below reach that with exact fp64 products and directed fp32 thresholds.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/quads.h"
+
+namespace quads {
+
+constexpr int kBlock = 16;              // NVFP4 block length
+constexpr int kScoreFanin = 64;         // fixed order of the channel-score sum
+constexpr int kE4m3MaxCode = 0x7E;      // 448
+constexpr int kAmaxGroups = 1024;       // partial maxima per tensor (max)
+
+// ---------------------------------------------------------------- device --
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read once: non-temporal hint).
+__device__ __forceinline__ uint4 ld_stream16(const void* p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+
+// fp32 value of an E4M3FN code 0..0x7E (exact).
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+    return c < 8 ? (float)c * 0x1p-9f
+                 : ldexpf((float)(8u + (c & 7u)), (int)(c >> 3) - 10);
+}
+
+// Magnitude of an E2M1 code 0..7.
+__device__ __forceinline__ float e2m1_value(uint32_t m) {
+    // 0, .5, 1, 1.5 -> m/2 ; 2, 3, 4, 6 -> (2 + (m&1)) * 2^((m>>1)-1)
+    return m < 4 ? 0.5f * (float)m : ldexpf((float)(2u + (m & 1u)), (int)(m >> 1) - 2);
+}
+
+// E4M3FN code nearest to q >= 0 (ties to even mantissa), saturating at 448.
+// q must lie on the same side of every E4M3 midpoint as the exact quotient it
+// stands for; a correctly rounded fp64 quotient of the operands used here does.
+__device__ __forceinline__ uint32_t e4m3_rne_code(double q) {
+    if (!(q < 448.0)) return kE4m3MaxCode;
+    if (q < 0x1p-6) return (uint32_t)rint(q * 512.0);       // subnormal codes 0..8
+    uint64_t b = (uint64_t)__double_as_longlong(q);
+    uint64_t r = (b + 0xFFFFFFFFFFFFull + ((b >> 49) & 1ull)) >> 49;   // exp | 3-bit mantissa
+    uint32_t c = (uint32_t)r - (1016u << 3);                 // rebias 1023 -> 7
+    return c > (uint32_t)kE4m3MaxCode ? (uint32_t)kE4m3MaxCode : c;
+}
+
+// Tensor scale s_t = RN32(A / 2688) for A = max|x| >= 0.  fp64 division then
+// one fp32 rounding equals the exact RN32 for every bf16 and fp32 A here.
+__device__ __forceinline__ float tensor_scale_from_amax(float amax) {
+    return (float)((double)amax / 2688.0);
+}
+
+// Largest fp32 <= t and smallest fp32 >= t, for t >= 0 (exact, via compares).
+__device__ __forceinline__ uint32_t f32_bits_rd(double t) {
+    float f = (float)t;
+    uint32_t b = __float_as_uint(f);
+    if ((double)f > t) b -= 1;
+    return b;
+}
+__device__ __forceinline__ uint32_t f32_bits_ru(double t) {
+    float f = (float)t;
+    uint32_t b = __float_as_uint(f);
+    if ((double)f < t) b += 1;
+    return b;
+}
+
+// Element-code thresholds for one block scale.  E2M1 decision boundaries in
+// units of s_b*s_t are 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5 (midpoints of the
+// grid).  thr[i] is an fp32 bit pattern such that, for |x| in fp32,
+// magnitude code = #{ i : bits(|x|) > thr[i] } exactly: at boundary i the
+// tie goes to the even code, so for even i the code rises when |x| > T_i
+// (thr = RD32(T_i)) and for odd i when |x| >= T_i (thr = RU32(T_i) - 1 ulp).
+// T_i = b_i * s_b * s_t is exact in fp64 (at most 31 significant bits).
+// Non-negative fp32 bit patterns order like their values, so the compares are
+// integer compares and independent of the denormal mode.
+__device__ __forceinline__ void e2m1_thresholds(float s_b, float s_t, uint32_t thr[7]) {
+    const float bnd[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    if (!(s_b > 0.0f) || !(s_t > 0.0f)) {
+#pragma unroll
+        for (int i = 0; i < 7; ++i) thr[i] = 0x7F800000u;   // never exceeded
+        return;
+    }
+#pragma unroll
+    for (int i = 0; i < 7; ++i) {
+        double t = (double)(bnd[i] * s_b) * (double)s_t;     // b_i*s_b exact in fp32
+        thr[i] = (i & 1) ? f32_bits_ru(t) - 1u : f32_bits_rd(t);
+    }
+}
+
+__device__ __forceinline__ uint32_t e2m1_mag_code(uint32_t abs_bits, const uint32_t thr[7]) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < 7; ++i) m += abs_bits > thr[i] ? 1u : 0u;
+    return m;
+}
+
+// bf16 bit pattern nearest to d (ties to even), subnormals kept; |d| finite
+// and below the bf16 overflow threshold.
+__device__ __forceinline__ uint32_t bf16_rne_from_f64(double d) {
+    uint64_t b = (uint64_t)__double_as_longlong(d);
+    uint32_t sign = (uint32_t)(b >> 48) & 0x8000u;
+    uint64_t ab = b & 0x7FFFFFFFFFFFFFFFull;
+    double a = __longlong_as_double((long long)ab);
+    uint32_t out;
+    if (a < 0x1p-126) {
+        out = (uint32_t)rint(a * 0x1p133);
+    } else {
+        uint64_t r = (ab + 0xFFFFFFFFFFFull + ((ab >> 45) & 1ull)) >> 45;
+        out = (uint32_t)(r - ((uint64_t)(1023 - 127) << 7));
+    }
+    return sign | out;
+}
+
+// bf16 nearest to an fp32 value (ties to even); finite inputs.
+__device__ __forceinline__ uint32_t bf16_rne_from_f32(float f) {
+    uint32_t b = __float_as_uint(f);
+    return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+// Wave64 reductions.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        uint32_t o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+    us2 r = __builtin_elementwise_max(__builtin_bit_cast(us2, a), __builtin_bit_cast(us2, b));
+    return __builtin_bit_cast(uint32_t, r);
+}
+
+// Tensor scale of segment `seg` from its partial maxima (or the caller's fixed
+// scale), computed by the first wave of the work-group into *s_out (LDS).
+__device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, int groups,
+                                                      const float* ts_in, int seg, float* s_out) {
+    if (threadIdx.x < 64) {
+        float st;
+        if (ts_in != nullptr) {
+            st = ts_in[0];
+        } else {
+            uint32_t m = 0;
+            for (int i = threadIdx.x; i < groups; i += 64) {
+                uint32_t v = partial[(int64_t)seg * groups + i];
+                m = v > m ? v : m;
+            }
+            m = wave_max_u32(m);
+            st = tensor_scale_from_amax(bf16_to_f32(m));
+        }
+        if (threadIdx.x == 0) *s_out = st;
+    }
+}
+
+// Threshold table: s_thr[c][0..6] for block-scale code c = 0..126.
+__device__ __forceinline__ void build_threshold_table(float s_t, uint32_t (*s_thr)[8]) {
+    for (int c = threadIdx.x; c <= kE4m3MaxCode; c += blockDim.x) {
+        uint32_t thr[7];
+        e2m1_thresholds(e4m3_value((uint32_t)c), s_t, thr);
+#pragma unroll
+        for (int i = 0; i < 7; ++i) s_thr[c][i] = thr[i];
+        s_thr[c][7] = 0x7F800000u;
+    }
+}
+
+// ------------------------------------------------------------------ host --
+
+#define QUADS_CHECK_LAUNCH()                                                  \
+    do {                                                                      \
+        hipError_t e__ = hipGetLastError();                                   \
+        if (e__ != hipSuccess) return ::quads::set_hip_error(e__);            \
+    } while (0)
+
+int set_hip_error(hipError_t e);
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
+inline bool ok_opt_ptr(const void* p) { return p == nullptr || aligned16(p); }
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Launchers shared between translation units (defined in quantize.hip).
+// Partial maxima of |x| over nseg contiguous segments of seg_elems elements
+// each, `groups` values per segment into partial[seg * groups + g].
+void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_t* partial,
+                         int groups, hipStream_t s);
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+// Number of work-groups of the partial-max pass for n elements.
+inline int amax_groups(int64_t n) {
+    int64_t g = (n + 8 * 256 * 8 - 1) / (8 * 256 * 8);   // >= 8 vectors of 8 per thread
+    if (g < 1) g = 1;
+    if (g > kAmaxGroups) g = kAmaxGroups;
+    return (int)g;
+}
+
+}  // namespace quads

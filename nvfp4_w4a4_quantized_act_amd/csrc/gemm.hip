@@ -1,0 +1,326 @@
+// Grouped W4A4 GEMM with the RAC compensation term (arXiv 2607.15810, Eq. (6)
+// applied to the compensated activation of Eq. (21)), for MoE experts.
+//
+// MFMA operand type.  An NVFP4 value v * s_b (E2M1 times an E4M3 block scale)
+// has at most 6 significant bits and magnitude in [2^-10, 2688], so it is
+// exact in fp16; products of two are exact in fp32.  The kernel therefore
+// dequantizes both operands exactly to fp16 and issues 32x32x16 fp16 MFMA
+// with fp32 accumulation; the fp32 tensor scales are applied in the epilogue.
+// gfx950's block-scaled fp4 MFMA takes one power-of-two scale per 32
+// elements, which cannot express E4M3 scales over 16 elements exactly.
+//
+// Tiling: 256 threads, a 128 x 128 output tile, K staged 64 at a time.  Each
+// thread loads 32 fp4 codes (16 bytes) and their two scale bytes of one A row
+// and one W row, converts them to fp16 (hardware fp4 -> fp16 convert, then a
+// packed fp16 multiply by the block scale) and stores them to LDS.  Four
+// waves (2 x 2) each own a 64 x 64 sub-tile = 2 x 2 MFMA tiles.
+//
+// Compensation: after the main K loop the same tile runs a second, short
+// loop over the k selected channels: A = the second-pass residual codes, B =
+// the weight columns sel[i] gathered per row.  It accumulates into its own
+// fp32 registers because its tensor scale differs; the epilogue forms
+//   Y = acc_main * (s_tA s_tW[e]) + acc_comp * (s_tR s_tW[e]).
+#include "common.h"
+
+namespace quads {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kLd = kBK + 8;           // halfs per LDS row (16-byte pad)
+constexpr int kGemmMaxE = 4096;
+
+struct GemmArgs {
+    const uint8_t* a_nib; const uint8_t* a_scale; const float* a_ts;
+    const int32_t* row_token; int64_t rows; int K;
+    const uint8_t* r_nib; const uint8_t* r_scale; const float* r_ts; const int32_t* sel; int k;
+    const uint8_t* w_nib; const uint8_t* w_scale; const float* w_ts;
+    const int32_t* offsets; int E; int N;
+    int epilogue; int out_bf16; void* out;
+};
+
+// (expert, first row, end row) of M-tile `tile`: experts' rows are cut into
+// tiles of kBM; tiles are numbered expert by expert.  Returns false (for the
+// whole work-group) when `tile` is past the last tile.
+__device__ bool find_tile(const int32_t* offsets, int E, int64_t rows, int tile, int* s_scan,
+                          int* s_res, int* e_out, int* m0_out, int* mend_out) {
+    if (offsets == nullptr) {                      // one expert, all rows
+        const int64_t m0 = (int64_t)tile * kBM;
+        *e_out = 0;
+        *m0_out = (int)m0;
+        *mend_out = (int)rows;
+        return m0 < rows;
+    }
+    const int per = (E + 255) / 256;
+    const int e0 = threadIdx.x * per;
+    const int e1 = e0 + per < E ? e0 + per : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = local;
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_scan[wid] = x;
+    if (threadIdx.x == 0) s_res[3] = 0;
+    __syncthreads();
+    int base = 0;
+    for (int i = 0; i < wid; ++i) base += s_scan[i];
+    int run = x - local + base;
+    for (int e = e0; e < e1; ++e) {
+        const int t = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+        if (tile >= run && tile < run + t) {     // exactly one thread matches
+            s_res[0] = e;
+            s_res[1] = offsets[e] + (tile - run) * kBM;
+            s_res[2] = offsets[e + 1];
+            s_res[3] = 1;
+        }
+        run += t;
+    }
+    __syncthreads();
+    *e_out = s_res[0];
+    *m0_out = s_res[1];
+    *mend_out = s_res[2];
+    return s_res[3] != 0;
+}
+
+// 16 fp4 codes (8 bytes) times an E4M3 block scale -> 16 exact fp16 values.
+__device__ __forceinline__ void dequant16(uint2 q, uint32_t sbyte, f16x8* lo, f16x8* hi) {
+    const _Float16 sb = (_Float16)e4m3_value(sbyte);
+    const f16x2 s2 = {sb, sb};
+    const uint32_t w[2] = {q.x, q.y};
+    f16x2 v[8];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        v[4 * i + 0] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 0) * s2;
+        v[4 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 1) * s2;
+        v[4 * i + 2] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 2) * s2;
+        v[4 * i + 3] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[i], 1.0f, 3) * s2;
+    }
+    *lo = (f16x8){v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+    *hi = (f16x8){v[4][0], v[4][1], v[5][0], v[5][1], v[6][0], v[6][1], v[7][0], v[7][1]};
+}
+
+// Load and dequantize 32 consecutive codes (two blocks) of one row starting at
+// channel kc (a multiple of 16); channels >= kend read as zero.
+__device__ __forceinline__ void load_row32(const uint8_t* nib_row, const uint8_t* sc_row, int kc,
+                                           int kend, bool valid, f16x8 out[4]) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int c = kc + 16 * j;
+        if (valid && c < kend) {
+            const uint2 q = *reinterpret_cast<const uint2*>(nib_row + c / 2);
+            dequant16(q, sc_row[c / 16], &out[2 * j], &out[2 * j + 1]);
+        } else {
+            out[2 * j] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+            out[2 * j + 1] = out[2 * j];
+        }
+    }
+}
+
+__device__ __forceinline__ void store_lds32(_Float16* dst, const f16x8 v[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<f16x8*>(dst + 8 * i) = v[i];
+}
+
+__device__ __forceinline__ void mma_stage(const _Float16* sA, const _Float16* sB, int wm, int wn,
+                                          int lane, f32x16 acc[2][2]) {
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+        const int kof = kk * 16 + 8 * (lane >> 5);
+        f16x8 a[2], b[2];
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+            a[mi] = *reinterpret_cast<const f16x8*>(sA + (wm * 64 + mi * 32 + (lane & 31)) * kLd + kof);
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj)
+            b[nj] = *reinterpret_cast<const f16x8*>(sB + (wn * 64 + nj * 32 + (lane & 31)) * kLd + kof);
+#pragma unroll
+        for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+    }
+}
+
+// Weight row of B-tile row r.  Plain: f0 + r.  SwiGLU: the tile holds 64
+// output features; rows 0-31 / 32-63 of each 64-row half are gate / up.
+__device__ __forceinline__ int w_row_of(int r, int f0, int N, bool swiglu, bool* valid) {
+    if (!swiglu) {
+        const int n = f0 + r;
+        *valid = n < N;
+        return n;
+    }
+    const int feat = f0 + (r >> 6) * 32 + (r & 31);
+    *valid = feat < N / 2;
+    return ((r >> 5) & 1) * (N / 2) + feat;
+}
+
+__global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
+    __shared__ _Float16 sA[kBM * kLd];
+    __shared__ _Float16 sB[kBN * kLd];
+    __shared__ int s_scan[8];
+    __shared__ int s_res[4];
+    int e, m0, mend;
+    if (!find_tile(g.offsets, g.E, g.rows, blockIdx.y, s_scan, s_res, &e, &m0, &mend)) return;
+    const bool swiglu = g.epilogue == QUADS_EPI_SWIGLU;
+    const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lr = tid >> 1, lh = tid & 1;           // loader: tile row, 32-channel half
+
+    // A row of this thread's loader slot
+    const int p = m0 + lr;
+    const bool a_valid = p < mend;
+    const int64_t src = a_valid ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
+    const uint8_t* a_nib_row = g.a_nib + src * (g.K / 2);
+    const uint8_t* a_sc_row = g.a_scale + src * (g.K / kBlock);
+    bool b_valid;
+    const int wrow = w_row_of(lr, f0, g.N, swiglu, &b_valid);
+    const int64_t wbase = ((int64_t)e * g.N + (b_valid ? wrow : 0));
+    const uint8_t* w_nib_row = g.w_nib + wbase * (g.K / 2);
+    const uint8_t* w_sc_row = g.w_scale + wbase * (g.K / kBlock);
+
+    f32x16 acc[2][2], accc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) { acc[i][j][v] = 0.f; accc[i][j][v] = 0.f; }
+
+    for (int k0 = 0; k0 < g.K; k0 += kBK) {
+        f16x8 va[4], vb[4];
+        load_row32(a_nib_row, a_sc_row, k0 + 32 * lh, g.K, a_valid, va);
+        load_row32(w_nib_row, w_sc_row, k0 + 32 * lh, g.K, b_valid, vb);
+        __syncthreads();
+        store_lds32(sA + lr * kLd + 32 * lh, va);
+        store_lds32(sB + lr * kLd + 32 * lh, vb);
+        __syncthreads();
+        mma_stage(sA, sB, wm, wn, lane, acc);
+    }
+
+    if (g.k > 0) {
+        const uint8_t* r_nib_row = g.r_nib + src * (g.k / 2);
+        const uint8_t* r_sc_row = g.r_scale + src * (g.k / kBlock);
+        for (int i0 = 0; i0 < g.k; i0 += kBK) {
+            f16x8 va[4], vb[4];
+            load_row32(r_nib_row, r_sc_row, i0 + 32 * lh, g.k, a_valid, va);
+            // gathered weight columns sel[i] of row wrow
+            _Float16 h[32];
+#pragma unroll 4
+            for (int u = 0; u < 32; ++u) {
+                const int i = i0 + 32 * lh + u;
+                float v = 0.0f;
+                if (b_valid && i < g.k) {
+                    const int j = g.sel[i];
+                    const uint32_t code = (w_nib_row[j >> 1] >> (4 * (j & 1))) & 0xFu;
+                    v = e2m1_value(code & 7u) * e4m3_value(w_sc_row[j >> 4]);
+                    if (code & 8u) v = -v;
+                }
+                h[u] = (_Float16)v;                  // exact
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                vb[q] = (f16x8){h[8 * q], h[8 * q + 1], h[8 * q + 2], h[8 * q + 3], h[8 * q + 4],
+                                h[8 * q + 5], h[8 * q + 6], h[8 * q + 7]};
+            __syncthreads();
+            store_lds32(sA + lr * kLd + 32 * lh, va);
+            store_lds32(sB + lr * kLd + 32 * lh, vb);
+            __syncthreads();
+            mma_stage(sA, sB, wm, wn, lane, accc);
+        }
+    }
+
+    // epilogue
+    const float s_ta = g.a_ts[0], s_tw = g.w_ts[e];
+    const float ca = s_ta * s_tw;
+    const float cr = g.k > 0 ? g.r_ts[0] * s_tw : 0.0f;
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int row_t = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            const int prow = m0 + row_t;
+            if (prow >= mend) continue;
+            float y[2];
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj) {
+                y[nj] = acc[mi][nj][v] * ca;
+                if (g.k > 0) y[nj] = fmaf(accc[mi][nj][v], cr, y[nj]);
+            }
+            if (swiglu) {
+                const int feat = f0 + wn * 32 + (lane & 31);
+                if (feat < g.N / 2) {
+                    const float gt = y[0], up = y[1];
+                    const float hval = gt / (1.0f + expf(-gt)) * up;
+                    ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] =
+                        (uint16_t)bf16_rne_from_f32(hval);
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int n = f0 + wn * 64 + nj * 32 + (lane & 31);
+                    if (n >= g.N) continue;
+                    const int64_t o = (int64_t)prow * g.N + n;
+                    if (g.out_bf16)
+                        ((uint16_t*)g.out)[o] = (uint16_t)bf16_rne_from_f32(y[nj]);
+                    else
+                        ((float*)g.out)[o] = y[nj];
+                }
+            }
+        }
+    }
+}
+
+}  // namespace quads
+
+using namespace quads;
+
+extern "C" size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int32_t E,
+                                         int64_t N) {
+    (void)rows; (void)K; (void)k; (void)E; (void)N;
+    return 0;
+}
+
+extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
+                                   const float* a_ts, const int32_t* row_token, int64_t rows,
+                                   int64_t K, const uint8_t* r_nib, const uint8_t* r_scale,
+                                   const float* r_ts, const int32_t* sel, int32_t k,
+                                   const uint8_t* w_nib, const uint8_t* w_scale,
+                                   const float* w_ts, const int32_t* offsets, int32_t E,
+                                   int64_t N, int epilogue, int out_dtype, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    (void)ws;
+    if (epilogue != QUADS_EPI_NONE && epilogue != QUADS_EPI_SWIGLU) return QUADS_EINVAL;
+    if (out_dtype != QUADS_OUT_F32 && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (epilogue == QUADS_EPI_SWIGLU && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (rows < 0 || rows >= ((int64_t)1 << 31) || K <= 0 || K % kBlock || K >= ((int64_t)1 << 30))
+        return QUADS_ESHAPE;
+    if (k < 0 || k % kBlock || k > K) return QUADS_ESHAPE;
+    if (E < 1 || E > kGemmMaxE || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
+    if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
+    if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
+    if (!ok_ptr(a_nib) || !ok_ptr(a_scale) || !ok_ptr(a_ts) || !ok_ptr(w_nib) ||
+        !ok_ptr(w_scale) || !ok_ptr(w_ts) || !ok_ptr(out))
+        return QUADS_EINVAL;
+    if (k > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale) || !ok_ptr(r_ts) || !ok_ptr(sel)))
+        return QUADS_EINVAL;
+    if (ws_bytes < quads_moe_w4a4_gemm_ws(rows, K, k, E, N)) return QUADS_EWORKSPACE;
+    if (rows == 0) return QUADS_OK;
+    GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
+               w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
+               out_dtype == QUADS_OUT_BF16, out};
+    const int64_t ntiles_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + kBN / 2 - 1) / (kBN / 2)
+                                                          : (N + kBN - 1) / kBN;
+    int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? E : 0);
+    hipLaunchKernelGGL(k_gemm_w4a4, dim3((unsigned)ntiles_n, (unsigned)ntiles_m), dim3(256), 0,
+                       (hipStream_t)stream, g);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}

@@ -1,0 +1,216 @@
+// Token-to-expert packing and the MoE combine.
+//
+// Packing is a stable counting sort of the T*topk (token, slot) pairs by
+// expert id, in three launches: per-chunk histograms, one work-group that
+// turns them into expert offsets and per-chunk bases, and a scatter in which
+// one wave walks its chunk 64 entries at a time, ranking equal ids with
+// ballots so that equal ids keep their flattened order.
+//
+// Combine: out[t] = sum over slots (in order) of w[t, slot] * y[pos[t, slot]],
+// eight output features per thread, fp32 fused multiply-adds.
+#include "common.h"
+
+namespace quads {
+
+constexpr int kPackChunk = 1024;       // entries per chunk
+constexpr int kPackMaxE = 4096;
+
+__global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ ids, int64_t n,
+                                                    int E, int32_t* __restrict__ cnt) {
+    __shared__ int s_h[kPackMaxE];
+    for (int e = threadIdx.x; e < E; e += 256) s_h[e] = 0;
+    __syncthreads();
+    const int64_t base = (int64_t)blockIdx.x * kPackChunk;
+    for (int i = threadIdx.x; i < kPackChunk; i += 256) {
+        const int64_t idx = base + i;
+        if (idx < n) {
+            const int e = ids[idx];
+            if (e >= 0 && e < E) atomicAdd(&s_h[e], 1);
+        }
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) cnt[(int64_t)blockIdx.x * E + e] = s_h[e];
+}
+
+// One work-group: offsets[e] = exclusive scan of expert totals; cnt[c][e] is
+// replaced by the first packed row of expert e's entries from chunk c.
+__global__ __launch_bounds__(1024) void k_pack_scan(int32_t* __restrict__ cnt, int nchunks, int E,
+                                                    int64_t n, int32_t* __restrict__ offsets) {
+    __shared__ int s_tot[kPackMaxE];
+    __shared__ int s_wave[16];
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        int run = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            const int v = cnt[(int64_t)c * E + e];
+            cnt[(int64_t)c * E + e] = run;
+            run += v;
+        }
+        s_tot[e] = run;
+    }
+    __syncthreads();
+    // exclusive scan of s_tot over E entries: each thread owns a contiguous run
+    const int per = (E + 1023) / 1024;
+    const int e0 = threadIdx.x * per;
+    const int e1 = e0 + per < E ? e0 + per : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += s_tot[e];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int x = local;
+    for (int off = 1; off < 64; off <<= 1) {
+        int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[wid] = x;
+    __syncthreads();
+    int wbase = 0;
+    for (int i = 0; i < wid; ++i) wbase += s_wave[i];
+    int run = x - local + wbase;
+    __syncthreads();
+    for (int e = e0; e < e1; ++e) {
+        const int t = s_tot[e];
+        s_tot[e] = run;
+        run += t;
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 1024) {
+        offsets[e] = s_tot[e];
+        for (int c = 0; c < nchunks; ++c) cnt[(int64_t)c * E + e] += s_tot[e];
+    }
+    if (threadIdx.x == 0) offsets[E] = (int32_t)n;
+}
+
+// One wave per chunk.
+__global__ __launch_bounds__(64) void k_pack_scatter(const int32_t* __restrict__ ids, int64_t n,
+                                                     int topk, int E,
+                                                     const int32_t* __restrict__ base,
+                                                     int32_t* __restrict__ row_token,
+                                                     int32_t* __restrict__ pos) {
+    __shared__ int s_next[kPackMaxE];
+    for (int e = threadIdx.x; e < E; e += 64) s_next[e] = base[(int64_t)blockIdx.x * E + e];
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const int lane = threadIdx.x;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int64_t c0 = (int64_t)blockIdx.x * kPackChunk;
+    for (int it = 0; it < kPackChunk / 64; ++it) {
+        const int64_t idx = c0 + it * 64 + lane;
+        int e = -1;
+        if (idx < n) {
+            e = ids[idx];
+            if (e < 0 || e >= E) e = -1;
+        }
+        uint64_t peers = __ballot(e >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
+            peers &= (e >= 0 && ((e >> b) & 1)) ? m : ~m;
+        }
+        int rank = 0, p = 0;
+        if (e >= 0) {
+            rank = __popcll(peers & lt);
+            p = s_next[e] + rank;
+        }
+        __syncthreads();
+        if (e >= 0) {
+            row_token[p] = (int32_t)(idx / topk);
+            pos[idx] = p;
+            if (rank == 0) s_next[e] += __popcll(peers);
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- combine --
+template <bool kBf16>
+__global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y,
+                                                 const int32_t* __restrict__ pos,
+                                                 const float* __restrict__ w, int64_t T, int topk,
+                                                 int64_t N, float* __restrict__ out) {
+    const int64_t groups = N / 8;
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= T * groups) return;
+    const int64_t t = gid / groups;
+    const int64_t c = (gid - t * groups) * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < topk; ++s) {
+        const float ws = w[t * topk + s];
+        const int64_t p = pos[t * topk + s];
+        float v[8];
+        if (kBf16) {
+            const uint4 q = *reinterpret_cast<const uint4*>((const uint16_t*)y + p * N + c);
+            const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                v[2 * i] = __uint_as_float(u[i] << 16);
+                v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
+            }
+        } else {
+            const float4* q = reinterpret_cast<const float4*>((const float*)y + p * N + c);
+            const float4 a = q[0], b = q[1];
+            v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+            v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(ws, v[i], acc[i]);
+    }
+    float4* o = reinterpret_cast<float4*>(out + t * N + c);
+    o[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    o[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
+}  // namespace quads
+
+using namespace quads;
+
+extern "C" size_t quads_moe_pack_ws(int64_t T, int32_t topk, int32_t E) {
+    if (T < 0 || topk < 1 || E < 1) return 0;
+    const int64_t nchunks = (T * topk + kPackChunk - 1) / kPackChunk;
+    return align_up((size_t)(nchunks > 0 ? nchunks : 1) * E * 4, 256);
+}
+
+extern "C" int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
+                              int32_t* offsets, int32_t* row_token, int32_t* pos, void* ws,
+                              size_t ws_bytes, void* stream) {
+    if (T < 0 || topk < 1 || topk > 64 || E < 1 || E > kPackMaxE) return QUADS_ESHAPE;
+    if ((int64_t)T * topk >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
+    if (!ok_ptr(offsets)) return QUADS_EINVAL;
+    if (T > 0 && (!ok_ptr(topk_ids) || !ok_ptr(row_token) || !ok_ptr(pos))) return QUADS_EINVAL;
+    if (ws_bytes < quads_moe_pack_ws(T, topk, E) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t n = T * topk;
+    const int nchunks = (int)((n + kPackChunk - 1) / kPackChunk);
+    int32_t* cnt = static_cast<int32_t*>(ws);
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(k_pack_count, dim3(nchunks), dim3(256), 0, s, topk_ids, n, (int)E, cnt);
+        QUADS_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(k_pack_scan, dim3(1), dim3(1024), 0, s, cnt, nchunks, (int)E, n, offsets);
+    QUADS_CHECK_LAUNCH();
+    if (nchunks > 0) {
+        hipLaunchKernelGGL(k_pack_scatter, dim3(nchunks), dim3(64), 0, s, topk_ids, n, (int)topk,
+                           (int)E, cnt, row_token, pos);
+        QUADS_CHECK_LAUNCH();
+    }
+    return QUADS_OK;
+}
+
+extern "C" int quads_moe_combine(const void* y, int y_dtype, const int32_t* pos,
+                                 const float* topk_w, int64_t T, int32_t topk, int64_t N,
+                                 float* out, void* stream) {
+    if (y_dtype != QUADS_OUT_F32 && y_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (T < 0 || topk < 1 || N <= 0 || N % 8) return QUADS_ESHAPE;
+    if (T > 0 && (!ok_ptr(y) || !ok_ptr(pos) || !ok_ptr(topk_w) || !ok_ptr(out)))
+        return QUADS_EINVAL;
+    if (T == 0) return QUADS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t threads = T * (N / 8);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (y_dtype == QUADS_OUT_BF16)
+        hipLaunchKernelGGL(k_combine<true>, grid, dim3(256), 0, s, y, pos, topk_w, T, (int)topk, N,
+                           out);
+    else
+        hipLaunchKernelGGL(k_combine<false>, grid, dim3(256), 0, s, y, pos, topk_w, T, (int)topk,
+                           N, out);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}

@@ -1,0 +1,206 @@
+// NVFP4 quantization of bf16 tensors: activation quantizer Q_A (Eq. (9)) and
+// the shared weight QDQ Q_W (Eq. (7), (12)) of arXiv 2607.15810, with the
+// format of its section 2.2.
+//
+// Two passes over the tensor: a partial-max pass (one value per work-group)
+// and the quantize pass, whose work-groups first fold the partial maxima into
+// the tensor scale, then build a per-tensor table of element-code thresholds
+// for all 127 block-scale codes in LDS, then stream 16-element blocks: one
+// block per lane per iteration, two 16-byte loads, one 8-byte nibble store
+// and one scale byte.
+#include "common.h"
+
+namespace quads {
+
+// Max of |x| (as bf16 bit patterns) over segment blockIdx.y of seg_elems
+// elements; one result per work-group into partial[blockIdx.y * gridDim.x + x].
+__global__ __launch_bounds__(256) void k_amax_partial(const uint16_t* __restrict__ x,
+                                                      int64_t seg_elems,
+                                                      uint32_t* __restrict__ partial) {
+    const int64_t nvec = seg_elems / 8;
+    const uint4* v = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * seg_elems);
+    uint32_t m = 0;
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < nvec; i += stride) {
+        uint4 q = ld_stream16(v + i);
+        m = pk_max_u16(m, q.x & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.y & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.z & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.w & 0x7FFF7FFFu);
+    }
+    uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    m = wave_max_u32(lo > hi ? lo : hi);
+    __shared__ uint32_t s_w[4];
+    if ((threadIdx.x & 63) == 0) s_w[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = s_w[0];
+        for (int i = 1; i < 4; ++i) r = s_w[i] > r ? s_w[i] : r;
+        partial[(int64_t)blockIdx.y * gridDim.x + blockIdx.x] = r;
+    }
+}
+
+// Quantize segment blockIdx.y (rows x K elements, contiguous) of bf16 x.
+__global__ __launch_bounds__(256) void k_quantize_bf16(
+    const uint16_t* __restrict__ x, int64_t seg_elems, const uint32_t* __restrict__ partial,
+    int groups, const float* __restrict__ ts_in, uint8_t* __restrict__ nib,
+    uint8_t* __restrict__ scale, float* __restrict__ ts_out, uint16_t* __restrict__ dq) {
+    __shared__ uint32_t s_thr[kE4m3MaxCode + 1][8];
+    __shared__ float s_st;
+    const int seg = blockIdx.y;
+    tensor_scale_prologue(partial, groups, ts_in, seg, &s_st);
+    __syncthreads();
+    const float s_t = s_st;
+    if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[seg] = s_t;
+    build_threshold_table(s_t, s_thr);
+    __syncthreads();
+
+    const int64_t nblk = seg_elems / kBlock;
+    const uint16_t* xs = x + (int64_t)seg * seg_elems;
+    uint8_t* ns = nib + (int64_t)seg * (seg_elems / 2);
+    uint8_t* ss = scale + (int64_t)seg * nblk;
+    uint16_t* ds = dq ? dq + (int64_t)seg * seg_elems : nullptr;
+    const double six_st = 6.0 * (double)s_t;                  // exact
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
+        const uint4* p = reinterpret_cast<const uint4*>(xs + b * kBlock);
+        uint4 q0 = ld_stream16(p);
+        uint4 q1 = ld_stream16(p + 1);
+        uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        uint32_t am = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
+        uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+        const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
+        const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
+        uint32_t thr[7];
+        {
+            uint4 t0 = *reinterpret_cast<const uint4*>(&s_thr[sb][0]);
+            uint4 t1 = *reinterpret_cast<const uint4*>(&s_thr[sb][4]);
+            thr[0] = t0.x; thr[1] = t0.y; thr[2] = t0.z; thr[3] = t0.w;
+            thr[4] = t1.x; thr[5] = t1.y; thr[6] = t1.z;
+        }
+        uint32_t packed[2] = {0u, 0u};
+        uint32_t mags[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t mag = e2m1_mag_code((h & 0x7FFFu) << 16, thr);
+            mags[e] = mag | ((h >> 12) & 8u);
+            packed[e >> 3] |= mags[e] << (4 * (e & 7));
+        }
+        *reinterpret_cast<uint2*>(ns + b * 8) = make_uint2(packed[0], packed[1]);
+        ss[b] = (uint8_t)sb;
+        if (ds) {
+            const float s_b = e4m3_value(sb);
+            uint32_t o[8];
+#pragma unroll
+            for (int e = 0; e < 16; e += 2) {
+                uint32_t r2[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const uint32_t c = mags[e + u];
+                    float v = e2m1_value(c & 7u) * s_b;                 // exact
+                    if (c & 8u) v = -v;
+                    r2[u] = bf16_rne_from_f64((double)v * (double)s_t);  // exact product
+                }
+                o[e >> 1] = r2[0] | (r2[1] << 16);
+            }
+            uint4* dp = reinterpret_cast<uint4*>(ds + b * kBlock);
+            dp[0] = make_uint4(o[0], o[1], o[2], o[3]);
+            dp[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
+__global__ void k_fill_f32(float* p, int n, float v) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = v;
+}
+
+void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_t* partial,
+                         int groups, hipStream_t s) {
+    hipLaunchKernelGGL(k_amax_partial, dim3(groups, nseg), dim3(256), 0, s, x, seg_elems, partial);
+}
+
+void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+    if (n > 0)
+        hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p,
+                           (int)n, v);
+}
+
+int quant_grid(int64_t nblk) {
+    int64_t g = (nblk + 255) / 256;
+    if (g > 4096) g = 4096;
+    return (int)(g < 1 ? 1 : g);
+}
+
+}  // namespace quads
+
+using namespace quads;
+
+extern "C" size_t quads_nvfp4_quantize_ws(int64_t M, int64_t K) {
+    (void)M; (void)K;
+    return align_up(kAmaxGroups * sizeof(uint32_t), 256);
+}
+
+extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* ts_in,
+                                    uint8_t* nib, uint8_t* scale, float* ts_out, void* ws,
+                                    size_t ws_bytes, void* stream) {
+    if (M < 0 || K <= 0 || K % kBlock) return QUADS_ESHAPE;
+    if (!ok_ptr(ts_out) || !ok_opt_ptr(ts_in)) return QUADS_EINVAL;
+    if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale))) return QUADS_EINVAL;
+    if (ws_bytes < quads_nvfp4_quantize_ws(M, K) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, s, ts_out, 1, 0.0f);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    const int64_t n = M * K;
+    uint32_t* partial = static_cast<uint32_t*>(ws);
+    int groups = 1;
+    if (!ts_in) {
+        groups = amax_groups(n);
+        hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial);
+        QUADS_CHECK_LAUNCH();
+    }
+    hipLaunchKernelGGL(k_quantize_bf16, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
+                       partial, groups, ts_in, nib, scale, ts_out, (uint16_t*)nullptr);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+extern "C" size_t quads_nvfp4_weight_qdq_ws(int64_t E, int64_t N, int64_t K) {
+    (void)N; (void)K;
+    if (E < 1) return 0;
+    return align_up((size_t)E * kAmaxGroups * sizeof(uint32_t), 256);
+}
+
+extern "C" int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, int64_t K,
+                                      uint8_t* w_nib, uint8_t* w_scale, float* w_ts,
+                                      uint16_t* w_dq, void* ws, size_t ws_bytes, void* stream) {
+    if (E < 1 || E > 65535 || N < 0 || K <= 0 || K % kBlock) return QUADS_ESHAPE;
+    if (!ok_ptr(w_ts) || !ok_opt_ptr(w_dq)) return QUADS_EINVAL;
+    if (N > 0 && (!ok_ptr(w) || !ok_ptr(w_nib) || !ok_ptr(w_scale))) return QUADS_EINVAL;
+    if (ws_bytes < quads_nvfp4_weight_qdq_ws(E, N, K) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (N == 0) {
+        hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((E + 255) / 256)), dim3(256), 0, s, w_ts,
+                           (int)E, 0.0f);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    const int64_t n = N * K;
+    int groups = amax_groups(n);
+    uint32_t* partial = static_cast<uint32_t*>(ws);
+    hipLaunchKernelGGL(k_amax_partial, dim3(groups, (unsigned)E), dim3(256), 0, s, w, n, partial);
+    QUADS_CHECK_LAUNCH();
+    int64_t qg = quant_grid(n / kBlock);
+    int64_t cap = (4096 + E - 1) / E;
+    if (qg > cap) qg = cap < 1 ? 1 : cap;
+    hipLaunchKernelGGL(k_quantize_bf16, dim3((unsigned)qg, (unsigned)E), dim3(256), 0, s, w, n,
+                       partial, groups, (const float*)nullptr, w_nib, w_scale, w_ts, w_dq);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}

@@ -1,0 +1,112 @@
+"""The C-ABI library loads, exports every symbol include/quads.h declares, and
+rejects bad arguments on the host before any launch (CPU only: no compute)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import nvfp4_w4a4_quantized_act_amd as Q
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    with open(os.path.join(ROOT, "include", "quads.h")) as f:
+        src = f.read()
+    return sorted(set(re.findall(r"\b(quads_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = Q.lib()
+    names = _declared()
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 13
+    missing = [n for n in names if not hasattr(lib, n)]
+    assert not missing, missing
+    assert lib.quads_version().startswith(b"quads-mi355x")
+
+
+def test_status_strings():
+    lib = Q.lib()
+    for st in (0, -1, -2, -3, -4):
+        assert lib.quads_status_string(st)
+
+
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced (checks fail first)
+MIS = ctypes.c_void_p(0x10004)           # misaligned
+
+
+def test_quantize_validation():
+    lib = Q.lib()
+    ws = lib.quads_nvfp4_quantize_ws(4, 32)
+    assert ws > 0
+    f = lib.quads_nvfp4_quantize
+    assert f(FAKE, 4, 30, None, FAKE, FAKE, FAKE, FAKE, ws, None) == -2      # K % 16
+    assert f(FAKE, -1, 32, None, FAKE, FAKE, FAKE, FAKE, ws, None) == -2     # M < 0
+    assert f(None, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ws, None) == -1      # null x
+    assert f(MIS, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ws, None) == -1       # misaligned
+    assert f(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == -3  # workspace
+    assert f(FAKE, 4, 32, None, FAKE, FAKE, FAKE, None, ws, None) == -3
+
+
+def test_rac_validation():
+    lib = Q.lib()
+    f = lib.quads_rac_quantize
+    ws = lib.quads_rac_quantize_ws(64, 256, 32)
+    args = lambda m, k_dim, k, wsz: f(FAKE, m, k_dim, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                      FAKE, None, FAKE, wsz, None)
+    assert args(64, 256, 8, ws) == -2          # k % 16
+    assert args(64, 256, 272, ws) == -2        # k > K
+    assert args(64, 250, 16, ws) == -2         # K % 16
+    assert args(64, 256, 32, ws - 1) == -3
+    assert f(FAKE, 64, 256, 32, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, ws,
+             None) == -1                        # sel missing with k > 0
+
+
+def test_weight_qdq_validation():
+    lib = Q.lib()
+    f = lib.quads_nvfp4_weight_qdq
+    ws = lib.quads_nvfp4_weight_qdq_ws(2, 8, 32)
+    assert f(FAKE, 0, 8, 32, FAKE, FAKE, FAKE, None, FAKE, ws, None) == -2
+    assert f(FAKE, 2, 8, 40, FAKE, FAKE, FAKE, None, FAKE, ws, None) == -2
+    assert f(FAKE, 2, 8, 32, FAKE, FAKE, FAKE, MIS, FAKE, ws, None) == -1
+    assert f(FAKE, 2, 8, 32, FAKE, FAKE, FAKE, None, FAKE, ws - 4, None) == -3
+
+
+def test_pack_validation():
+    lib = Q.lib()
+    f = lib.quads_moe_pack
+    ws = lib.quads_moe_pack_ws(16, 2, 4)
+    assert f(FAKE, 16, 0, 4, FAKE, FAKE, FAKE, FAKE, ws, None) == -2
+    assert f(FAKE, 16, 2, 0, FAKE, FAKE, FAKE, FAKE, ws, None) == -2
+    assert f(FAKE, 16, 2, 4, None, FAKE, FAKE, FAKE, ws, None) == -1
+
+
+def test_gemm_validation():
+    lib = Q.lib()
+    f = lib.quads_moe_w4a4_gemm
+    ws = lib.quads_moe_w4a4_gemm_ws(64, 256, 16, 4, 64)
+
+    def call(rows=64, k_dim=256, k=16, e=4, n=64, epi=0, odt=0, offsets=FAKE, sel=FAKE,
+             wsz=ws, out=FAKE):
+        return f(FAKE, FAKE, FAKE, None, rows, k_dim, FAKE, FAKE, FAKE, sel, k, FAKE, FAKE, FAKE,
+                 offsets, e, n, epi, odt, out, FAKE, wsz, None)
+    assert call(k_dim=250) == -2
+    assert call(k=8) == -2
+    assert call(k=512) == -2
+    assert call(e=0) == -2
+    assert call(n=63, epi=1, odt=1) == -2      # SwiGLU needs even N
+    assert call(epi=1, odt=0) == -1            # SwiGLU needs bf16 output
+    assert call(epi=7) == -1
+    assert call(offsets=None) == -1            # offsets required for E > 1
+    assert call(sel=None) == -1                # sel required for k > 0
+    assert call(out=MIS) == -1
+
+
+def test_combine_validation():
+    lib = Q.lib()
+    f = lib.quads_moe_combine
+    assert f(FAKE, 0, FAKE, FAKE, 4, 2, 12, FAKE, None) == -2     # N % 8
+    assert f(FAKE, 5, FAKE, FAKE, 4, 2, 16, FAKE, None) == -1     # dtype
+    assert f(None, 0, FAKE, FAKE, 4, 2, 16, FAKE, None) == -1

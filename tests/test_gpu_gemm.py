@@ -1,0 +1,209 @@
+"""GPU parity: grouped W4A4 GEMM with the RAC compensation term against the
+oracle.  Tolerance |y_gpu - y_oracle| <= 1e-5 * sum_i |a_i w_i| per element
+(bf16 outputs add half a bf16 ulp of the oracle value); SwiGLU within one bf16
+ulp of the oracle's SwiGLU of the GPU's own fp32 gate and up values."""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import moe as OM
+from oracle import nvfp4 as ON
+from oracle import rac as OR
+
+pytestmark = pytest.mark.gpu
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def Q():
+    import nvfp4_w4a4_quantized_act_amd as lib
+    lib.lib()
+    return lib
+
+
+def _t(a):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to("cuda:0")
+
+
+def _operands(x_bits, w_bits, k):
+    """Oracle-side quantization of the GEMM inputs (independent of the GPU)."""
+    out = OR.rac_quantize(F.bf16_to_f64(x_bits), k)
+    wp, ws, wt, _ = ON.weight_qdq(w_bits)
+    return out, (wp, ws, wt)
+
+
+def _gpu_gemm(Q, out, w, n, k, offsets=None, row_token=None, rows=None, **kw):
+    a = (_t(out["nib"]), _t(out["scale"]), _t(np.array([out["ts"]], np.float32)))
+    r = (_t(out["r_nib"]), _t(out["r_scale"]), _t(np.array([out["r_ts"]], np.float32))) \
+        if k else None
+    sel = _t(out["sel"]) if k else None
+    wt = (_t(w[0]), _t(w[1]), _t(w[2]))
+    y = Q.quads_moe_w4a4_gemm(a, wt, n, rows=rows, r=r, sel=sel,
+                              offsets=None if offsets is None else _t(offsets),
+                              row_token=None if row_token is None else _t(row_token), **kw)
+    torch.cuda.synchronize()
+    return y
+
+
+def _oracle(out, w, k, offsets, row_token=None):
+    r = (out["r_nib"], out["r_scale"], out["r_ts"]) if k else None
+    return OM.grouped_gemm((out["nib"], out["scale"], out["ts"]), r, out["sel"], w, offsets,
+                           row_token)
+
+
+def _assert_close(got, exp, bound, bf16=False):
+    err = np.abs(got - exp)
+    lim = TOL * bound
+    if bf16:
+        lim = lim + np.abs(exp) * 2.0 ** -8
+    bad = err > lim
+    assert not bad.any(), (np.argwhere(bad)[:5], err[bad][:5], lim[bad][:5])
+    return float((err / np.maximum(bound, 1e-300)).max())
+
+
+@pytest.mark.parametrize("m,kd,n,k", [(32, 256, 128, 16), (200, 272, 136, 32), (64, 512, 256, 0),
+                                      (1, 16, 1, 16), (129, 1024, 130, 64)])
+def test_dense(Q, m, kd, n, k):
+    print(f"dense gemm m={m} K={kd} N={n} k={k}", flush=True)
+    rng = np.random.default_rng(m * 7 + kd + n + k)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((m, kd)).astype(np.float32))
+    x[:, :: max(1, kd // 5)] = synth.f32_to_bf16_bits(
+        rng.standard_normal((m, len(range(0, kd, max(1, kd // 5))))).astype(np.float32) * 16)
+    w = synth.weights(rng, 1, n, kd)
+    out, wq = _operands(x, w, k)
+    y = _gpu_gemm(Q, out, wq, n, k).cpu().numpy()
+    exp, bound = _oracle(out, wq, k, [0, m])
+    _assert_close(y, exp, bound)
+
+
+def test_config1(Q):
+    d = synth.make(1)
+    out, wq = _operands(d["x"], d["w"], d["rac_k"])
+    y = _gpu_gemm(Q, out, wq, 128, d["rac_k"]).cpu().numpy()
+    exp, bound = _oracle(out, wq, d["rac_k"], [0, 32])
+    _assert_close(y, exp, bound)
+
+
+def test_all_positive_operands(Q):
+    """sum |a w| = |sum a w|: the tolerance is exercised at its edge (K = 4096)."""
+    rng = np.random.default_rng(5)
+    x = synth.f32_to_bf16_bits(np.abs(rng.standard_normal((96, 4096))).astype(np.float32))
+    w = np.abs(synth.weights(rng, 1, 64, 4096).view(np.int16)).view(np.uint16)
+    out, wq = _operands(x, w, 128)
+    y = _gpu_gemm(Q, out, wq, 64, 128).cpu().numpy()
+    exp, bound = _oracle(out, wq, 128, [0, 96])
+    rel = _assert_close(y, exp, bound)
+    print("max relative error", rel)
+
+
+def test_exact_power_of_two_scales(Q):
+    """On-grid inputs with power-of-two tensor scales and few terms: every
+    partial sum is exact in fp32, so the GPU must equal the oracle exactly."""
+    rng = np.random.default_rng(6)
+    m, kd, n = 64, 64, 64
+    sb = np.full((m, kd // 16), 0x38)                 # s_b = 1
+    mag = rng.integers(0, 8, (m, kd))
+    mag[:, ::16] = 7
+    sb[0, 0] = 0x7E
+    x = F.E2M1_MAG[mag] * np.where(rng.random((m, kd)) < .5, -1, 1) * \
+        np.repeat(F.E4M3_GRID[sb], 16, -1)
+    wm = rng.integers(0, 8, (n, kd))
+    wm[:, ::16] = 7
+    wv = F.E2M1_MAG[wm] * np.where(rng.random((n, kd)) < .5, -1, 1)
+    wv[0, 16] = 6 * 448        # the two tensor maxima never meet in one product
+    out, wq = _operands(F.f64_to_bf16_rne(x), F.f64_to_bf16_rne(wv)[None], 0)
+    y = _gpu_gemm(Q, out, wq, n, 0).cpu().numpy()
+    exp, _ = _oracle(out, wq, 0, [0, m])
+    assert np.array_equal(y.astype(np.float64), exp)
+
+
+def test_bf16_output(Q):
+    rng = np.random.default_rng(7)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((70, 320)).astype(np.float32))
+    w = synth.weights(rng, 1, 96, 320)
+    out, wq = _operands(x, w, 32)
+    y = _gpu_gemm(Q, out, wq, 96, 32, out_dtype=Q.OUT_BF16).cpu().numpy().view(np.uint16)
+    exp, bound = _oracle(out, wq, 32, [0, 70])
+    _assert_close(F.bf16_to_f64(y), exp, bound, bf16=True)
+
+
+def _moe_case(seed, t, e, topk, h, n, k):
+    rng = np.random.default_rng(seed)
+    choices = [j for j in range(e) if j != 3]          # expert 3 gets no rows
+    ids = np.stack([rng.choice(choices, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((t, h)).astype(np.float32))
+    w = synth.weights(rng, e, n, h)
+    return ids, x, w
+
+
+def test_grouped_gather_rows(Q):
+    """Packed rows gathered through row_token, uneven experts, an empty expert."""
+    ids, x, w = _moe_case(8, 150, 8, 3, 256, 192, 32)
+    off, rt, pos = OM.pack_routes(ids, 8)
+    out, wq = _operands(x, w, 32)
+    y = _gpu_gemm(Q, out, wq, 192, 32, offsets=off, row_token=rt).cpu().numpy()
+    exp, bound = _oracle(out, wq, 32, off, rt)
+    _assert_close(y, exp, bound)
+
+
+def test_grouped_swiglu(Q):
+    ids, x, w = _moe_case(9, 300, 6, 2, 192, 2 * 80, 16)
+    off, rt, pos = OM.pack_routes(ids, 6)
+    out, wq = _operands(x, w, 16)
+    g = _gpu_gemm(Q, out, wq, 160, 16, offsets=off, row_token=rt).cpu().numpy()
+    exp, bound = _oracle(out, wq, 16, off, rt)
+    _assert_close(g, exp, bound)
+    h = _gpu_gemm(Q, out, wq, 160, 16, offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
+                  out_dtype=Q.OUT_BF16).cpu().numpy().view(np.uint16)
+    ref = F.bf16_to_f64(OM.swiglu(g.astype(np.float64)))
+    got = F.bf16_to_f64(h)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp * 1.0001)
+
+
+def test_moe_config3_gate_up_sampled(Q):
+    """Full gate/up GEMM of the 128-expert layer (32768 packed rows, K = 2048,
+    N = 1536, k = 64); the oracle checks 12 experts' rows."""
+    d = synth.make(3, with_weights=False)
+    rng = np.random.default_rng(31)
+    ids = d["topk_ids"]
+    off, rt, pos = OM.pack_routes(ids, 128)
+    out = OR.rac_quantize(F.bf16_to_f64(d["x"]), 64)
+    experts = [0, 1, 17, 40, 63, 64, 90, 100, 111, 120, 126, 127]
+    # unsampled experts hold all-zero weights (codes, scales and tensor scale 0)
+    wp = np.zeros((128, 1536, 1024), np.uint8)
+    ws = np.zeros((128, 1536, 128), np.uint8)
+    wt = np.zeros(128, np.float32)
+    wsub = synth.weights(rng, len(experts), 1536, 2048)
+    for i, e in enumerate(experts):
+        wp[e], ws[e], wt[e] = ON.quantize_bf16(wsub[i])
+    print("config3 gate_up gemm", flush=True)
+    y = _gpu_gemm(Q, out, (wp, ws, wt), 1536, 64, offsets=off, row_token=rt).cpu().numpy()
+    for e in experts:
+        sub_off = np.array([0, off[e + 1] - off[e]])
+        sub_rt = rt[off[e]:off[e + 1]]
+        exp, bound = OM.grouped_gemm(
+            (out["nib"], out["scale"], out["ts"]), (out["r_nib"], out["r_scale"], out["r_ts"]),
+            out["sel"], (wp[e:e + 1], ws[e:e + 1], wt[e:e + 1]), sub_off, sub_rt)
+        _assert_close(y[off[e]:off[e + 1]], exp, bound)
+
+
+def test_dense_config2_sampled(Q):
+    """Config 2 shape (4096 x 4096 x 4096, k = 128); the oracle checks 256 rows."""
+    d = synth.make(2)
+    out, wq = _operands(d["x"], d["w"], 128)
+    print("config2 gemm", flush=True)
+    y = _gpu_gemm(Q, out, wq, 4096, 128).cpu().numpy()
+    rows = np.random.default_rng(2).choice(4096, 256, replace=False)
+    sub = dict(out)
+    for key in ("nib", "scale", "r_nib", "r_scale"):
+        sub[key] = out[key][rows]
+    exp, bound = _oracle(sub, wq, 128, [0, 256])
+    rel = _assert_close(y[rows], exp, bound)
+    print("max relative error", rel)
