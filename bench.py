@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the QUADS rollout hot path on one MI355X.
+
+Workload (the MoE expert FFN layer the GEMM target is quoted on): 128
+experts, hidden 2048, expert intermediate 768, top-8 routing, 4096 tokens,
+RAC with k = 64 channels at both GEMM inputs.  One step is one forward pass of
+the layer through the library:
+
+  quads_rac_quantize(hidden)            NVFP4 + RAC at the gate/up input
+  quads_moe_pack(topk_ids)              token -> expert packing
+  quads_moe_w4a4_gemm(gate/up, SwiGLU)  grouped W4A4 GEMM + compensation, bf16 h
+  quads_rac_quantize(h)                 NVFP4 + RAC at the down input
+  quads_moe_w4a4_gemm(down)             grouped W4A4 GEMM + compensation, bf16 out
+  quads_moe_combine                     routing-weighted sum per token
+
+The weight QDQ (quads_nvfp4_weight_qdq) runs once per weight refresh, not per
+forward pass; it is timed on its own and reported as `weight_qdq_ms`.
+
+Inputs are seeded synthetic tensors (synth.py) already resident in HBM when
+the timed region starts.  `value` is the step's algorithmic GEMM work,
+2 * rows * N * (K + k) summed over both GEMMs, divided by the step time.
+`roofline` is for the dominant kernel, the gate/up GEMM: its algorithmic
+flops per launch over its mean launch time (HIP events on the launch stream),
+against the dense fp16 MFMA peak (the GEMM's operands are exact fp16).
+`cpu_baseline` times the NumPy oracle on a bounded sample of the same layer.
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_FP16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
+
+
+def _parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a device copy of this size (for counter calibration)")
+    return ap.parse_args()
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
+                                   "part of it", "n_gpus": args.gpus}))
+        sys.exit(2)
+    cores = len(os.sched_getaffinity(0))
+    os.environ.setdefault("OPENBLAS_NUM_THREADS", str(cores))
+    import numpy as np
+    import torch
+
+    import nvfp4_w4a4_quantized_act_amd as Q
+    import synth
+
+    cfg = synth.CONFIGS[3]
+    T, E, H, I, TOPK, KR = cfg["t"], cfg["e"], cfg["h"], cfg["i"], cfg["topk"], cfg["rac_k"]
+    rows = T * TOPK
+    dev = torch.device("cuda:0")
+    Q.lib()
+
+    data = synth.make(3)
+
+    def up(a):
+        a = np.ascontiguousarray(a)
+        return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).to(dev)
+
+    x = up(data["x"])
+    ids = up(data["topk_ids"])
+    tw = up(data["topk_w"])
+    w13 = up(data["w13"])
+    w2 = up(data["w2"])
+    del data["w13"], data["w2"]
+
+    # weight QDQ, once per refresh (timed on its own)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    w13q = Q.quads_nvfp4_weight_qdq(w13)[:3]
+    w2q = Q.quads_nvfp4_weight_qdq(w2)[:3]
+    torch.cuda.synchronize()
+    ev[0].record()
+    for _ in range(3):
+        w13q = Q.quads_nvfp4_weight_qdq(w13)[:3]
+        w2q = Q.quads_nvfp4_weight_qdq(w2)[:3]
+    ev[1].record()
+    torch.cuda.synchronize()
+    weight_qdq_ms = ev[0].elapsed_time(ev[1]) / 3
+    del w13, w2
+
+    nev = 12
+    timers = []
+
+    def step(record):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)] if record else None
+
+        def mark(i):
+            if record:
+                evs[i].record()
+        mark(0)
+        a = Q.quads_rac_quantize(x, KR)
+        mark(1)
+        off, rt, pos = Q.quads_moe_pack(ids, E)
+        mark(2)
+        h = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), w13q, 2 * I, rows=rows,
+                                  r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"],
+                                  offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
+                                  out_dtype=Q.OUT_BF16)
+        mark(3)
+        b = Q.quads_rac_quantize(h, KR)
+        mark(4)
+        y2 = Q.quads_moe_w4a4_gemm((b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
+                                   r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"],
+                                   offsets=off, out_dtype=Q.OUT_BF16)
+        mark(5)
+        out = Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
+        mark(6)
+        if record:
+            timers.append(evs)
+        return out
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    names = ["rac_gate_up", "pack", "gemm_gate_up_swiglu", "rac_down", "gemm_down", "combine"]
+    per_op = {n: 0.0 for n in names}
+    for evs in timers:
+        for i, n in enumerate(names):
+            per_op[n] += evs[i].elapsed_time(evs[i + 1]) / len(timers)
+
+    fl_gu = 2.0 * rows * (2 * I) * (H + KR)
+    fl_dn = 2.0 * rows * H * (I + KR)
+    value = (fl_gu + fl_dn) / (ms_per_step * 1e-3) / 1e12
+    gu_tflops = fl_gu / (per_op["gemm_gate_up_swiglu"] * 1e-3) / 1e12
+    dn_tflops = fl_dn / (per_op["gemm_down"] * 1e-3) / 1e12
+    q_bytes_gu = 2.5625 * T * H + 0.5625 * T * KR
+    q_bytes_dn = 2.5625 * rows * I + 0.5625 * rows * KR
+    ops = {
+        "rac_gate_up": {"ms": per_op["rac_gate_up"],
+                        "GB/s": q_bytes_gu / (per_op["rac_gate_up"] * 1e-3) / 1e9},
+        "rac_down": {"ms": per_op["rac_down"],
+                     "GB/s": q_bytes_dn / (per_op["rac_down"] * 1e-3) / 1e9},
+        "pack": {"ms": per_op["pack"]},
+        "gemm_gate_up_swiglu": {"ms": per_op["gemm_gate_up_swiglu"], "TFLOP/s": gu_tflops},
+        "gemm_down": {"ms": per_op["gemm_down"], "TFLOP/s": dn_tflops},
+        "combine": {"ms": per_op["combine"]},
+    }
+    for k in ("rac_gate_up", "rac_down"):
+        ops[k]["hbm_frac"] = ops[k]["GB/s"] / PEAK_HBM_GBS
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(np, torch, data, w13q, w2q, cfg, args.cpu_sample_tokens, cores)
+
+    line = {
+        "metric": "MoE W4A4+RAC grouped-GEMM TFLOP/s & quantizer GB/s, % of MI355X roofline",
+        "value": value,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16",
+        "data": "synthetic",
+        "config": {"workload": "moe_ffn_e128_h2048_i768_top8_t4096_rac64",
+                   "tokens": T, "experts": E, "hidden": H, "intermediate": I, "top_k": TOPK,
+                   "rac_k": KR, "packed_rows": rows, "gemm_operands": "nvfp4 -> exact fp16",
+                   "accumulate": "fp32", "parallelism": "single_gpu"},
+        "roofline": {"bound": "mfma", "kernel": "k_gemm_w4a4<SWIGLU> (gate/up GEMM)",
+                     "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": None},
+        "cpu_baseline": cpu,
+        "ops": ops,
+        "weight_qdq_ms": weight_qdq_ms,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(np, torch, data, w13q, w2q, cfg, t_sample, cores):
+    """The oracle, as it stands, on the first t_sample tokens of the same layer
+    (weights: the GPU's packed NVFP4 weights, bit-identical to the oracle's
+    weight QDQ).  Returns algorithmic GEMM TFLOP/s of the sample."""
+    from oracle import formats as OF
+    from oracle import moe as OM
+    from oracle import rac as OR
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = cores
+    E, H, I, TOPK, KR = cfg["e"], cfg["h"], cfg["i"], cfg["topk"], cfg["rac_k"]
+    w13 = tuple(t.cpu().numpy() for t in w13q)
+    w2 = tuple(t.cpu().numpy() for t in w2q)
+    x = data["x"][:t_sample]
+    ids = data["topk_ids"][:t_sample]
+    tw = data["topk_w"][:t_sample]
+    rows = t_sample * TOPK
+    t0 = time.perf_counter()
+    a = OR.rac_quantize(OF.bf16_to_f64(x), KR)
+    off, rt, pos = OM.pack_routes(ids, E)
+    y1, _ = OM.grouped_gemm((a["nib"], a["scale"], a["ts"]), (a["r_nib"], a["r_scale"], a["r_ts"]),
+                            a["sel"], w13, off, rt, want_bound=False)
+    h = OM.swiglu(y1)
+    b = OR.rac_quantize(OF.bf16_to_f64(h), KR)
+    y2, _ = OM.grouped_gemm((b["nib"], b["scale"], b["ts"]), (b["r_nib"], b["r_scale"], b["r_ts"]),
+                            b["sel"], w2, off, None, want_bound=False)
+    OM.combine(y2, pos, tw, t_sample, TOPK)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * (2 * I) * (H + KR) + 2.0 * rows * H * (I + KR)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {t_sample} of 4096 tokens ({rows} packed rows), full layer "
+                      f"forward through the fp64 NumPy oracle, {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

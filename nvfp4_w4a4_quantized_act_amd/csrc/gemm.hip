@@ -159,6 +159,7 @@ __device__ __forceinline__ int w_row_of(int r, int f0, int N, bool swiglu, bool*
     return ((r >> 5) & 1) * (N / 2) + feat;
 }
 
+template <int kEpi>
 __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     __shared__ _Float16 sA[kBM * kLd];
     __shared__ _Float16 sB[kBN * kLd];
@@ -166,7 +167,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     __shared__ int s_res[4];
     int e, m0, mend;
     if (!find_tile(g.offsets, g.E, g.rows, blockIdx.y, s_scan, s_res, &e, &m0, &mend)) return;
-    const bool swiglu = g.epilogue == QUADS_EPI_SWIGLU;
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -319,8 +320,11 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
     const int64_t ntiles_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + kBN / 2 - 1) / (kBN / 2)
                                                           : (N + kBN - 1) / kBN;
     int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? E : 0);
-    hipLaunchKernelGGL(k_gemm_w4a4, dim3((unsigned)ntiles_n, (unsigned)ntiles_m), dim3(256), 0,
-                       (hipStream_t)stream, g);
+    const dim3 grid((unsigned)ntiles_n, (unsigned)ntiles_m);
+    if (epilogue == QUADS_EPI_SWIGLU)
+        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_SWIGLU>, grid, dim3(256), 0, (hipStream_t)stream, g);
+    else
+        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_NONE>, grid, dim3(256), 0, (hipStream_t)stream, g);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }
