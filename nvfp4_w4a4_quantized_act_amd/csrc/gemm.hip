@@ -44,20 +44,21 @@ struct GemmArgs {
 // (expert, first row, end row) of M-tile `tile`: experts' rows are cut into
 // tiles of kBM; tiles are numbered expert by expert.  Returns false (for the
 // whole work-group) when `tile` is past the last tile.
-__device__ bool find_tile(const int32_t* offsets, int E, int64_t rows, int tile, int* s_scan,
-                          int* s_res, int* e_out, int* m0_out, int* mend_out) {
+__device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int tile, int bm,
+                             int* s_scan, int* s_res, int* e_out, int* m0_out, int* mend_out) {
     if (offsets == nullptr) {                      // one expert, all rows
-        const int64_t m0 = (int64_t)tile * kBM;
+        const int64_t m0 = (int64_t)tile * bm;
         *e_out = 0;
         *m0_out = (int)m0;
         *mend_out = (int)rows;
         return m0 < rows;
     }
-    const int per = (E + 255) / 256;
+    const int nthr = blockDim.x;
+    const int per = (E + nthr - 1) / nthr;
     const int e0 = threadIdx.x * per;
     const int e1 = e0 + per < E ? e0 + per : E;
     int local = 0;
-    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int x = local;
     for (int off = 1; off < 64; off <<= 1) {
@@ -71,10 +72,10 @@ __device__ bool find_tile(const int32_t* offsets, int E, int64_t rows, int tile,
     for (int i = 0; i < wid; ++i) base += s_scan[i];
     int run = x - local + base;
     for (int e = e0; e < e1; ++e) {
-        const int t = (offsets[e + 1] - offsets[e] + kBM - 1) / kBM;
+        const int t = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
         if (tile >= run && tile < run + t) {     // exactly one thread matches
             s_res[0] = e;
-            s_res[1] = offsets[e] + (tile - run) * kBM;
+            s_res[1] = offsets[e] + (tile - run) * bm;
             s_res[2] = offsets[e + 1];
             s_res[3] = 1;
         }
@@ -166,7 +167,8 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     __shared__ int s_scan[8];
     __shared__ int s_res[4];
     int e, m0, mend;
-    if (!find_tile(g.offsets, g.E, g.rows, blockIdx.y, s_scan, s_res, &e, &m0, &mend)) return;
+    if (!find_tile_bm(g.offsets, g.E, g.rows, blockIdx.y, kBM, s_scan, s_res, &e, &m0, &mend))
+        return;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
 
@@ -278,6 +280,294 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     }
 }
 
+
+// ------------------------------------------------------------ big tiles --
+// 256 x 256 output tile, 512 threads = 8 waves in a 2 x 4 grid, two waves per
+// SIMD so that one wave's dequantization overlaps the other's MFMAs; each
+// wave owns a 128 x 64 sub-tile = 4 x 2 MFMA tiles.  K advances 64 channels
+// per stage through two fp16 LDS buffers (2 x 64 KB, A and W slices).
+//
+// Thread t loads half-row t%2 of A row t/2 and of W row t/2 (32 codes = 16
+// bytes + 2 scale bytes each).  Loads run two stages ahead (two register
+// sets): while the waves run the MFMAs of stage i, the thread dequantizes
+// the data of stage i+1, which arrived during stage i-1, exactly to fp16 and
+// stores it into the other LDS buffer, and the loads of stage i+2 are in
+// flight.  In a 128-byte LDS row, 16-byte chunk c sits at chunk
+// c ^ ((row >> 1) & 7), so the 16 rows served together by the 64-bank LDS
+// hit distinct banks.
+//
+// Work-group numbering: the hardware deals work-group ids round-robin over
+// the 8 XCDs, each with its own L2.  Tiles are numbered M-tile-major and cut
+// into groups of `grp` consecutive tiles (two M tiles' worth of N tiles:
+// shared activation rows, usually one expert's weights); group g of XCD x is
+// tile group 8 g + x, so every XCD walks the tile list at the same pace and
+// the (upper-bound) tail of empty tiles is shared evenly.
+//
+// Compensation (k > 0): its stages run first into the same accumulators,
+// which are then multiplied by s_tR / s_tA before the main stages; the
+// epilogue multiplies by s_tA s_tW[e].  32-row MFMA blocks past the end of
+// an expert's rows are skipped.  Requires K % 64 == 0 and k % 64 == 0.
+namespace v2 {
+
+constexpr int BM = 256, BN = 256, BK = 64;
+constexpr int kThreads = 512;
+constexpr int kStage = (BM + BN) * BK;          // halfs per LDS stage
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ int swz(int r, int c) { return r * BK + 8 * (c ^ ((r >> 1) & 7)); }
+
+struct Raw {
+    uint4 n;            // 32 fp4 codes
+    uint32_t sc;        // 2 E4M3 block scales (low 16 bits)
+};
+
+__device__ __forceinline__ Raw load_raw(const uint8_t* nib_row, const uint8_t* sc_row, int kc,
+                                        bool valid) {
+    Raw r;
+    if (valid) {
+        r.n = *reinterpret_cast<const uint4*>(nib_row + kc / 2);
+        r.sc = *reinterpret_cast<const uint16_t*>(sc_row + kc / kBlock);
+    } else {
+        r.n = make_uint4(0, 0, 0, 0);
+        r.sc = 0;
+    }
+    return r;
+}
+
+__device__ __forceinline__ f16x8 cvt8(uint32_t w, _Float16 s) {
+    const f16x2 s2 = {s, s};
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Dequantize the 32-code half-row exactly to fp16 and store it as chunks
+// 4 half .. 4 half + 3 of LDS row `row` (st = start of the A or W region).
+__device__ __forceinline__ void store_slice(const Raw& r, _Float16* st, int row, int half) {
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.sc, 1.0f, false);   // exact
+    const int c = 4 * half;
+    *reinterpret_cast<f16x8*>(st + swz(row, c + 0)) = cvt8(r.n.x, s01[0]);
+    *reinterpret_cast<f16x8*>(st + swz(row, c + 1)) = cvt8(r.n.y, s01[0]);
+    *reinterpret_cast<f16x8*>(st + swz(row, c + 2)) = cvt8(r.n.z, s01[1]);
+    *reinterpret_cast<f16x8*>(st + swz(row, c + 3)) = cvt8(r.n.w, s01[1]);
+}
+
+// Compensation W half-row: codes w[n, sel[i0 + 32 half + u]], u = 0..31, each
+// with its own block scale, stored like store_slice.
+__device__ __forceinline__ void gather_store(const uint8_t* w_nib_row, const uint8_t* w_sc_row,
+                                             const int32_t* sel, int i0, bool valid,
+                                             _Float16* st, int row, int half) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        uint32_t nb[8], sb[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = sel[i0 + 32 * half + 8 * q + u];
+            nb[u] = w_nib_row[j >> 1] >> (4 * (j & 1));
+            sb[u] = w_sc_row[j >> 4];
+        }
+        _Float16 hv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const _Float16 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb[u], 1.0f, false)[0];
+            const _Float16 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(nb[u] & 0xFu, 1.0f, 0)[0] * s;
+            hv[u] = valid ? v : (_Float16)0;
+        }
+        *reinterpret_cast<f16x8*>(st + swz(row, 4 * half + q)) =
+            (f16x8){hv[0], hv[1], hv[2], hv[3], hv[4], hv[5], hv[6], hv[7]};
+    }
+}
+
+// Per-lane LDS offset (halfs, relative to a 32-row block) of the fragment of
+// sub-step kk: row lane%32, logical chunk 2 kk + lane/32.  Block bases are
+// multiples of 32 rows, so the swizzle depends on the lane only.
+__device__ __forceinline__ int frag_off(int lane, int kk) {
+    const int r = lane & 31;
+    return r * BK + 8 * ((2 * kk + (lane >> 5)) ^ ((r >> 1) & 7));
+}
+
+// MFMAs of one 16-deep sub-step of a stage (foff = frag_off(lane, kk)).
+__device__ __forceinline__ void mma_kk(const _Float16* st, int foff, int wm, int wn, int mact,
+                                       f32x16 acc[4][2]) {
+    const _Float16* sa = st + wm * 128 * BK + foff;
+    const _Float16* sb = st + BM * BK + wn * 64 * BK + foff;
+    f16x8 a[4], b[2];
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) b[nj] = *reinterpret_cast<const f16x8*>(sb + nj * 32 * BK);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(sa + mi * 32 * BK);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi < mact) {
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+        }
+    }
+}
+
+// One stage: MFMAs on `cur` with the dequantization of (ra, rb) into `nxt`
+// spread between the sub-steps.
+__device__ __forceinline__ void stage(const _Float16* cur, _Float16* nxt, bool store,
+                                      const Raw& ra, const Raw& rb, int lr, int lh, int wm, int wn,
+                                      int mact, const int fo[4], f32x16 acc[4][2]) {
+    mma_kk(cur, fo[0], wm, wn, mact, acc);
+    mma_kk(cur, fo[1], wm, wn, mact, acc);
+    if (store) store_slice(ra, nxt, lr, lh);
+    mma_kk(cur, fo[2], wm, wn, mact, acc);
+    if (store) store_slice(rb, nxt + BM * BK, lr, lh);
+    mma_kk(cur, fo[3], wm, wn, mact, acc);
+}
+
+// Weight row of B-tile row r.  Plain: f0 + r.  SwiGLU: the tile holds 128
+// output features; in each wave's 64 rows, rows 0-31 are gate and 32-63 up
+// for the same 32 features.
+__device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool* valid) {
+    if (!swiglu) {
+        const int n = f0 + r;
+        *valid = n < N;
+        return n;
+    }
+    const int feat = f0 + (r >> 6) * 32 + (r & 31);
+    *valid = feat < N / 2;
+    return ((r >> 5) & 1) * (N / 2) + feat;
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n, int grp) {
+    __shared__ _Float16 smem[2 * kStage];
+    __shared__ int s_scan[16];
+    __shared__ int s_res[4];
+    // XCD-aware numbering: hardware id h runs on XCD h % 8
+    const int h = blockIdx.x;
+    const int slot = h / kXcds;
+    const int tile = (slot / grp) * (kXcds * grp) + (h % kXcds) * grp + slot % grp;
+    const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
+    int e, m0, mend;
+    if (!find_tile_bm(g.offsets, g.E, g.rows, tile_m, BM, s_scan, s_res, &e, &m0, &mend))
+        return;
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int f0 = tile_n * (swiglu ? BN / 2 : BN);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 2, wn = wave & 3;
+    int mact = (mend - (m0 + wm * 128) + 31) / 32;
+    mact = __builtin_amdgcn_readfirstlane(mact < 0 ? 0 : (mact > 4 ? 4 : mact));
+    const int lr = tid >> 1, lh = tid & 1;
+
+    const int p = m0 + lr;
+    const bool a_valid = p < mend;
+    const int64_t src = a_valid ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
+    bool b_valid;
+    const int wrow = w_row_v2(lr, f0, g.N, swiglu, &b_valid);
+    const int64_t wr = (int64_t)e * g.N + (b_valid ? wrow : 0);
+    const uint8_t* a_nib_row = g.a_nib + src * (g.K / 2);
+    const uint8_t* a_sc_row = g.a_scale + src * (g.K / kBlock);
+    const uint8_t* w_nib_row = g.w_nib + wr * (g.K / 2);
+    const uint8_t* w_sc_row = g.w_scale + wr * (g.K / kBlock);
+    int fo[4];
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) fo[kk] = frag_off(lane, kk);
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
+
+    // compensation stages
+    if (g.k > 0) {
+        const uint8_t* r_nib_row = g.r_nib + src * (g.k / 2);
+        const uint8_t* r_sc_row = g.r_scale + src * (g.k / kBlock);
+        for (int i0 = 0; i0 < g.k; i0 += BK) {
+            const Raw ra = load_raw(r_nib_row, r_sc_row, i0 + 32 * lh, a_valid);
+            store_slice(ra, smem, lr, lh);
+            gather_store(w_nib_row, w_sc_row, g.sel, i0, b_valid, smem + BM * BK, lr, lh);
+            __syncthreads();
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) mma_kk(smem, fo[kk], wm, wn, mact, acc);
+            __syncthreads();
+        }
+        const float s_ta = g.a_ts[0];
+        const float rho = s_ta > 0.0f ? g.r_ts[0] / s_ta : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * rho;
+    }
+
+    // main stages: LDS double buffer, loads two stages ahead
+    const int nk = g.K / BK;
+    {
+        const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, a_valid);
+        const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, b_valid);
+        store_slice(ra, smem, lr, lh);
+        store_slice(rb, smem + BM * BK, lr, lh);
+    }
+    Raw a0 = load_raw(a_nib_row, a_sc_row, (nk > 1 ? BK : 0) + 32 * lh, a_valid && nk > 1);
+    Raw b0 = load_raw(w_nib_row, w_sc_row, (nk > 1 ? BK : 0) + 32 * lh, b_valid && nk > 1);
+    Raw a1, b1;
+    __syncthreads();
+    for (int it = 0; it < nk; it += 2) {
+        // even stage `it`: LDS buffer 0; (a0, b0) hold stage it+1
+        if (it + 2 < nk) {
+            a1 = load_raw(a_nib_row, a_sc_row, (it + 2) * BK + 32 * lh, a_valid);
+            b1 = load_raw(w_nib_row, w_sc_row, (it + 2) * BK + 32 * lh, b_valid);
+        }
+        stage(smem, smem + kStage, it + 1 < nk, a0, b0, lr, lh, wm, wn, mact, fo, acc);
+        __syncthreads();
+        if (it + 1 >= nk) break;
+        // odd stage `it+1`: LDS buffer 1; (a1, b1) hold stage it+2
+        if (it + 3 < nk) {
+            a0 = load_raw(a_nib_row, a_sc_row, (it + 3) * BK + 32 * lh, a_valid);
+            b0 = load_raw(w_nib_row, w_sc_row, (it + 3) * BK + 32 * lh, b_valid);
+        }
+        stage(smem + kStage, smem, it + 2 < nk, a1, b1, lr, lh, wm, wn, mact, fo, acc);
+        __syncthreads();
+    }
+
+    // epilogue
+    const float ca = g.a_ts[0] * g.w_ts[e];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= mact) continue;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+            const int prow = m0 + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            if (prow >= mend) continue;
+            if (swiglu) {
+                const int feat = f0 + wn * 32 + (lane & 31);
+                if (feat < g.N / 2) {
+                    const float gt = acc[mi][0][v] * ca;
+                    const float up = acc[mi][1][v] * ca;
+                    const float hval = gt / (1.0f + expf(-gt)) * up;
+                    ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] =
+                        (uint16_t)bf16_rne_from_f32(hval);
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int n = f0 + wn * 64 + nj * 32 + (lane & 31);
+                    if (n >= g.N) continue;
+                    const float y = acc[mi][nj][v] * ca;
+                    const int64_t o = (int64_t)prow * g.N + n;
+                    if (g.out_bf16)
+                        ((uint16_t*)g.out)[o] = (uint16_t)bf16_rne_from_f32(y);
+                    else
+                        ((float*)g.out)[o] = y;
+                }
+            }
+        }
+    }
+}
+
+}  // namespace v2
+
 }  // namespace quads
 
 using namespace quads;
@@ -317,14 +607,31 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
                out_dtype == QUADS_OUT_BF16, out};
+    hipStream_t st = (hipStream_t)stream;
+    if (K % v2::BK == 0 && k % v2::BK == 0) {
+        const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
+                                                          : (N + v2::BN - 1) / v2::BN;
+        const int64_t nt_m = (rows + v2::BM - 1) / v2::BM + (offsets ? E : 0);
+        const int64_t grp = 2 * nt_n;
+        const int64_t span = grp * v2::kXcds;
+        const dim3 grid2((unsigned)((nt_m * nt_n + span - 1) / span * span));
+        if (epilogue == QUADS_EPI_SWIGLU)
+            hipLaunchKernelGGL(v2::k_gemm_w4a4_v2<QUADS_EPI_SWIGLU>, grid2, dim3(v2::kThreads), 0,
+                               st, g, (int)nt_n, (int)grp);
+        else
+            hipLaunchKernelGGL(v2::k_gemm_w4a4_v2<QUADS_EPI_NONE>, grid2, dim3(v2::kThreads), 0,
+                               st, g, (int)nt_n, (int)grp);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
     const int64_t ntiles_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + kBN / 2 - 1) / (kBN / 2)
                                                           : (N + kBN - 1) / kBN;
     int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? E : 0);
     const dim3 grid((unsigned)ntiles_n, (unsigned)ntiles_m);
     if (epilogue == QUADS_EPI_SWIGLU)
-        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_SWIGLU>, grid, dim3(256), 0, (hipStream_t)stream, g);
+        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_SWIGLU>, grid, dim3(256), 0, st, g);
     else
-        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_NONE>, grid, dim3(256), 0, (hipStream_t)stream, g);
+        hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_NONE>, grid, dim3(256), 0, st, g);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

@@ -123,6 +123,25 @@ def test_exact_power_of_two_scales(Q):
     assert np.array_equal(y.astype(np.float64), exp)
 
 
+@pytest.mark.parametrize("kd", [320, 256])
+def test_extreme_dynamic_range(Q, kd):
+    """Blocks far below the tensor maximum get subnormal or zero E4M3 scales;
+    one row is all zero."""
+    rng = np.random.default_rng(kd)
+    x = rng.standard_normal((90, kd)).astype(np.float32)
+    x *= np.exp2(rng.integers(-14, 1, (90, kd // 16))).repeat(16, axis=1).astype(np.float32)
+    x[3] = 0
+    x[0, 0] = 64.0
+    w = synth.weights(rng, 1, 72, kd)
+    w[0, :, 16:32] = synth.f32_to_bf16_bits(
+        rng.standard_normal((72, 16)).astype(np.float32) * np.float32(1e-7))
+    out, wq = _operands(synth.f32_to_bf16_bits(x), w, 64)
+    assert (out["scale"] < 8).any() and (wq[1] < 8).any()        # subnormal scales present
+    y = _gpu_gemm(Q, out, wq, 72, 64).cpu().numpy()
+    exp, bound = _oracle(out, wq, 64, [0, 90])
+    _assert_close(y, exp, bound)
+
+
 def test_bf16_output(Q):
     rng = np.random.default_rng(7)
     x = synth.f32_to_bf16_bits(rng.standard_normal((70, 320)).astype(np.float32))
@@ -142,24 +161,28 @@ def _moe_case(seed, t, e, topk, h, n, k):
     return ids, x, w
 
 
-def test_grouped_gather_rows(Q):
-    """Packed rows gathered through row_token, uneven experts, an empty expert."""
-    ids, x, w = _moe_case(8, 150, 8, 3, 256, 192, 32)
+@pytest.mark.parametrize("t,h,n,k", [(150, 256, 192, 32), (400, 256, 320, 64), (700, 512, 96, 128)])
+def test_grouped_gather_rows(Q, t, h, n, k):
+    """Packed rows gathered through row_token, uneven experts (several 256-row
+    tiles and ragged tails), an empty expert; both tilings (k % 64 != 0 and
+    == 0)."""
+    ids, x, w = _moe_case(8 + t, t, 8, 3, h, n, k)
     off, rt, pos = OM.pack_routes(ids, 8)
-    out, wq = _operands(x, w, 32)
-    y = _gpu_gemm(Q, out, wq, 192, 32, offsets=off, row_token=rt).cpu().numpy()
-    exp, bound = _oracle(out, wq, 32, off, rt)
+    out, wq = _operands(x, w, k)
+    y = _gpu_gemm(Q, out, wq, n, k, offsets=off, row_token=rt).cpu().numpy()
+    exp, bound = _oracle(out, wq, k, off, rt)
     _assert_close(y, exp, bound)
 
 
-def test_grouped_swiglu(Q):
-    ids, x, w = _moe_case(9, 300, 6, 2, 192, 2 * 80, 16)
+@pytest.mark.parametrize("k,h,feat", [(16, 192, 80), (64, 256, 200), (0, 128, 64)])
+def test_grouped_swiglu(Q, k, h, feat):
+    ids, x, w = _moe_case(9 + k, 600, 6, 2, h, 2 * feat, k)
     off, rt, pos = OM.pack_routes(ids, 6)
-    out, wq = _operands(x, w, 16)
-    g = _gpu_gemm(Q, out, wq, 160, 16, offsets=off, row_token=rt).cpu().numpy()
-    exp, bound = _oracle(out, wq, 16, off, rt)
+    out, wq = _operands(x, w, k)
+    g = _gpu_gemm(Q, out, wq, 2 * feat, k, offsets=off, row_token=rt).cpu().numpy()
+    exp, bound = _oracle(out, wq, k, off, rt)
     _assert_close(g, exp, bound)
-    h = _gpu_gemm(Q, out, wq, 160, 16, offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
+    h = _gpu_gemm(Q, out, wq, 2 * feat, k, offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
                   out_dtype=Q.OUT_BF16).cpu().numpy().view(np.uint16)
     ref = F.bf16_to_f64(OM.swiglu(g.astype(np.float64)))
     got = F.bf16_to_f64(h)
