@@ -145,7 +145,10 @@ int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, int32_t E,
  *   row_token  NULL: row(p) = p (Ta = rows);  else int32 [rows], row(p) =
  *              row_token[p] < Ta
  *   r_nib, r_scale, r_ts, sel, k   second pass (quads_rac_quantize layout);
- *              k == 0 gives plain W4A4 and these may be NULL
+ *              sel must be strictly ascending in [0, K) (as quads_rac_quantize
+ *              writes it; other values give undefined results, never
+ *              out-of-bounds accesses); k == 0 gives plain W4A4 and these may
+ *              be NULL
  *   w_nib, w_scale, w_ts   weights [E, N, K/2], [E, N, K/16], fp32 [E]
  *   offsets    int32 [E+1] with offsets[0] = 0, offsets[E] = rows,
  *              non-decreasing; NULL only when E == 1 (all rows, expert 0)

@@ -220,7 +220,8 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
                 const int i = i0 + 32 * lh + u;
                 float v = 0.0f;
                 if (b_valid && i < g.k) {
-                    const int j = g.sel[i];
+                    int j = g.sel[i];
+                    j = j < 0 ? 0 : (j >= g.K ? g.K - 1 : j);   // bounds only
                     const uint32_t code = (w_nib_row[j >> 1] >> (4 * (j & 1))) & 0xFu;
                     v = e2m1_value(code & 7u) * e4m3_value(w_sc_row[j >> 4]);
                     if (code & 8u) v = -v;
@@ -357,14 +358,15 @@ __device__ __forceinline__ void store_slice(const Raw& r, _Float16* st, int row,
 // Compensation W half-row: codes w[n, sel[i0 + 32 half + u]], u = 0..31, each
 // with its own block scale, stored like store_slice.
 __device__ __forceinline__ void gather_store(const uint8_t* w_nib_row, const uint8_t* w_sc_row,
-                                             const int32_t* sel, int i0, bool valid,
+                                             const int32_t* sel, int i0, int kdim, bool valid,
                                              _Float16* st, int row, int half) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         uint32_t nb[8], sb[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-            const int j = sel[i0 + 32 * half + 8 * q + u];
+            int j = sel[i0 + 32 * half + 8 * q + u];
+            j = j < 0 ? 0 : (j >= kdim ? kdim - 1 : j);      // bounds only; sel must be in [0, K)
             nb[u] = w_nib_row[j >> 1] >> (4 * (j & 1));
             sb[u] = w_sc_row[j >> 4];
         }
@@ -485,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
         for (int i0 = 0; i0 < g.k; i0 += BK) {
             const Raw ra = load_raw(r_nib_row, r_sc_row, i0 + 32 * lh, a_valid);
             store_slice(ra, smem, lr, lh);
-            gather_store(w_nib_row, w_sc_row, g.sel, i0, b_valid, smem + BM * BK, lr, lh);
+            gather_store(w_nib_row, w_sc_row, g.sel, i0, g.K, b_valid, smem + BM * BK, lr, lh);
             __syncthreads();
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk) mma_kk(smem, fo[kk], wm, wn, mact, acc);

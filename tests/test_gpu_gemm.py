@@ -230,3 +230,29 @@ def test_dense_config2_sampled(Q):
     exp, bound = _oracle(sub, wq, 128, [0, 256])
     rel = _assert_close(y[rows], exp, bound)
     print("max relative error", rel)
+
+
+def test_tiny_residual_scale_fallback(Q):
+    """s_tR / s_tA below 2^-60: the compensation runs before the main loop (the
+    in-loop rescaling could overflow); results must still match."""
+    rng = np.random.default_rng(41)
+    x = (rng.standard_normal((80, 256)) * 2.0 ** -10).astype(np.float32)
+    x[:, :16] = 0.0
+    x[0, 0] = 2688.0 * 2.0 ** 50        # s_t = 2^50 exactly, so this element has r = 0
+    out, wq = _operands(synth.f32_to_bf16_bits(x), synth.weights(rng, 1, 64, 256), 64)
+    assert out["r_ts"] / out["ts"] < 2.0 ** -60
+    y = _gpu_gemm(Q, out, wq, 64, 64).cpu().numpy()
+    exp, bound = _oracle(out, wq, 64, [0, 80])
+    _assert_close(y, exp, bound)
+
+
+@pytest.mark.parametrize("k", [64, 192])
+def test_compensation_chunks_across_stages(Q, k):
+    """Selected channels spread over many K stages, several 64-column chunks."""
+    rng = np.random.default_rng(42 + k)
+    x = rng.standard_normal((300, 1024)).astype(np.float32)
+    x[:, rng.choice(1024, 40, replace=False)] *= 30
+    out, wq = _operands(synth.f32_to_bf16_bits(x), synth.weights(rng, 1, 320, 1024), k)
+    y = _gpu_gemm(Q, out, wq, 320, k).cpu().numpy()
+    exp, bound = _oracle(out, wq, k, [0, 300])
+    _assert_close(y, exp, bound)
