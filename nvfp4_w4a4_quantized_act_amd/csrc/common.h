@@ -168,15 +168,98 @@ __device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, i
     }
 }
 
-// Threshold table: s_thr[c][0..6] for block-scale code c = 0..126.
-__device__ __forceinline__ void build_threshold_table(float s_t, uint32_t (*s_thr)[8]) {
-    for (int c = threadIdx.x; c <= kE4m3MaxCode; c += blockDim.x) {
-        uint32_t thr[7];
-        e2m1_thresholds(e4m3_value((uint32_t)c), s_t, thr);
-#pragma unroll
-        for (int i = 0; i < 7; ++i) s_thr[c][i] = thr[i];
-        s_thr[c][7] = 0x7F800000u;
+// Per-tensor code table, one 32-byte row per block-scale code c = 0..126
+// (row 127 unused): words 0..6 are the exact element-code thresholds of
+// e2m1_thresholds, word 7 is the fast-path multiplier (fp32 bits) or
+// kSlowPath.
+//
+// Fast path: for bf16 |x| in a block with scale code c, the hardware E2M1
+// conversion of RN32(x * mul) (round to nearest even, saturating, sign kept)
+// gives exactly the code the thresholds give, for every bf16 input.  Both
+// RN32(a * mul) and the conversion are monotone in a, so it suffices that for
+// each boundary i the largest bf16 value at or below threshold i converts to
+// a code <= i and the smallest bf16 value above it to a code >= i + 1.  The
+// table builder tries mul = RN32(1 / (s_b s_t)) and its neighbours up to two
+// ulps away and checks exactly that, with the same instruction the kernels
+// use; codes where no candidate passes keep the exact compare path.
+constexpr uint32_t kSlowPath = 0xFFFFFFFFu;
+
+__device__ __forceinline__ uint32_t fast_code(float a, float mul) {
+    return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a * mul, 0.0f, 1.0f, 0) & 0xFu;
+}
+
+__device__ __forceinline__ void build_table_row(int c, float s_t, bool allow_fast,
+                                                uint32_t* row) {
+    uint32_t thr[7];
+    const float s_b = e4m3_value((uint32_t)c);
+    e2m1_thresholds(s_b, s_t, thr);
+    uint32_t mul = kSlowPath;
+    if (!(s_b > 0.0f) || !(s_t > 0.0f)) {
+        mul = 0u;                                   // every code is 0 (sign kept)
+    } else if (allow_fast) {
+        const float r0 = (float)(1.0 / ((double)s_b * (double)s_t));
+        if (r0 > 0.0f && r0 < 3.0e38f) {
+            const int offs[5] = {0, -1, 1, -2, 2};
+            for (int q = 0; q < 5 && mul == kSlowPath; ++q) {
+                const float r = __uint_as_float(__float_as_uint(r0) + offs[q]);
+                bool ok = true;
+                for (int i = 0; i < 7; ++i) {
+                    const uint32_t lo = thr[i] & 0xFFFF0000u;   // largest bf16 <= threshold
+                    const uint32_t hi = lo + 0x10000u;           // smallest bf16 above it
+                    ok = ok && fast_code(__uint_as_float(lo), r) <= (uint32_t)i;
+                    if (hi < 0x7F800000u)
+                        ok = ok && fast_code(__uint_as_float(hi), r) >= (uint32_t)(i + 1);
+                }
+                if (ok) mul = __float_as_uint(r);
+            }
+        }
     }
+#pragma unroll
+    for (int i = 0; i < 7; ++i) row[i] = thr[i];
+    row[7] = mul;
+}
+
+// Threshold table in LDS or global memory: s_thr[c][0..7] for c = 0..126.
+__device__ __forceinline__ void build_threshold_table(float s_t, uint32_t (*s_thr)[8],
+                                                      bool allow_fast = false) {
+    for (int c = threadIdx.x; c <= kE4m3MaxCode; c += blockDim.x)
+        build_table_row(c, s_t, allow_fast, s_thr[c]);
+}
+
+// 16 codes of one block (bf16 bits in w[8], two per word) with the table row
+// of its scale: 8 packed bytes (even channel in the low nibble).
+__device__ __forceinline__ uint2 encode_block_bf16(const uint32_t w[8], const uint4 t0,
+                                                   const uint4 t1) {
+    uint32_t packed[2] = {0u, 0u};
+    if (t1.w != kSlowPath) {
+        const float mul = __uint_as_float(t1.w);
+#define QUADS_ENC_PAIR(e, sel)                                                           \
+    packed[(e) >> 2] = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(                          \
+        packed[(e) >> 2], __uint_as_float(w[e] << 16) * mul,                              \
+        __uint_as_float(w[e] & 0xFFFF0000u) * mul, 1.0f, sel)
+        QUADS_ENC_PAIR(0, 0); QUADS_ENC_PAIR(1, 1); QUADS_ENC_PAIR(2, 2); QUADS_ENC_PAIR(3, 3);
+        QUADS_ENC_PAIR(4, 0); QUADS_ENC_PAIR(5, 1); QUADS_ENC_PAIR(6, 2); QUADS_ENC_PAIR(7, 3);
+#undef QUADS_ENC_PAIR
+    } else {
+        const uint32_t thr[7] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z};
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            const uint32_t code = e2m1_mag_code((h & 0x7FFFu) << 16, thr) | ((h >> 12) & 8u);
+            packed[e >> 3] |= code << (4 * (e & 7));
+        }
+    }
+    return make_uint2(packed[0], packed[1]);
+}
+
+// Exact signed value v (E2M1, unscaled) of the 8 codes in one packed word.
+__device__ __forceinline__ void decode8(uint32_t w, float v[8]) {
+    const auto p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const auto p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const auto p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const auto p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    v[0] = p0[0]; v[1] = p0[1]; v[2] = p1[0]; v[3] = p1[1];
+    v[4] = p2[0]; v[5] = p2[1]; v[6] = p3[0]; v[7] = p3[1];
 }
 
 // ------------------------------------------------------------------ host --
@@ -201,6 +284,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_t* partial,
                          int groups, hipStream_t s);
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+// Tensor scale and code table per segment (1024 words of `table` each).
+void launch_scale_finalize(const uint32_t* partial, int groups, const float* ts_in, int nseg,
+                           float* ts_out, uint32_t* table, hipStream_t s);
 
 // Number of work-groups of the partial-max pass for n elements.
 inline int amax_groups(int64_t n) {

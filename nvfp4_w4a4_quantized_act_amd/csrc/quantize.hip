@@ -40,19 +40,35 @@ __global__ __launch_bounds__(256) void k_amax_partial(const uint16_t* __restrict
     }
 }
 
-// Quantize segment blockIdx.y (rows x K elements, contiguous) of bf16 x.
-__global__ __launch_bounds__(256) void k_quantize_bf16(
-    const uint16_t* __restrict__ x, int64_t seg_elems, const uint32_t* __restrict__ partial,
-    int groups, const float* __restrict__ ts_in, uint8_t* __restrict__ nib,
-    uint8_t* __restrict__ scale, float* __restrict__ ts_out, uint16_t* __restrict__ dq) {
-    __shared__ uint32_t s_thr[kE4m3MaxCode + 1][8];
+// Tensor scale and code table of segment blockIdx.x, once per tensor:
+// s_t = RN32(max|x| / 2688) from the partial maxima (or the caller's fixed
+// scale), then the 127-row code table (see build_table_row).
+__global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restrict__ partial,
+                                                        int groups, const float* __restrict__ ts_in,
+                                                        float* __restrict__ ts_out,
+                                                        uint32_t* __restrict__ table) {
     __shared__ float s_st;
-    const int seg = blockIdx.y;
+    const int seg = blockIdx.x;
     tensor_scale_prologue(partial, groups, ts_in, seg, &s_st);
     __syncthreads();
     const float s_t = s_st;
-    if (blockIdx.x == 0 && threadIdx.x == 0) ts_out[seg] = s_t;
-    build_threshold_table(s_t, s_thr);
+    if (threadIdx.x == 0) ts_out[seg] = s_t;
+    // a fixed caller scale may let |x| * mul overflow: keep the exact path then
+    build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(table + (int64_t)seg * 1024),
+                          ts_in == nullptr);
+}
+
+// Quantize segment blockIdx.y (rows x K elements, contiguous) of bf16 x with
+// the tensor scale ts[seg] and code table of k_scale_finalize.
+__global__ __launch_bounds__(256) void k_quantize_bf16(
+    const uint16_t* __restrict__ x, int64_t seg_elems, const float* __restrict__ ts,
+    const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
+    uint16_t* __restrict__ dq) {
+    __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
+    const int seg = blockIdx.y;
+    const uint4* tg = reinterpret_cast<const uint4*>(table + (int64_t)seg * 1024);
+    for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x) s_tab[i] = tg[i];
+    const float s_t = ts[seg];
     __syncthreads();
 
     const int64_t nblk = seg_elems / kBlock;
@@ -64,47 +80,29 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
         const uint4* p = reinterpret_cast<const uint4*>(xs + b * kBlock);
-        uint4 q0 = ld_stream16(p);
-        uint4 q1 = ld_stream16(p + 1);
-        uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+        const uint4 q0 = ld_stream16(p);
+        const uint4 q1 = ld_stream16(p + 1);
+        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
         uint32_t am = 0;
 #pragma unroll
         for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
-        uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+        const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
         const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
         const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
-        uint32_t thr[7];
-        {
-            uint4 t0 = *reinterpret_cast<const uint4*>(&s_thr[sb][0]);
-            uint4 t1 = *reinterpret_cast<const uint4*>(&s_thr[sb][4]);
-            thr[0] = t0.x; thr[1] = t0.y; thr[2] = t0.z; thr[3] = t0.w;
-            thr[4] = t1.x; thr[5] = t1.y; thr[6] = t1.z;
-        }
-        uint32_t packed[2] = {0u, 0u};
-        uint32_t mags[16];
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const uint32_t mag = e2m1_mag_code((h & 0x7FFFu) << 16, thr);
-            mags[e] = mag | ((h >> 12) & 8u);
-            packed[e >> 3] |= mags[e] << (4 * (e & 7));
-        }
-        *reinterpret_cast<uint2*>(ns + b * 8) = make_uint2(packed[0], packed[1]);
+        const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
+        *reinterpret_cast<uint2*>(ns + b * 8) = packed;
         ss[b] = (uint8_t)sb;
         if (ds) {
             const float s_b = e4m3_value(sb);
+            float v[16];
+            decode8(packed.x, v);
+            decode8(packed.y, v + 8);
             uint32_t o[8];
 #pragma unroll
             for (int e = 0; e < 16; e += 2) {
-                uint32_t r2[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const uint32_t c = mags[e + u];
-                    float v = e2m1_value(c & 7u) * s_b;                 // exact
-                    if (c & 8u) v = -v;
-                    r2[u] = bf16_rne_from_f64((double)v * (double)s_t);  // exact product
-                }
-                o[e >> 1] = r2[0] | (r2[1] << 16);
+                const uint32_t r0 = bf16_rne_from_f64((double)(v[e] * s_b) * (double)s_t);
+                const uint32_t r1 = bf16_rne_from_f64((double)(v[e + 1] * s_b) * (double)s_t);
+                o[e >> 1] = r0 | (r1 << 16);                  // v*s_b exact; product exact
             }
             uint4* dp = reinterpret_cast<uint4*>(ds + b * kBlock);
             dp[0] = make_uint4(o[0], o[1], o[2], o[3]);
@@ -123,6 +121,12 @@ void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_
     hipLaunchKernelGGL(k_amax_partial, dim3(groups, nseg), dim3(256), 0, s, x, seg_elems, partial);
 }
 
+void launch_scale_finalize(const uint32_t* partial, int groups, const float* ts_in, int nseg,
+                           float* ts_out, uint32_t* table, hipStream_t s) {
+    hipLaunchKernelGGL(k_scale_finalize, dim3(nseg), dim3(128), 0, s, partial, groups, ts_in,
+                       ts_out, table);
+}
+
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
     if (n > 0)
         hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p,
@@ -139,9 +143,15 @@ int quant_grid(int64_t nblk) {
 
 using namespace quads;
 
+// Workspace: partial maxima (kAmaxGroups words) then the code table (1024
+// words) per segment.
+static size_t quant_ws_bytes(int64_t nseg) {
+    return align_up((size_t)nseg * kAmaxGroups * 4, 256) + align_up((size_t)nseg * 1024 * 4, 256);
+}
+
 extern "C" size_t quads_nvfp4_quantize_ws(int64_t M, int64_t K) {
     (void)M; (void)K;
-    return align_up(kAmaxGroups * sizeof(uint32_t), 256);
+    return quant_ws_bytes(1);
 }
 
 extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* ts_in,
@@ -159,14 +169,17 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     }
     const int64_t n = M * K;
     uint32_t* partial = static_cast<uint32_t*>(ws);
+    uint32_t* table = partial + align_up(kAmaxGroups * 4, 256) / 4;
     int groups = 1;
     if (!ts_in) {
         groups = amax_groups(n);
         hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial);
         QUADS_CHECK_LAUNCH();
     }
+    launch_scale_finalize(partial, groups, ts_in, 1, ts_out, table, s);
+    QUADS_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_quantize_bf16, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
-                       partial, groups, ts_in, nib, scale, ts_out, (uint16_t*)nullptr);
+                       ts_out, table, nib, scale, (uint16_t*)nullptr);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }
@@ -174,7 +187,7 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
 extern "C" size_t quads_nvfp4_weight_qdq_ws(int64_t E, int64_t N, int64_t K) {
     (void)N; (void)K;
     if (E < 1) return 0;
-    return align_up((size_t)E * kAmaxGroups * sizeof(uint32_t), 256);
+    return quant_ws_bytes(E);
 }
 
 extern "C" int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, int64_t K,
@@ -194,13 +207,16 @@ extern "C" int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, i
     const int64_t n = N * K;
     int groups = amax_groups(n);
     uint32_t* partial = static_cast<uint32_t*>(ws);
+    uint32_t* table = partial + align_up((size_t)E * kAmaxGroups * 4, 256) / 4;
     hipLaunchKernelGGL(k_amax_partial, dim3(groups, (unsigned)E), dim3(256), 0, s, w, n, partial);
+    QUADS_CHECK_LAUNCH();
+    launch_scale_finalize(partial, groups, nullptr, (int)E, w_ts, table, s);
     QUADS_CHECK_LAUNCH();
     int64_t qg = quant_grid(n / kBlock);
     int64_t cap = (4096 + E - 1) / E;
     if (qg > cap) qg = cap < 1 ? 1 : cap;
     hipLaunchKernelGGL(k_quantize_bf16, dim3((unsigned)qg, (unsigned)E), dim3(256), 0, s, w, n,
-                       partial, groups, (const float*)nullptr, w_nib, w_scale, w_ts, w_dq);
+                       w_ts, table, w_nib, w_scale, w_dq);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

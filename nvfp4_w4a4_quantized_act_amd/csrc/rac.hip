@@ -1,101 +1,105 @@
 // Residual Activation Compensation (arXiv 2607.15810, section 3.3).
 //
-//  pass 1  (one 64-token x 64-channel tile per work-group): NVFP4 of x as in
-//          the quantizer, the fp32 residual r = x - DQ(Q(x)) (Eq. (20), sign
-//          flipped) with one fused multiply-add, then per channel the
-//          in-order fp64 sum of r^2 over the tile's 64 tokens and max |r|.
+//  scale   the tensor scale and code table of x, once (as in the quantizer).
+//  pass 1  (64-token x 256-channel tiles; a work-group walks several token
+//          chunks of one channel slice): NVFP4 of x as in the quantizer, the
+//          fp32 residual r = x - DQ(Q(x)) (Eq. (20), sign flipped) with one
+//          fused multiply-add, staged in LDS, then per channel the in-order
+//          fp64 sum of r^2 over the chunk's 64 tokens and max |r|.
 //  levels  the 64-ary fixed-order tree over those per-tile partials, one
 //          launch per level, until one score per channel is left (Eq. (23)).
 //  select  one work-group: radix select of the k largest scores (Eq. (24)),
 //          ties to the lower index, written ascending; the tensor scale of
-//          the gathered residual from the per-channel maxima.
-//  pass 2  gathers r[:, S] (recomputed from x, the codes and the block
-//          scales of pass 1) and NVFP4-quantizes it in 16-blocks along the
-//          compacted index (the second term of Eq. (21)).
+//          the gathered residual from the per-channel maxima, and its code
+//          table (exact compare path: the residual is fp32, not bf16).
+//  pass 2  one thread per element of r[:, S] (recomputed from x, the codes
+//          and the block scales of pass 1), NVFP4-quantized in 16-blocks along
+//          the compacted index (the second term of Eq. (21)).
 #include "common.h"
 
 namespace quads {
 
 constexpr int kTileRows = 64;          // == kScoreFanin: one level-0 group
-constexpr int kTileCols = 64;
 constexpr int kRacMaxK = 8192;         // channels handled by the select kernel
 
 // ------------------------------------------------------------------ pass 1 --
+// Tile: 64 tokens x 256 channels.  Thread t quantizes 4 blocks (tile rows
+// t/16 + 16 q, channel block t%16), keeps the fp32 residuals in LDS, then
+// owns channel t of the tile for the in-order sum over the 64 tokens.
+constexpr int kP1Cols = 256;
+
 __global__ __launch_bounds__(256) void k_rac_pass1(
-    const uint16_t* __restrict__ x, int64_t M, int K, const uint32_t* __restrict__ partial,
-    int groups, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale, float* __restrict__ ts,
+    const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ ts,
+    const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
     double* __restrict__ p0, uint32_t* __restrict__ cm0) {
-    __shared__ uint32_t s_thr[kE4m3MaxCode + 1][8];
-    __shared__ double s_r2[kTileRows][kTileCols + 1];
-    __shared__ uint32_t s_ra[kTileRows][kTileCols + 1];
-    __shared__ float s_st;
-    tensor_scale_prologue(partial, groups, nullptr, 0, &s_st);
-    __syncthreads();
-    const float s_t = s_st;
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts[0] = s_t;
-    build_threshold_table(s_t, s_thr);
+    __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
+    __shared__ float s_r[kTileRows][kP1Cols + 4];
+    for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x)
+        s_tab[i] = reinterpret_cast<const uint4*>(table)[i];
+    const float s_t = ts[0];
+    const double six_st = 6.0 * (double)s_t;
     __syncthreads();
 
-    const int rl = threadIdx.x >> 2;                 // tile row 0..63
-    const int cb = threadIdx.x & 3;                  // 16-channel block in the tile
-    const int64_t row = (int64_t)blockIdx.x * kTileRows + rl;
-    const int c0 = blockIdx.y * kTileCols + cb * kBlock;
-    float r[16];
-    if (row < M && c0 < K) {
-        const int64_t b = (row * K + c0) / kBlock;   // block index in the tensor
-        const uint4* p = reinterpret_cast<const uint4*>(x + row * K + c0);
-        uint4 q0 = ld_stream16(p);
-        uint4 q1 = ld_stream16(p + 1);
-        uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        uint32_t am = 0;
+    const int cb = threadIdx.x & 15;                 // 16-channel block in the tile
+    const int c0 = blockIdx.y * kP1Cols + cb * kBlock;
+    const int gc = blockIdx.y * kP1Cols + threadIdx.x;
+    const int64_t nchunk = (M + kTileRows - 1) / kTileRows;
+    for (int64_t ch = blockIdx.x; ch < nchunk; ch += gridDim.x) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
-        uint32_t lo = am & 0xFFFFu, hi = am >> 16;
-        const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
-        const uint32_t sb =
-            s_t > 0.0f ? e4m3_rne_code((double)amax_b / (6.0 * (double)s_t)) : 0u;
-        uint32_t thr[7];
-        {
-            uint4 t0 = *reinterpret_cast<const uint4*>(&s_thr[sb][0]);
-            uint4 t1 = *reinterpret_cast<const uint4*>(&s_thr[sb][4]);
-            thr[0] = t0.x; thr[1] = t0.y; thr[2] = t0.z; thr[3] = t0.w;
-            thr[4] = t1.x; thr[5] = t1.y; thr[6] = t1.z;
+        for (int q = 0; q < 4; ++q) {
+            const int rl = (threadIdx.x >> 4) + 16 * q;
+            const int64_t row = ch * kTileRows + rl;
+            float r[16];
+            if (row < M && c0 < K) {
+                const int64_t b = (row * K + c0) / kBlock;
+                const uint4* p = reinterpret_cast<const uint4*>(x + row * K + c0);
+                const uint4 q0 = ld_stream16(p);
+                const uint4 q1 = ld_stream16(p + 1);
+                const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                uint32_t am = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
+                const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+                const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
+                const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
+                const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
+                *reinterpret_cast<uint2*>(nib + b * 8) = packed;
+                scale[b] = (uint8_t)sb;
+                const float s_b = e4m3_value(sb);
+                float v[16];
+                decode8(packed.x, v);
+                decode8(packed.y, v + 8);
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float xv =
+                        __uint_as_float(e & 1 ? w[e >> 1] & 0xFFFF0000u : w[e >> 1] << 16);
+                    r[e] = fmaf(-(v[e] * s_b), s_t, xv);    // RN32(x - v s_b s_t), v s_b exact
+                }
+            } else {
+#pragma unroll
+                for (int e = 0; e < 16; ++e) r[e] = 0.0f;
+            }
+#pragma unroll
+            for (int e = 0; e < 16; e += 4)
+                *reinterpret_cast<float4*>(&s_r[rl][cb * kBlock + e]) =
+                    make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
         }
-        const float s_b = e4m3_value(sb);
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t h = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
-            const uint32_t mag = e2m1_mag_code((h & 0x7FFFu) << 16, thr);
-            const uint32_t code = mag | ((h >> 12) & 8u);
-            packed[e >> 3] |= code << (4 * (e & 7));
-            float sv = e2m1_value(mag) * s_b;                      // exact
-            if (code & 8u) sv = -sv;
-            r[e] = fmaf(-sv, s_t, bf16_to_f32(h));                  // RN32(x - v s_b s_t)
-        }
-        *reinterpret_cast<uint2*>(nib + b * 8) = make_uint2(packed[0], packed[1]);
-        scale[b] = (uint8_t)sb;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 16; ++e) r[e] = 0.0f;
-    }
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-        const double rd = (double)r[e];
-        s_r2[rl][cb * kBlock + e] = rd * rd;                         // exact
-        s_ra[rl][cb * kBlock + e] = __float_as_uint(r[e]) & 0x7FFFFFFFu;
-    }
-    __syncthreads();
-    const int col = threadIdx.x & 63;
-    const int gc = blockIdx.y * kTileCols + col;
-    if (threadIdx.x < 64) {
+        __syncthreads();
         double acc = 0.0;
-        for (int i = 0; i < kTileRows; ++i) acc = acc + s_r2[i][col];   // token order
-        if (gc < K) p0[(int64_t)blockIdx.x * K + gc] = acc;
-    } else if (threadIdx.x < 128) {
         uint32_t m = 0;
-        for (int i = 0; i < kTileRows; ++i) m = s_ra[i][col] > m ? s_ra[i][col] : m;
-        if (gc < K) cm0[(int64_t)blockIdx.x * K + gc] = m;
+#pragma unroll 16
+        for (int i = 0; i < kTileRows; ++i) {                 // token order
+            const float rv = s_r[i][threadIdx.x];
+            const double rd = (double)rv;
+            acc = acc + rd * rd;                              // r^2 exact in fp64
+            const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
+            m = ab > m ? ab : m;
+        }
+        if (gc < K) {
+            p0[ch * K + gc] = acc;
+            cm0[ch * K + gc] = m;
+        }
+        __syncthreads();
     }
 }
 
@@ -113,10 +117,23 @@ __global__ __launch_bounds__(256) void k_tree_level(const double* __restrict__ i
     const int64_t r1 = r0 + kScoreFanin < n ? r0 + kScoreFanin : n;
     double acc = 0.0;
     uint32_t m = 0;
-    for (int64_t r = r0; r < r1; ++r) {
-        acc = acc + in[r * K + c];
-        const uint32_t v = cin[r * K + c];
-        m = v > m ? v : m;
+    if (r1 - r0 == kScoreFanin) {
+        double v[kScoreFanin];
+#pragma unroll
+        for (int i = 0; i < kScoreFanin; ++i) v[i] = in[(r0 + i) * K + c];   // loads first
+#pragma unroll
+        for (int i = 0; i < kScoreFanin; ++i) acc = acc + v[i];              // then the chain
+#pragma unroll 16
+        for (int i = 0; i < kScoreFanin; ++i) {
+            const uint32_t u = cin[(r0 + i) * K + c];
+            m = u > m ? u : m;
+        }
+    } else {
+        for (int64_t r = r0; r < r1; ++r) {
+            acc = acc + in[r * K + c];
+            const uint32_t u = cin[r * K + c];
+            m = u > m ? u : m;
+        }
     }
     out[g * K + c] = acc;
     cout[g * K + c] = m;
@@ -155,13 +172,15 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
                                                      const uint32_t* __restrict__ colmax, int K,
                                                      int k, int32_t* __restrict__ sel,
                                                      float* __restrict__ r_ts,
-                                                     double* __restrict__ score_out) {
+                                                     double* __restrict__ score_out,
+                                                     uint32_t* __restrict__ r_table) {
     __shared__ unsigned long long s_key[kRacMaxK];
     __shared__ int s_hist[256];
     __shared__ int s_tmp[40];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_need;
     __shared__ uint32_t s_amax[16];
+    __shared__ float s_rts;
     const int tid = threadIdx.x;
     for (int j = tid; j < K; j += 1024) {
         const double v = score[j];
@@ -181,14 +200,34 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
             if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xFF)], 1);
         }
         __syncthreads();
-        if (tid == 0) {
-            int need = s_need, d = 255;
-            for (; d > 0; --d) {
-                if (s_hist[d] >= need) break;
-                need -= s_hist[d];
+        if (tid < 64) {
+            // lane l owns bins 255-4l .. 252-4l (descending); find the bin where
+            // the count from the top first reaches `need`
+            const int need = s_need;
+            int h[4], own = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                h[q] = s_hist[255 - 4 * tid - q];
+                own += h[q];
             }
-            s_need = need;
-            s_prefix = prefix | ((unsigned long long)d << shift);
+            int incl = own;                                   // inclusive scan over lanes
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const int y = __shfl_up(incl, off, 64);
+                if (tid >= off) incl += y;
+            }
+            const int above = incl - own;                     // count in higher bins
+            if (above < need && incl >= need) {               // exactly one lane
+                int rem = need - above, d = 255 - 4 * tid;
+#pragma unroll
+                for (int q = 0; q < 3; ++q) {
+                    if (h[q] >= rem) break;
+                    rem -= h[q];
+                    --d;
+                }
+                s_need = rem;
+                s_prefix = prefix | ((unsigned long long)d << shift);
+            }
         }
         mask |= 0xFFull << shift;
         __syncthreads();
@@ -208,7 +247,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
         int e = eq_before;
         for (int j = j0; j < j1; ++j) {
             const unsigned long long key = s_key[j];
-            if (key > thr || (key == thr && e++ < need_ties)) ++n_sel;
+            if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) ++n_sel;
         }
     }
     int sel_before = block_excl_scan_1024(n_sel, s_tmp, &total);
@@ -217,7 +256,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
         int e = eq_before, o = sel_before;
         for (int j = j0; j < j1; ++j) {
             const unsigned long long key = s_key[j];
-            if (key > thr || (key == thr && e++ < need_ties)) {
+            if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) {
                 sel[o++] = j;
                 const uint32_t c = colmax[j];
                 am = c > am ? c : am;
@@ -230,61 +269,62 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     if (tid == 0) {
         uint32_t m = 0;
         for (int i = 0; i < 16; ++i) m = s_amax[i] > m ? s_amax[i] : m;
-        r_ts[0] = tensor_scale_from_amax(__uint_as_float(m));
+        s_rts = tensor_scale_from_amax(__uint_as_float(m));
+        r_ts[0] = s_rts;
     }
+    __syncthreads();
+    build_threshold_table(s_rts, reinterpret_cast<uint32_t(*)[8]>(r_table), false);
 }
 
 // ----------------------------------------------------------------- pass 2 --
-// One thread per (row, 16-block of the compacted index).
+// One thread per residual element (row, i); the 16 lanes of a block reduce
+// its maximum with shuffles, neighbouring lanes pair their nibbles.
 __global__ __launch_bounds__(256) void k_rac_pass2(
     const uint16_t* __restrict__ x, int64_t M, int K, const int32_t* __restrict__ sel, int k,
     const uint8_t* __restrict__ nib, const uint8_t* __restrict__ scale,
-    const float* __restrict__ ts, const float* __restrict__ r_ts, uint8_t* __restrict__ r_nib,
+    const float* __restrict__ ts, const float* __restrict__ r_ts,
+    const uint32_t* __restrict__ r_table, uint8_t* __restrict__ r_nib,
     uint8_t* __restrict__ r_scale) {
-    __shared__ uint32_t s_thr[kE4m3MaxCode + 1][8];
-    __shared__ int s_sel[kRacMaxK];
+    __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
+    for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x)
+        s_tab[i] = reinterpret_cast<const uint4*>(r_table)[i];
     const float s_t = ts[0];
     const float s_tr = r_ts[0];
-    build_threshold_table(s_tr, s_thr);
-    for (int i = threadIdx.x; i < k; i += blockDim.x) s_sel[i] = sel[i];
-    __syncthreads();
-    const int kb = k / kBlock;
-    const int64_t nblk = M * kb;
     const double six_str = 6.0 * (double)s_tr;
-    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < nblk;
-         t += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t row = t / kb;
-        const int bi = (int)(t - row * kb);
-        const uint16_t* xr = x + row * K;
-        const uint8_t* nr = nib + row * (K / 2);
-        const uint8_t* sr = scale + row * (K / kBlock);
-        float r[16];
-        uint32_t am = 0;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const int j = s_sel[bi * kBlock + e];
-            const uint32_t h = xr[j];
-            const uint32_t code = (nr[j >> 1] >> (4 * (j & 1))) & 0xFu;
-            float sv = e2m1_value(code & 7u) * e4m3_value(sr[j >> 4]);
+    __syncthreads();
+    const int64_t n = M * k;                       // k % 16 == 0: blocks never straddle
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n;
+         base += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = base + threadIdx.x;
+        const bool live = t < n;                       // uniform over each 16-lane block
+        float r = 0.0f;
+        if (live) {
+            const int64_t row = t / k;
+            const int i = (int)(t - row * k);
+            const int j = sel[i];
+            const uint32_t h = x[row * K + j];
+            const uint32_t code = (nib[row * (K / 2) + (j >> 1)] >> (4 * (j & 1))) & 0xFu;
+            float sv = e2m1_value(code & 7u) * e4m3_value(scale[row * (K / kBlock) + (j >> 4)]);
             if (code & 8u) sv = -sv;
-            r[e] = fmaf(-sv, s_t, bf16_to_f32(h));
-            const uint32_t ab = __float_as_uint(r[e]) & 0x7FFFFFFFu;
-            am = ab > am ? ab : am;
+            r = fmaf(-sv, s_t, bf16_to_f32(h));
+        }
+        const uint32_t rb = __float_as_uint(r);
+        uint32_t am = rb & 0x7FFFFFFFu;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            const uint32_t o = __shfl_xor(am, off, 16);
+            am = o > am ? o : am;
         }
         const uint32_t sb =
             s_tr > 0.0f ? e4m3_rne_code((double)__uint_as_float(am) / six_str) : 0u;
-        uint32_t thr[7];
-#pragma unroll
-        for (int i = 0; i < 7; ++i) thr[i] = s_thr[sb][i];
-        uint32_t packed[2] = {0u, 0u};
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-            const uint32_t rb = __float_as_uint(r[e]);
-            const uint32_t code = e2m1_mag_code(rb & 0x7FFFFFFFu, thr) | ((rb >> 28) & 8u);
-            packed[e >> 3] |= code << (4 * (e & 7));
+        const uint4 t0 = s_tab[2 * sb], t1 = s_tab[2 * sb + 1];
+        const uint32_t thr[7] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z};
+        const uint32_t c = e2m1_mag_code(rb & 0x7FFFFFFFu, thr) | ((rb >> 28) & 8u);
+        const uint32_t other = __shfl_xor(c, 1, 16);
+        if (live) {
+            if ((t & 1) == 0) r_nib[t >> 1] = (uint8_t)(c | (other << 4));
+            if ((t & 15) == 0) r_scale[t >> 4] = (uint8_t)sb;
         }
-        *reinterpret_cast<uint2*>(r_nib + t * 8) = make_uint2(packed[0], packed[1]);
-        r_scale[t] = (uint8_t)sb;
     }
 }
 
@@ -299,6 +339,8 @@ __global__ void k_fill_f64(double* p, int n, double v) {
 
 struct RacWs {
     uint32_t* partial;
+    uint32_t* table;       // code table of x
+    uint32_t* r_table;     // code table of the gathered residual
     double* pa;
     uint32_t* ca;
     double* pb;
@@ -312,6 +354,8 @@ RacWs rac_ws_layout(char* base, int64_t M, int64_t K) {
     RacWs w;
     size_t off = 0;
     w.partial = (uint32_t*)(base + off); off += align_up(kAmaxGroups * 4, 256);
+    w.table = (uint32_t*)(base + off); off += 1024 * 4;
+    w.r_table = (uint32_t*)(base + off); off += 1024 * 4;
     w.pa = (double*)(base + off); off += align_up((size_t)(c0 > 1 ? c0 : 1) * K * 8, 256);
     w.ca = (uint32_t*)(base + off); off += align_up((size_t)(c0 > 1 ? c0 : 1) * K * 4, 256);
     w.pb = (double*)(base + off); off += align_up((size_t)c1 * K * 8, 256);
@@ -356,10 +400,14 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
     const int groups = amax_groups(M * K);
     launch_amax_partial(x, M * K, 1, w.partial, groups, s);
     QUADS_CHECK_LAUNCH();
+    launch_scale_finalize(w.partial, groups, nullptr, 1, ts, w.table, s);
+    QUADS_CHECK_LAUNCH();
     const int64_t c0 = (M + kTileRows - 1) / kTileRows;
-    hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)c0, (unsigned)((K + kTileCols - 1) / kTileCols)),
-                       dim3(256), 0, s, x, M, (int)K, w.partial, groups, nib, scale, ts, w.pa,
-                       w.ca);
+    const int64_t ctiles = (K + kP1Cols - 1) / kP1Cols;
+    int64_t gx = 2048 / ctiles;
+    gx = gx < 1 ? 1 : (gx > c0 ? c0 : gx);
+    hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)gx, (unsigned)ctiles), dim3(256), 0, s, x, M,
+                       (int)K, ts, w.table, nib, scale, w.pa, w.ca);
     QUADS_CHECK_LAUNCH();
     // fixed-order tree over the level-0 partials
     double* pin = w.pa; uint32_t* cin = w.ca;
@@ -380,14 +428,14 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
         return QUADS_OK;
     }
     hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)K, (int)k, sel,
-                       r_ts, score_out);
+                       r_ts, score_out, w.r_table);
     QUADS_CHECK_LAUNCH();
     if (k > 0) {
-        const int64_t nblk = M * (k / kBlock);
-        int64_t grid = (nblk + 255) / 256;
-        if (grid > 4096) grid = 4096;
+        const int64_t nel = M * (int64_t)k;
+        int64_t grid = (nel + 255) / 256;
+        if (grid > 2048) grid = 2048;
         hipLaunchKernelGGL(k_rac_pass2, dim3((unsigned)grid), dim3(256), 0, s, x, M, (int)K, sel,
-                           (int)k, nib, scale, ts, r_ts, r_nib, r_scale);
+                           (int)k, nib, scale, ts, r_ts, w.r_table, r_nib, r_scale);
         QUADS_CHECK_LAUNCH();
     } else {
         launch_fill_f32(r_ts, 1, 0.0f, s);
