@@ -43,7 +43,7 @@ def _parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=256)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this size (for counter calibration)")
     return ap.parse_args()
