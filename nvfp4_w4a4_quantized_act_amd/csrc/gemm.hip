@@ -390,37 +390,104 @@ __device__ __forceinline__ int frag_off(int lane, int kk) {
     return r * BK + 8 * ((2 * kk + (lane >> 5)) ^ ((r >> 1) & 7));
 }
 
-// MFMAs of one 16-deep sub-step of a stage (foff = frag_off(lane, kk)).
-__device__ __forceinline__ void mma_kk(const _Float16* st, int foff, int wm, int wn, int mact,
-                                       f32x16 acc[4][2]) {
-    const _Float16* sa = st + wm * 128 * BK + foff;
-    const _Float16* sb = st + BM * BK + wn * 64 * BK + foff;
+// MFMAs of one 16-deep sub-step of a stage (foff = frag_off(lane, kk)) for
+// the wave's first MACT 32-row blocks.  MACT is a template argument so that
+// the loop bodies have no branches around the MFMAs, which lets the compiler
+// interleave them with the loads, conversions and LDS stores of the stage.
+template <int MACT>
+__device__ __forceinline__ void mma_kk(const _Float16* sa_base, const _Float16* sb_base, int foff,
+                                       int wm, int wn, f32x16 acc[4][2]) {
+    if (MACT == 0) return;
+    const _Float16* sa = sa_base + wm * 128 * BK + foff;
+    const _Float16* sb = sb_base + wn * 64 * BK + foff;
     f16x8 a[4], b[2];
 #pragma unroll
     for (int nj = 0; nj < 2; ++nj) b[nj] = *reinterpret_cast<const f16x8*>(sb + nj * 32 * BK);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(sa + mi * 32 * BK);
+    for (int mi = 0; mi < MACT; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(sa + mi * 32 * BK);
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        if (mi < mact) {
+    for (int mi = 0; mi < MACT; ++mi)
 #pragma unroll
-            for (int nj = 0; nj < 2; ++nj)
-                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+        for (int nj = 0; nj < 2; ++nj)
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+}
+
+// Copies the weight columns of the selected channels that fall in this
+// stage (k0 .. k0 + 63) from the stage's W tile into ws_s (column = index
+// into sel): thread rows crow, channels of parity cpar.  Lane i of every wave
+// holds my_sel = sel[i] (kc <= 64 channels), so the stage's channels are one
+// ballot and their indices come from readlane: no memory loads.
+__device__ __forceinline__ void capture(const _Float16* cur_w, _Float16* ws_s, int my_sel,
+                                        int k0, int crow, int cpar) {
+    unsigned long long m = __ballot(my_sel >= k0 && my_sel < k0 + BK);
+    while (m) {
+        const int ic = __ffsll(m) - 1;
+        m &= m - 1;
+        if ((ic & 1) == cpar) {
+            const int c = __builtin_amdgcn_readlane(my_sel, ic) - k0;
+            ws_s[swz(crow, ic >> 3) + (ic & 7)] = cur_w[swz(crow, c >> 3) + (c & 7)];
         }
     }
 }
 
 // One stage: MFMAs on `cur` with the dequantization of (ra, rb) into `nxt`
 // spread between the sub-steps.
-__device__ __forceinline__ void stage(const _Float16* cur, _Float16* nxt, bool store,
-                                      const Raw& ra, const Raw& rb, int lr, int lh, int wm, int wn,
-                                      int mact, const int fo[4], f32x16 acc[4][2]) {
-    mma_kk(cur, fo[0], wm, wn, mact, acc);
-    mma_kk(cur, fo[1], wm, wn, mact, acc);
-    if (store) store_slice(ra, nxt, lr, lh);
-    mma_kk(cur, fo[2], wm, wn, mact, acc);
-    if (store) store_slice(rb, nxt + BM * BK, lr, lh);
-    mma_kk(cur, fo[3], wm, wn, mact, acc);
+template <int MACT>
+__device__ __forceinline__ void stage(const _Float16* cur, _Float16* nxt, const Raw& ra,
+                                      const Raw& rb, int lr, int lh, int wm, int wn,
+                                      const int fo[4], f32x16 acc[4][2]) {
+    mma_kk<MACT>(cur, cur + BM * BK, fo[0], wm, wn, acc);
+    mma_kk<MACT>(cur, cur + BM * BK, fo[1], wm, wn, acc);
+    store_slice(ra, nxt, lr, lh);
+    mma_kk<MACT>(cur, cur + BM * BK, fo[2], wm, wn, acc);
+    store_slice(rb, nxt + BM * BK, lr, lh);
+    mma_kk<MACT>(cur, cur + BM * BK, fo[3], wm, wn, acc);
+}
+
+// find_tile_bm computed by each wave on its own (no LDS, no barrier): lane l
+// counts the tiles of experts l*per .. l*per + per - 1, a wave scan gives the
+// first tile of each lane's range, and the owning lane broadcasts the result.
+__device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int bm,
+                               int* e_out, int* m0_out, int* mend_out) {
+    if (offsets == nullptr) {
+        const int64_t m0 = (int64_t)tile * bm;
+        *e_out = 0;
+        *m0_out = (int)m0;
+        *mend_out = (int)rows;
+        return m0 < rows;
+    }
+    const int lane = threadIdx.x & 63;
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    const int e1 = e0 + per < E ? e0 + per : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    int run = x - local, fe = -1, fm0 = 0, fme = 0;
+    if (tile >= run && tile < x) {
+        for (int e = e0; e < e1; ++e) {
+            const int t = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+            if (tile < run + t) {
+                fe = e;
+                fm0 = offsets[e] + (tile - run) * bm;
+                fme = offsets[e + 1];
+                break;
+            }
+            run += t;
+        }
+    }
+    const unsigned long long owners = __ballot(fe >= 0);
+    if (owners == 0ull) return false;
+    const int src = __ffsll(owners) - 1;
+    *e_out = __shfl(fe, src, 64);
+    *m0_out = __shfl(fm0, src, 64);
+    *mend_out = __shfl(fme, src, 64);
+    return true;
 }
 
 // Weight row of B-tile row r.  Plain: f0 + r.  SwiGLU: the tile holds 128
@@ -437,19 +504,112 @@ __device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool*
     return ((r >> 5) & 1) * (N / 2) + feat;
 }
 
+// Compensation stages with gathered weight columns (first, before the main
+// stages), then acc *= s_tR / s_tA.  Used when the captured order below
+// cannot be taken (k > 64, or s_tR < 2^-80 s_tA).
+template <int MACT>
+__device__ __forceinline__ void comp_first(const GemmArgs& g, _Float16* smem, int64_t src,
+                                           bool a_valid, bool b_valid, const uint8_t* w_nib_row,
+                                           const uint8_t* w_sc_row, int lr, int lh, int wm,
+                                           int wn, const int fo[4], f32x16 acc[4][2]) {
+    const uint8_t* r_nib_row = g.r_nib + src * (g.k / 2);
+    const uint8_t* r_sc_row = g.r_scale + src * (g.k / kBlock);
+    for (int i0 = 0; i0 < g.k; i0 += BK) {
+        const Raw ra = load_raw(r_nib_row, r_sc_row, i0 + 32 * lh, a_valid);
+        store_slice(ra, smem, lr, lh);
+        gather_store(w_nib_row, w_sc_row, g.sel, i0, g.K, b_valid, smem + BM * BK, lr, lh);
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) mma_kk<MACT>(smem, smem + BM * BK, fo[kk], wm, wn, acc);
+        __syncthreads();
+    }
+    const float rho = g.r_ts[0] / g.a_ts[0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * rho;
+}
+
+// Main stages through two LDS buffers, the loads of stage s + 1 in flight
+// during stage s.  Stage offsets past the end are clamped to the last stage
+// (a redundant, in-bounds load whose data goes to the idle buffer and is
+// never read), so the loop body has no conditional loads or stores; rows
+// past the tile's end load a valid row and their results are never written.
+//
+// With kc = 64 the weight columns of the selected channels are captured from
+// the staged W tiles into ws_s on the way, and one compensation stage follows:
+// acc *= up (= s_tA / s_tR <= 2^80, so |acc| stays below 2^120), then acc +=
+// R x W[:, S]; the epilogue scale is then s_tR s_tW.
+template <int MACT>
+__device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _Float16* ws_s,
+                                            int kc, float up, int64_t src, bool a_valid,
+                                            const uint8_t* a_nib_row, const uint8_t* a_sc_row,
+                                            const uint8_t* w_nib_row, const uint8_t* w_sc_row,
+                                            int lr, int lh, int wm, int wn, const int fo[4],
+                                            f32x16 acc[4][2]) {
+    const int crow = threadIdx.x & 255, cpar = threadIdx.x >> 8;
+    const int lane = threadIdx.x & 63;
+    const int my_sel = lane < kc ? g.sel[lane] : -1;
+    const int nk = g.K / BK;
+    const int klast = g.K - BK;
+    // With kc > 0, the load that would fetch the (clamped) stage past the end
+    // fetches this row's R codes instead; the last stage stores them into the
+    // idle buffer's A slice for the compensation stage.  Rows past the tile's
+    // end read R row 0 (src = 0); their results are never written.
+    const uint8_t* r_nib_row = kc > 0 ? g.r_nib + src * (g.k / 2) : a_nib_row;
+    const uint8_t* r_sc_row = kc > 0 ? g.r_scale + src * (g.k / kBlock) : a_sc_row;
+    {
+        const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, true);
+        const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, true);
+        store_slice(ra, smem, lr, lh);
+        store_slice(rb, smem + BM * BK, lr, lh);
+    }
+    Raw a0, b0;
+    if (nk > 1) {
+        a0 = load_raw(a_nib_row, a_sc_row, BK + 32 * lh, true);
+    } else {
+        a0 = load_raw(r_nib_row, r_sc_row, 32 * lh, true);
+    }
+    b0 = load_raw(w_nib_row, w_sc_row, min(BK, klast) + 32 * lh, true);
+    __syncthreads();
+    for (int it = 0; it < nk; ++it) {
+        _Float16* cur = smem + (it & 1) * kStage;
+        _Float16* nxt = smem + ((it & 1) ^ 1) * kStage;
+        stage<MACT>(cur, nxt, a0, b0, lr, lh, wm, wn, fo, acc);
+        const bool past = it + 2 >= nk;
+        const uint8_t* an = past ? r_nib_row : a_nib_row + (it + 2) * (BK / 2);
+        const uint8_t* as = past ? r_sc_row : a_sc_row + (it + 2) * (BK / kBlock);
+        a0 = load_raw(an, as, 32 * lh, true);
+        b0 = load_raw(w_nib_row, w_sc_row, min((it + 2) * BK, klast) + 32 * lh, true);
+        if (kc > 0) capture(cur + BM * BK, ws_s, my_sel, it * BK, crow, cpar);
+        __syncthreads();
+    }
+    if (kc == 0) return;
+    // compensation stage: A = R in the buffer the last stage stored into, B = ws_s
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * up;
+    const _Float16* rbuf = smem + (nk & 1) * kStage;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) mma_kk<MACT>(rbuf, ws_s, fo[kk], wm, wn, acc);
+}
+
 template <int kEpi>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n, int grp) {
     __shared__ _Float16 smem[2 * kStage];
-    __shared__ int s_scan[16];
-    __shared__ int s_res[4];
+    __shared__ _Float16 ws_s[BN * BK];           // captured weight columns W[:, S]
     // XCD-aware numbering: hardware id h runs on XCD h % 8
     const int h = blockIdx.x;
     const int slot = h / kXcds;
     const int tile = (slot / grp) * (kXcds * grp) + (h % kXcds) * grp + slot % grp;
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
-    if (!find_tile_bm(g.offsets, g.E, g.rows, tile_m, BM, s_scan, s_res, &e, &m0, &mend))
-        return;
+    if (!find_tile_wave(g.offsets, g.E, g.rows, tile_m, BM, &e, &m0, &mend)) return;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -479,62 +639,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
-
-    // compensation stages
-    if (g.k > 0) {
-        const uint8_t* r_nib_row = g.r_nib + src * (g.k / 2);
-        const uint8_t* r_sc_row = g.r_scale + src * (g.k / kBlock);
-        for (int i0 = 0; i0 < g.k; i0 += BK) {
-            const Raw ra = load_raw(r_nib_row, r_sc_row, i0 + 32 * lh, a_valid);
-            store_slice(ra, smem, lr, lh);
-            gather_store(w_nib_row, w_sc_row, g.sel, i0, g.K, b_valid, smem + BM * BK, lr, lh);
-            __syncthreads();
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) mma_kk(smem, fo[kk], wm, wn, mact, acc);
-            __syncthreads();
-        }
-        const float s_ta = g.a_ts[0];
-        const float rho = s_ta > 0.0f ? g.r_ts[0] / s_ta : 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * rho;
+    // Compensation order.  With kc = 64 selected channels (one stage) and
+    // s_tR >= 2^-80 s_tA, the weight columns are captured during the main
+    // stages and the compensation runs last, after acc *= s_tA / s_tR
+    // (<= 2^80, so |acc| stays below 2^120).  Otherwise it runs first with
+    // gathered weight columns and acc *= s_tR / s_tA.  s_tR = 0 means every
+    // residual code is 0 and the compensation is skipped.
+    const float s_ta = g.a_ts[0];
+    const float s_tr = g.k > 0 ? g.r_ts[0] : 0.0f;
+    const bool comp = g.k > 0 && s_tr > 0.0f;
+    const bool capture_path = !comp || (g.k == BK && s_tr >= s_ta * 0x1p-80f);
+    const float cscale = comp && capture_path ? s_tr : s_ta;
+    const int kc = comp && capture_path ? g.k : 0;
+    const float up = kc > 0 ? s_ta / s_tr : 1.0f;
+    if (kc > 0) {                                       // no stale values in unused columns
+        for (int i = tid; i < BN * BK / 8; i += kThreads)
+            reinterpret_cast<f16x8*>(ws_s)[i] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
-
-    // main stages: LDS double buffer, loads two stages ahead
-    const int nk = g.K / BK;
-    {
-        const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, a_valid);
-        const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, b_valid);
-        store_slice(ra, smem, lr, lh);
-        store_slice(rb, smem + BM * BK, lr, lh);
-    }
-    Raw a0 = load_raw(a_nib_row, a_sc_row, (nk > 1 ? BK : 0) + 32 * lh, a_valid && nk > 1);
-    Raw b0 = load_raw(w_nib_row, w_sc_row, (nk > 1 ? BK : 0) + 32 * lh, b_valid && nk > 1);
-    Raw a1, b1;
-    __syncthreads();
-    for (int it = 0; it < nk; it += 2) {
-        // even stage `it`: LDS buffer 0; (a0, b0) hold stage it+1
-        if (it + 2 < nk) {
-            a1 = load_raw(a_nib_row, a_sc_row, (it + 2) * BK + 32 * lh, a_valid);
-            b1 = load_raw(w_nib_row, w_sc_row, (it + 2) * BK + 32 * lh, b_valid);
-        }
-        stage(smem, smem + kStage, it + 1 < nk, a0, b0, lr, lh, wm, wn, mact, fo, acc);
-        __syncthreads();
-        if (it + 1 >= nk) break;
-        // odd stage `it+1`: LDS buffer 1; (a1, b1) hold stage it+2
-        if (it + 3 < nk) {
-            a0 = load_raw(a_nib_row, a_sc_row, (it + 3) * BK + 32 * lh, a_valid);
-            b0 = load_raw(w_nib_row, w_sc_row, (it + 3) * BK + 32 * lh, b_valid);
-        }
-        stage(smem + kStage, smem, it + 2 < nk, a1, b1, lr, lh, wm, wn, mact, fo, acc);
-        __syncthreads();
+    switch (mact) {
+#define QUADS_TILE(M)                                                                          \
+    case M:                                                                                    \
+        if (comp && !capture_path)                                                             \
+            comp_first<M>(g, smem, src, a_valid, b_valid, w_nib_row, w_sc_row, lr, lh, wm, wn, \
+                          fo, acc);                                                            \
+        main_stages<M>(g, smem, ws_s, kc, up, src, a_valid, a_nib_row, a_sc_row, w_nib_row,    \
+                       w_sc_row, lr, lh, wm, wn, fo, acc);                                     \
+        break;
+        QUADS_TILE(4) QUADS_TILE(3) QUADS_TILE(2) QUADS_TILE(1)
+        default: QUADS_TILE(0)
+#undef QUADS_TILE
     }
 
     // epilogue
-    const float ca = g.a_ts[0] * g.w_ts[e];
+    const float ca = cscale * g.w_ts[e];
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         if (mi >= mact) continue;

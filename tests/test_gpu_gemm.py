@@ -232,15 +232,17 @@ def test_dense_config2_sampled(Q):
     print("max relative error", rel)
 
 
-def test_tiny_residual_scale_fallback(Q):
-    """s_tR / s_tA below 2^-60: the compensation runs before the main loop (the
-    in-loop rescaling could overflow); results must still match."""
+@pytest.mark.parametrize("p2,lo,hi", [(50, -80, -60), (62, -200, -80)])
+def test_tiny_residual_scale(Q, p2, lo, hi):
+    """s_tR / s_tA far below 1.  Between 2^-80 and 2^-60 the main accumulator
+    is scaled up by s_tA / s_tR before the compensation stage; below 2^-80 the
+    compensation runs first with gathered weight columns.  Both must match."""
     rng = np.random.default_rng(41)
     x = (rng.standard_normal((80, 256)) * 2.0 ** -10).astype(np.float32)
     x[:, :16] = 0.0
-    x[0, 0] = 2688.0 * 2.0 ** 50        # s_t = 2^50 exactly, so this element has r = 0
+    x[0, 0] = 2688.0 * 2.0 ** p2        # s_t = 2^p2 exactly, so this element has r = 0
     out, wq = _operands(synth.f32_to_bf16_bits(x), synth.weights(rng, 1, 64, 256), 64)
-    assert out["r_ts"] / out["ts"] < 2.0 ** -60
+    assert 2.0 ** lo < out["r_ts"] / out["ts"] < 2.0 ** hi
     y = _gpu_gemm(Q, out, wq, 64, 64).cpu().numpy()
     exp, bound = _oracle(out, wq, 64, [0, 80])
     _assert_close(y, exp, bound)
