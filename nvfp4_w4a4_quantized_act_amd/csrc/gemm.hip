@@ -432,16 +432,31 @@ __device__ __forceinline__ void capture(const _Float16* cur_w, _Float16* ws_s, i
 
 // One stage: MFMAs on `cur` with the dequantization of (ra, rb) into `nxt`
 // spread between the sub-steps.
-template <int MACT>
+// ALIVE: this wave's A slice (tile rows 32 wave .. 32 wave + 31) holds rows
+// of the tile; otherwise the wave neither loads nor stores A (those LDS rows
+// feed only MFMA blocks that are skipped).  LATE: the two waves that share a
+// SIMD (waves w and w + 4) run the stage in opposite phase -- one starts with
+// MFMAs, the other with its conversions and LDS stores -- so that one wave's
+// vector work overlaps the other's MFMAs.
+template <int MACT, bool ALIVE, bool LATE>
 __device__ __forceinline__ void stage(const _Float16* cur, _Float16* nxt, const Raw& ra,
                                       const Raw& rb, int lr, int lh, int wm, int wn,
                                       const int fo[4], f32x16 acc[4][2]) {
-    mma_kk<MACT>(cur, cur + BM * BK, fo[0], wm, wn, acc);
-    mma_kk<MACT>(cur, cur + BM * BK, fo[1], wm, wn, acc);
-    store_slice(ra, nxt, lr, lh);
-    mma_kk<MACT>(cur, cur + BM * BK, fo[2], wm, wn, acc);
-    store_slice(rb, nxt + BM * BK, lr, lh);
-    mma_kk<MACT>(cur, cur + BM * BK, fo[3], wm, wn, acc);
+    if (LATE) {
+        if (ALIVE) store_slice(ra, nxt, lr, lh);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[0], wm, wn, acc);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[1], wm, wn, acc);
+        store_slice(rb, nxt + BM * BK, lr, lh);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[2], wm, wn, acc);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[3], wm, wn, acc);
+    } else {
+        mma_kk<MACT>(cur, cur + BM * BK, fo[0], wm, wn, acc);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[1], wm, wn, acc);
+        if (ALIVE) store_slice(ra, nxt, lr, lh);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[2], wm, wn, acc);
+        mma_kk<MACT>(cur, cur + BM * BK, fo[3], wm, wn, acc);
+        store_slice(rb, nxt + BM * BK, lr, lh);
+    }
 }
 
 // find_tile_bm computed by each wave on its own (no LDS, no barrier): lane l
@@ -471,11 +486,16 @@ __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int 
     int run = x - local, fe = -1, fm0 = 0, fme = 0;
     if (tile >= run && tile < x) {
         for (int e = e0; e < e1; ++e) {
-            const int t = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+            const int n = offsets[e + 1] - offsets[e];
+            const int t = (n + bm - 1) / bm;
             if (tile < run + t) {
+                // the expert's rows split evenly over its t tiles, in 32-row
+                // multiples: a 280-row expert gets 160 + 120 rows rather than
+                // 256 + 24, so neither tile is a near-empty one
+                const int per_tile = ((n + t - 1) / t + 31) / 32 * 32;
                 fe = e;
-                fm0 = offsets[e] + (tile - run) * bm;
-                fme = offsets[e + 1];
+                fm0 = offsets[e] + (tile - run) * per_tile;
+                fme = fm0 + per_tile < offsets[e + 1] ? fm0 + per_tile : offsets[e + 1];
                 break;
             }
             run += t;
@@ -542,7 +562,7 @@ __device__ __forceinline__ void comp_first(const GemmArgs& g, _Float16* smem, in
 // the staged W tiles into ws_s on the way, and one compensation stage follows:
 // acc *= up (= s_tA / s_tR <= 2^80, so |acc| stays below 2^120), then acc +=
 // R x W[:, S]; the epilogue scale is then s_tR s_tW.
-template <int MACT>
+template <int MACT, bool ALIVE, bool LATE>
 __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _Float16* ws_s,
                                             int kc, float up, int64_t src, bool a_valid,
                                             const uint8_t* a_nib_row, const uint8_t* a_sc_row,
@@ -561,13 +581,18 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
     const uint8_t* r_nib_row = kc > 0 ? g.r_nib + src * (g.k / 2) : a_nib_row;
     const uint8_t* r_sc_row = kc > 0 ? g.r_scale + src * (g.k / kBlock) : a_sc_row;
     {
-        const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, true);
         const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, true);
-        store_slice(ra, smem, lr, lh);
         store_slice(rb, smem + BM * BK, lr, lh);
+        if (ALIVE) {
+            const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, true);
+            store_slice(ra, smem, lr, lh);
+        }
     }
     Raw a0, b0;
-    if (nk > 1) {
+    if (!ALIVE) {
+        a0.n = make_uint4(0, 0, 0, 0);
+        a0.sc = 0;
+    } else if (nk > 1) {
         a0 = load_raw(a_nib_row, a_sc_row, BK + 32 * lh, true);
     } else {
         a0 = load_raw(r_nib_row, r_sc_row, 32 * lh, true);
@@ -577,11 +602,13 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
     for (int it = 0; it < nk; ++it) {
         _Float16* cur = smem + (it & 1) * kStage;
         _Float16* nxt = smem + ((it & 1) ^ 1) * kStage;
-        stage<MACT>(cur, nxt, a0, b0, lr, lh, wm, wn, fo, acc);
-        const bool past = it + 2 >= nk;
-        const uint8_t* an = past ? r_nib_row : a_nib_row + (it + 2) * (BK / 2);
-        const uint8_t* as = past ? r_sc_row : a_sc_row + (it + 2) * (BK / kBlock);
-        a0 = load_raw(an, as, 32 * lh, true);
+        stage<MACT, ALIVE, LATE>(cur, nxt, a0, b0, lr, lh, wm, wn, fo, acc);
+        if (ALIVE) {
+            const bool past = it + 2 >= nk;
+            const uint8_t* an = past ? r_nib_row : a_nib_row + (it + 2) * (BK / 2);
+            const uint8_t* as = past ? r_sc_row : a_sc_row + (it + 2) * (BK / kBlock);
+            a0 = load_raw(an, as, 32 * lh, true);
+        }
         b0 = load_raw(w_nib_row, w_sc_row, min((it + 2) * BK, klast) + 32 * lh, true);
         if (kc > 0) capture(cur + BM * BK, ws_s, my_sel, it * BK, crow, cpar);
         __syncthreads();
@@ -656,17 +683,25 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
         for (int i = tid; i < BN * BK / 8; i += kThreads)
             reinterpret_cast<f16x8*>(ws_s)[i] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
     }
-    switch (mact) {
-#define QUADS_TILE(M)                                                                          \
-    case M:                                                                                    \
+    // wave-uniform: does this wave's A slice (tile rows 32 wave ..) hold rows?
+    const bool alive = m0 + 32 * wave < mend;
+    switch (__builtin_amdgcn_readfirstlane(mact + (alive ? 8 : 0))) {
+#define QUADS_TILE(M, L)                                                                       \
+    case M + (L ? 8 : 0):                                                                      \
         if (comp && !capture_path)                                                             \
             comp_first<M>(g, smem, src, a_valid, b_valid, w_nib_row, w_sc_row, lr, lh, wm, wn, \
                           fo, acc);                                                            \
-        main_stages<M>(g, smem, ws_s, kc, up, src, a_valid, a_nib_row, a_sc_row, w_nib_row,    \
-                       w_sc_row, lr, lh, wm, wn, fo, acc);                                     \
+        if (wm)                                                                                \
+            main_stages<M, L, true>(g, smem, ws_s, kc, up, src, a_valid, a_nib_row, a_sc_row,  \
+                                    w_nib_row, w_sc_row, lr, lh, wm, wn, fo, acc);             \
+        else                                                                                   \
+            main_stages<M, L, false>(g, smem, ws_s, kc, up, src, a_valid, a_nib_row, a_sc_row, \
+                                     w_nib_row, w_sc_row, lr, lh, wm, wn, fo, acc);            \
         break;
-        QUADS_TILE(4) QUADS_TILE(3) QUADS_TILE(2) QUADS_TILE(1)
-        default: QUADS_TILE(0)
+        QUADS_TILE(4, true) QUADS_TILE(3, true) QUADS_TILE(2, true) QUADS_TILE(1, true)
+        QUADS_TILE(0, true) QUADS_TILE(4, false) QUADS_TILE(3, false) QUADS_TILE(2, false)
+        QUADS_TILE(1, false)
+        default: QUADS_TILE(0, false)
 #undef QUADS_TILE
     }
 
