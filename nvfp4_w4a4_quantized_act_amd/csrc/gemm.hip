@@ -408,11 +408,14 @@ __device__ __forceinline__ void mma_kk(const _Float16* sa_base, const _Float16* 
     for (int nj = 0; nj < 2; ++nj) b[nj] = *reinterpret_cast<const f16x8*>(sb + nj * 32 * BK);
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi) a[mi] = *reinterpret_cast<const f16x8*>(sa + mi * 32 * BK);
+    // weights as the first operand: acc[mi][nj] holds the transposed 32 x 32
+    // block, lane l owning activation row l % 32 and output features
+    // 8 (v / 4) + 4 (l / 32) + v % 4 of register v (four consecutive ones)
 #pragma unroll
     for (int mi = 0; mi < MACT; ++mi)
 #pragma unroll
         for (int nj = 0; nj < 2; ++nj)
-            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a[mi], b[nj], acc[mi][nj], 0, 0, 0);
+            acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[nj], a[mi], acc[mi][nj], 0, 0, 0);
 }
 
 // Copies the weight columns of the selected channels that fall in this
@@ -710,36 +713,66 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
 
     // epilogue
     const float ca = cscale * g.w_ts[e];
+    const int prow_l = m0 + wm * 128 + (lane & 31);
+    const int nq = 4 * (lane >> 5);
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
         if (mi >= mact) continue;
+        const int prow = prow_l + mi * 32;
+        if (prow >= mend) continue;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int prow = m0 + wm * 128 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            if (prow >= mend) continue;
+        for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
             if (swiglu) {
-                const int feat = f0 + wn * 32 + (lane & 31);
-                if (feat < g.N / 2) {
-                    const float gt = acc[mi][0][v] * ca;
-                    const float up = acc[mi][1][v] * ca;
+                const int feat = f0 + wn * 32 + 8 * q + nq;      // features feat .. feat + 3
+                uint32_t hb[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float gt = acc[mi][0][4 * q + u] * ca;
+                    const float up = acc[mi][1][4 * q + u] * ca;
                     // silu(g) u with the hardware exp2 and reciprocal: relative
                     // error a few 1e-6, far inside half a bf16 ulp (2^-9)
                     const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
-                    const float hval = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
-                    ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] =
-                        (uint16_t)bf16_rne_from_f32(hval);
+                    hb[u] = bf16_rne_from_f32(gt * __builtin_amdgcn_rcpf(1.0f + ex) * up);
+                }
+                const int nh = g.N / 2;
+                uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
+                if (feat + 3 < nh && (nh & 3) == 0) {
+                    *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (feat + u < nh) o[u] = (uint16_t)hb[u];
                 }
             } else {
 #pragma unroll
                 for (int nj = 0; nj < 2; ++nj) {
-                    const int n = f0 + wn * 64 + nj * 32 + (lane & 31);
-                    if (n >= g.N) continue;
-                    const float y = acc[mi][nj][v] * ca;
+                    const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca;
                     const int64_t o = (int64_t)prow * g.N + n;
-                    if (g.out_bf16)
-                        ((uint16_t*)g.out)[o] = (uint16_t)bf16_rne_from_f32(y);
-                    else
-                        ((float*)g.out)[o] = y;
+                    const bool vec = n + 3 < g.N && (g.N & 3) == 0;
+                    if (g.out_bf16) {
+                        uint16_t* ob = (uint16_t*)g.out + o;
+                        if (vec) {
+                            *reinterpret_cast<uint2*>(ob) =
+                                make_uint2(bf16_rne_from_f32(y[0]) | (bf16_rne_from_f32(y[1]) << 16),
+                                           bf16_rne_from_f32(y[2]) | (bf16_rne_from_f32(y[3]) << 16));
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) ob[u] = (uint16_t)bf16_rne_from_f32(y[u]);
+                        }
+                    } else {
+                        float* of = (float*)g.out + o;
+                        if (vec) {
+                            *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) of[u] = y[u];
+                        }
+                    }
                 }
             }
         }
