@@ -21,8 +21,11 @@ the timed region starts.  `value` is the step's algorithmic GEMM work,
 2 * rows * N * (K + k) summed over both GEMMs, divided by the step time.
 `roofline` is for the dominant kernel, the gate/up GEMM: its algorithmic
 flops per launch over its mean launch time (HIP events on the launch stream),
-against the dense fp16 MFMA peak (the GEMM's operands are exact fp16).
-`cpu_baseline` times the NumPy oracle on a bounded sample of the same layer.
+against the dense fp16 MFMA peak (the GEMM's operands are exact fp16);
+`traffic` is its HBM-side bytes per launch from the FETCH_SIZE / WRITE_SIZE
+counter summary under profiles/ (null when that summary was taken on other
+GEMM sources).  `cpu_baseline` times the NumPy oracle on a bounded sample of
+the same layer.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -36,6 +39,12 @@ import time
 PEAK_FP16_TFLOPS = 2500.0        # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_gemm_gate_up_traffic.md")
+GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_quantized_act_amd", "csrc", f)
+                for f in ("gemm.hip", "common.h")]
+GEMM_KERNEL_KEY = "k_gemm_w4a4_v2<1>"     # the gate/up (SwiGLU) GEMM kernel
+
 
 def _parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -43,14 +52,124 @@ def _parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this size (for counter calibration)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
+                         "`bench.py --copy-probe-mib N` into the traffic summary under profiles/")
     return ap.parse_args()
+
+
+def _gemm_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def _counter_per_dispatch(directory, counter):
+    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
+    import csv
+    import glob
+    out = {}
+    for f in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        per = {}
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        for (_, name), v in per.items():
+            out.setdefault(name, []).append(v)
+    return out
+
+
+def traffic_summary(fetch_dir, write_dir, copy_mib):
+    """HBM-side bytes per launch of the gate/up GEMM: FETCH_SIZE and WRITE_SIZE
+    (KiB per dispatch), each scaled by bytes / counter of a plain device copy of
+    copy_mib MiB (which reads and writes copy_mib MiB)."""
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for n, vs in d.items() if key in n for v in vs]
+        if not vals:
+            raise SystemExit(f"no dispatch of a kernel matching {key!r}")
+        return vals
+
+    def copy_val(d):
+        vals = [v for n, vs in d.items() if "copy" in n.lower() for v in vs]
+        if not vals:
+            raise SystemExit("no copy kernel dispatch found (run with --copy-probe-mib)")
+        return max(vals)
+
+    g_f = sum(pick(fetch, GEMM_KERNEL_KEY)) / len(pick(fetch, GEMM_KERNEL_KEY))
+    g_w = sum(pick(write, GEMM_KERNEL_KEY)) / len(pick(write, GEMM_KERNEL_KEY))
+    c_f, c_w = copy_val(fetch), copy_val(write)
+    copy_bytes = copy_mib * (1 << 20)
+    f_scale, w_scale = copy_bytes / c_f, copy_bytes / c_w
+    traffic = g_f * f_scale + g_w * w_scale
+    lines = [
+        "# HBM traffic of the gate/up GEMM: MoE FFN, 128 experts, T=4096, hidden 2048, "
+        "intermediate 768, top-8, RAC k=64",
+        "",
+        "Commands (repository root, one MI355X), then this summary on any host:",
+        "",
+        "```",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE "
+        f"--output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- python -u $REPO/bench.py "
+        f"--steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE "
+        f"--output-format csv -d $REPO/gpurun_out/pmc_write -o w -- python -u $REPO/bench.py "
+        f"--steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"python bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write "
+        f"--copy-probe-mib {copy_mib}",
+        "```",
+        "",
+        "| quantity | value |",
+        "|---|---|",
+        f"| GEMM FETCH_SIZE per dispatch (KiB) | {g_f:.1f} |",
+        f"| GEMM WRITE_SIZE per dispatch (KiB) | {g_w:.1f} |",
+        f"| copy of {copy_mib} MiB: FETCH_SIZE (KiB) | {c_f:.1f} |",
+        f"| copy of {copy_mib} MiB: WRITE_SIZE (KiB) | {c_w:.1f} |",
+        f"| scale, read bytes per FETCH_SIZE unit | {f_scale:.2f} |",
+        f"| scale, written bytes per WRITE_SIZE unit | {w_scale:.2f} |",
+        f"| GEMM read bytes per launch | {g_f * f_scale:.0f} |",
+        f"| GEMM written bytes per launch | {g_w * w_scale:.0f} |",
+        "",
+        f"traffic_bytes_per_launch: {traffic:.0f}",
+        f"gemm_source_sha256: {_gemm_source_hash()}",
+        "",
+    ]
+    with open(TRAFFIC_FILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+def measured_traffic():
+    """Traffic bytes per launch from the committed counter summary, or None when
+    it is missing or was taken on a different GEMM source."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            text = fh.read()
+    except OSError:
+        return None
+    vals = dict(l.split(": ", 1) for l in text.splitlines() if l.startswith(
+        ("traffic_bytes_per_launch: ", "gemm_source_sha256: ")))
+    if vals.get("gemm_source_sha256") != _gemm_source_hash():
+        return None
+    return float(vals["traffic_bytes_per_launch"])
 
 
 def main():
     args = _parse()
+    if args.traffic_from:
+        traffic_summary(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 512)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
                                    "part of it", "n_gpus": args.gpus}))
@@ -191,9 +310,9 @@ def main():
                    "tokens": T, "experts": E, "hidden": H, "intermediate": I, "top_k": TOPK,
                    "rac_k": KR, "packed_rows": rows, "gemm_operands": "nvfp4 -> exact fp16",
                    "accumulate": "fp32", "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": "k_gemm_w4a4<SWIGLU> (gate/up GEMM)",
+        "roofline": {"bound": "mfma", "kernel": "v2::k_gemm_w4a4_v2<1> (gate/up GEMM, SwiGLU epilogue)",
                      "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": None},
+                     "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "ops": ops,
         "weight_qdq_ms": weight_qdq_ms,
