@@ -148,23 +148,32 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 }
 
 // Tensor scale of segment `seg` from its partial maxima (or the caller's fixed
-// scale), computed by the first wave of the work-group into *s_out (LDS).
+// scale), computed by the whole work-group (at most 8 partials per thread,
+// loaded together) into *s_out (LDS; s_red holds one value per wave).
 __device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, int groups,
-                                                      const float* ts_in, int seg, float* s_out) {
-    if (threadIdx.x < 64) {
-        float st;
-        if (ts_in != nullptr) {
-            st = ts_in[0];
-        } else {
-            uint32_t m = 0;
-            for (int i = threadIdx.x; i < groups; i += 64) {
-                uint32_t v = partial[(int64_t)seg * groups + i];
-                m = v > m ? v : m;
-            }
-            m = wave_max_u32(m);
-            st = tensor_scale_from_amax(bf16_to_f32(m));
-        }
-        if (threadIdx.x == 0) *s_out = st;
+                                                      const float* ts_in, int seg, float* s_out,
+                                                      uint32_t* s_red) {
+    const int nw = (blockDim.x + 63) >> 6;
+    if (ts_in != nullptr) {
+        if (threadIdx.x == 0) *s_out = ts_in[0];
+        return;
+    }
+    uint32_t v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = threadIdx.x + q * blockDim.x;
+        v[q] = i < groups ? partial[(int64_t)seg * groups + i] : 0u;
+    }
+    uint32_t m = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) m = v[q] > m ? v[q] : m;
+    m = wave_max_u32(m);
+    if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int i = 0; i < nw; ++i) r = s_red[i] > r ? s_red[i] : r;
+        *s_out = tensor_scale_from_amax(bf16_to_f32(r));
     }
 }
 

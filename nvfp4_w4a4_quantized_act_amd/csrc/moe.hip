@@ -12,8 +12,9 @@
 
 namespace quads {
 
-constexpr int kPackChunk = 1024;       // entries per chunk
+constexpr int kPackChunk = 256;        // entries per chunk
 constexpr int kPackMaxE = 4096;
+constexpr int kPackScanLds = 24576;    // chunk counts the scan keeps in LDS
 
 __global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ ids, int64_t n,
                                                     int E, int32_t* __restrict__ cnt) {
@@ -33,19 +34,69 @@ __global__ __launch_bounds__(256) void k_pack_count(const int32_t* __restrict__ 
 }
 
 // One work-group: offsets[e] = exclusive scan of expert totals; cnt[c][e] is
-// replaced by the first packed row of expert e's entries from chunk c.
+// replaced by the number of expert e's entries in chunks before c (the
+// scatter adds offsets[e]).
 __global__ __launch_bounds__(1024) void k_pack_scan(int32_t* __restrict__ cnt, int nchunks, int E,
                                                     int64_t n, int32_t* __restrict__ offsets) {
     __shared__ int s_tot[kPackMaxE];
     __shared__ int s_wave[16];
-    for (int e = threadIdx.x; e < E; e += 1024) {
-        int run = 0;
-        for (int c = 0; c < nchunks; ++c) {
-            const int v = cnt[(int64_t)c * E + e];
-            cnt[(int64_t)c * E + e] = run;
-            run += v;
+    __shared__ int s_cnt[kPackScanLds];
+    // Per-expert exclusive scans over chunks, kPackScanLds counts at a time
+    // through LDS (coalesced in and out).  Thread groups of P lanes share an
+    // expert: each lane sums a run of chunks, a shuffle scan over the group
+    // gives the lane's base, then the lane writes its run.  s_tot carries the
+    // running total of each expert across LDS tiles.
+    for (int e = threadIdx.x; e < E; e += 1024) s_tot[e] = 0;
+    int P = 1;
+    while (P < 64 && 2 * P * E <= 1024) P *= 2;
+    const int tile = kPackScanLds / E;                    // chunks per LDS tile (>= 6)
+    const int lane = threadIdx.x & 63;
+    for (int c0 = 0; c0 < nchunks; c0 += tile) {
+        const int nc = nchunks - c0 < tile ? nchunks - c0 : tile;
+        const int64_t g0 = (int64_t)c0 * E;
+        __syncthreads();
+        for (int b = 0; b < nc * E; b += 8 * 1024) {       // 8 loads in flight per thread
+            int v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = b + u * 1024 + (int)threadIdx.x;
+                v[u] = i < nc * E ? cnt[g0 + i] : 0;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = b + u * 1024 + (int)threadIdx.x;
+                if (i < nc * E) s_cnt[i] = v[u];
+            }
         }
-        s_tot[e] = run;
+        __syncthreads();
+        const int L = (nc + P - 1) / P;
+        for (int t = threadIdx.x; t < ((E * P + 63) / 64) * 64; t += 1024) {
+            const int e = t / P, part = t % P;              // groups never straddle a wave
+            const bool act = e < E;
+            const int ca = part * L, cb = ca + L < nc ? ca + L : nc;
+            int local = 0;
+            if (act)
+                for (int c = ca; c < cb; ++c) local += s_cnt[c * E + e];
+            int incl = local;
+            for (int off = 1; off < P; off <<= 1) {
+                const int y = __shfl_up(incl, off, P);
+                if ((lane % P) >= off) incl += y;
+            }
+            const int total = __shfl(incl, P - 1, P);
+            if (act) {
+                int run = s_tot[e] + incl - local;
+                for (int c = ca; c < cb; ++c) {
+                    const int v = s_cnt[c * E + e];
+                    s_cnt[c * E + e] = run;
+                    run += v;
+                }
+            }
+            // every lane of the group has read s_tot[e] before part 0 updates it
+            __builtin_amdgcn_wave_barrier();
+            if (act && part == 0) s_tot[e] += total;
+        }
+        __syncthreads();
+        for (int i = threadIdx.x; i < nc * E; i += 1024) cnt[g0 + i] = s_cnt[i];
     }
     __syncthreads();
     // exclusive scan of s_tot over E entries: each thread owns a contiguous run
@@ -54,7 +105,7 @@ __global__ __launch_bounds__(1024) void k_pack_scan(int32_t* __restrict__ cnt, i
     const int e1 = e0 + per < E ? e0 + per : E;
     int local = 0;
     for (int e = e0; e < e1; ++e) local += s_tot[e];
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int wid = threadIdx.x >> 6;
     int x = local;
     for (int off = 1; off < 64; off <<= 1) {
         int y = __shfl_up(x, off, 64);
@@ -72,10 +123,7 @@ __global__ __launch_bounds__(1024) void k_pack_scan(int32_t* __restrict__ cnt, i
         run += t;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += 1024) {
-        offsets[e] = s_tot[e];
-        for (int c = 0; c < nchunks; ++c) cnt[(int64_t)c * E + e] += s_tot[e];
-    }
+    for (int e = threadIdx.x; e < E; e += 1024) offsets[e] = s_tot[e];
     if (threadIdx.x == 0) offsets[E] = (int32_t)n;
 }
 
@@ -83,23 +131,29 @@ __global__ __launch_bounds__(1024) void k_pack_scan(int32_t* __restrict__ cnt, i
 __global__ __launch_bounds__(64) void k_pack_scatter(const int32_t* __restrict__ ids, int64_t n,
                                                      int topk, int E,
                                                      const int32_t* __restrict__ base,
+                                                     const int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ row_token,
                                                      int32_t* __restrict__ pos) {
     __shared__ int s_next[kPackMaxE];
-    for (int e = threadIdx.x; e < E; e += 64) s_next[e] = base[(int64_t)blockIdx.x * E + e];
+    for (int e = threadIdx.x; e < E; e += 64)
+        s_next[e] = offsets[e] + base[(int64_t)blockIdx.x * E + e];
     __syncthreads();
     int nbits = 0;
     while ((1 << nbits) < E) ++nbits;
     const int lane = threadIdx.x;
     const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
     const int64_t c0 = (int64_t)blockIdx.x * kPackChunk;
+    int ev[kPackChunk / 64];                               // all ids of the chunk in flight
+#pragma unroll
     for (int it = 0; it < kPackChunk / 64; ++it) {
         const int64_t idx = c0 + it * 64 + lane;
-        int e = -1;
-        if (idx < n) {
-            e = ids[idx];
-            if (e < 0 || e >= E) e = -1;
-        }
+        ev[it] = idx < n ? ids[idx] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kPackChunk / 64; ++it) {
+        const int64_t idx = c0 + it * 64 + lane;
+        int e = ev[it];
+        if (e < 0 || e >= E) e = -1;
         uint64_t peers = __ballot(e >= 0);
         for (int b = 0; b < nbits; ++b) {
             const uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
@@ -188,7 +242,7 @@ extern "C" int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, 
     QUADS_CHECK_LAUNCH();
     if (nchunks > 0) {
         hipLaunchKernelGGL(k_pack_scatter, dim3(nchunks), dim3(64), 0, s, topk_ids, n, (int)topk,
-                           (int)E, cnt, row_token, pos);
+                           (int)E, cnt, offsets, row_token, pos);
         QUADS_CHECK_LAUNCH();
     }
     return QUADS_OK;

@@ -48,14 +48,47 @@ __global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restri
                                                         float* __restrict__ ts_out,
                                                         uint32_t* __restrict__ table) {
     __shared__ float s_st;
+    __shared__ uint32_t s_red[2];
     const int seg = blockIdx.x;
-    tensor_scale_prologue(partial, groups, ts_in, seg, &s_st);
+    tensor_scale_prologue(partial, groups, ts_in, seg, &s_st, s_red);   // groups <= 8 * 128
     __syncthreads();
     const float s_t = s_st;
     if (threadIdx.x == 0) ts_out[seg] = s_t;
     // a fixed caller scale may let |x| * mul overflow: keep the exact path then
     build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(table + (int64_t)seg * 1024),
                           ts_in == nullptr);
+}
+
+// One 16-element block b of a segment: codes, scale byte, optional bf16 QDQ.
+__device__ __forceinline__ void quantize_block(const uint4 q0, const uint4 q1, int64_t b,
+                                               float s_t, double six_st, const uint4* s_tab,
+                                               uint8_t* ns, uint8_t* ss, uint16_t* ds) {
+    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
+    const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+    const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
+    const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
+    const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
+    *reinterpret_cast<uint2*>(ns + b * 8) = packed;
+    ss[b] = (uint8_t)sb;
+    if (ds) {
+        const float s_b = e4m3_value(sb);
+        float v[16];
+        decode8(packed.x, v);
+        decode8(packed.y, v + 8);
+        uint32_t o[8];
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const uint32_t r0 = bf16_rne_from_f64((double)(v[e] * s_b) * (double)s_t);
+            const uint32_t r1 = bf16_rne_from_f64((double)(v[e + 1] * s_b) * (double)s_t);
+            o[e >> 1] = r0 | (r1 << 16);                      // v*s_b exact; product exact
+        }
+        uint4* dp = reinterpret_cast<uint4*>(ds + b * kBlock);
+        dp[0] = make_uint4(o[0], o[1], o[2], o[3]);
+        dp[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
 }
 
 // Quantize segment blockIdx.y (rows x K elements, contiguous) of bf16 x with
@@ -77,36 +110,22 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
     uint8_t* ss = scale + (int64_t)seg * nblk;
     uint16_t* ds = dq ? dq + (int64_t)seg * seg_elems : nullptr;
     const double six_st = 6.0 * (double)s_t;                  // exact
+    // two blocks per thread per iteration (b and b + stride), loads first
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk; b += stride) {
-        const uint4* p = reinterpret_cast<const uint4*>(xs + b * kBlock);
-        const uint4 q0 = ld_stream16(p);
-        const uint4 q1 = ld_stream16(p + 1);
-        const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-        uint32_t am = 0;
+    for (int64_t b0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b0 < nblk; b0 += 2 * stride) {
+        uint4 q[2][2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
-        const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
-        const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
-        const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
-        const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
-        *reinterpret_cast<uint2*>(ns + b * 8) = packed;
-        ss[b] = (uint8_t)sb;
-        if (ds) {
-            const float s_b = e4m3_value(sb);
-            float v[16];
-            decode8(packed.x, v);
-            decode8(packed.y, v + 8);
-            uint32_t o[8];
+        for (int u = 0; u < 2; ++u) {
+            const int64_t b = b0 + u * stride;
+            const uint4* p = reinterpret_cast<const uint4*>(xs + (b < nblk ? b : b0) * kBlock);
+            q[u][0] = ld_stream16(p);
+            q[u][1] = ld_stream16(p + 1);
+        }
 #pragma unroll
-            for (int e = 0; e < 16; e += 2) {
-                const uint32_t r0 = bf16_rne_from_f64((double)(v[e] * s_b) * (double)s_t);
-                const uint32_t r1 = bf16_rne_from_f64((double)(v[e + 1] * s_b) * (double)s_t);
-                o[e >> 1] = r0 | (r1 << 16);                  // v*s_b exact; product exact
-            }
-            uint4* dp = reinterpret_cast<uint4*>(ds + b * kBlock);
-            dp[0] = make_uint4(o[0], o[1], o[2], o[3]);
-            dp[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        for (int u = 0; u < 2; ++u) {
+            const int64_t b = b0 + u * stride;
+            if (b >= nblk) break;
+            quantize_block(q[u][0], q[u][1], b, s_t, six_st, s_tab, ns, ss, ds);
         }
     }
 }
@@ -134,7 +153,7 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 }
 
 int quant_grid(int64_t nblk) {
-    int64_t g = (nblk + 255) / 256;
+    int64_t g = (nblk + 511) / 512;                           // two blocks per thread
     if (g > 4096) g = 4096;
     return (int)(g < 1 ? 1 : g);
 }

@@ -179,6 +179,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     __shared__ int s_tmp[40];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_need;
+    __shared__ int s_done;
     __shared__ uint32_t s_amax[16];
     __shared__ float s_rts;
     const int tid = threadIdx.x;
@@ -187,11 +188,14 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
         s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
         if (score_out) score_out[j] = v;
     }
-    if (tid == 0) { s_prefix = 0ull; s_need = k; }
+    if (tid == 0) { s_prefix = 0ull; s_need = k; s_done = k == 0; }
     __syncthreads();
-    // MSB-first radix select of the k-th largest key, 8 bits per pass.
+    // MSB-first radix select of the k-th largest key, 8 bits per pass.  It
+    // stops early once every key under the chosen prefix is needed: the
+    // selected set is then the keys whose prefix is greater, plus all keys
+    // with that prefix (the tie rule below takes all of them).
     unsigned long long mask = 0ull;
-    for (int shift = 56; shift >= 0; shift -= 8) {
+    for (int shift = 56; shift >= 0 && !s_done; shift -= 8) {
         if (tid < 256) s_hist[tid] = 0;
         __syncthreads();
         const unsigned long long prefix = s_prefix;
@@ -218,35 +222,38 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
             }
             const int above = incl - own;                     // count in higher bins
             if (above < need && incl >= need) {               // exactly one lane
-                int rem = need - above, d = 255 - 4 * tid;
+                int rem = need - above, d = 255 - 4 * tid, hd = h[0];
 #pragma unroll
                 for (int q = 0; q < 3; ++q) {
-                    if (h[q] >= rem) break;
+                    if (h[q] >= rem) { hd = h[q]; break; }
                     rem -= h[q];
                     --d;
+                    hd = h[q + 1];
                 }
                 s_need = rem;
                 s_prefix = prefix | ((unsigned long long)d << shift);
+                s_done = hd == rem;
             }
         }
         mask |= 0xFFull << shift;
         __syncthreads();
     }
-    const unsigned long long thr = s_prefix;    // the k-th largest key
+    // keys compare on the bits resolved so far (all 64 unless stopped early)
+    const unsigned long long thr = s_prefix;    // the k-th largest key (under mask)
     const int need_ties = s_need;               // how many keys equal to thr to take
     // ties at thr in index order: rank among equal keys via a chunked scan
     const int per = (K + 1023) / 1024;
     const int j0 = tid * per;
     const int j1 = j0 + per < K ? j0 + per : K;
     int n_eq = 0;
-    for (int j = j0; j < j1; ++j) n_eq += s_key[j] == thr;
+    for (int j = j0; j < j1; ++j) n_eq += (s_key[j] & mask) == thr;
     int total;
     int eq_before = block_excl_scan_1024(n_eq, s_tmp, &total);
     int n_sel = 0;
     {
         int e = eq_before;
         for (int j = j0; j < j1; ++j) {
-            const unsigned long long key = s_key[j];
+            const unsigned long long key = s_key[j] & mask;
             if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) ++n_sel;
         }
     }
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     {
         int e = eq_before, o = sel_before;
         for (int j = j0; j < j1; ++j) {
-            const unsigned long long key = s_key[j];
+            const unsigned long long key = s_key[j] & mask;
             if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) {
                 sel[o++] = j;
                 const uint32_t c = colmax[j];
