@@ -282,6 +282,8 @@ def main():
     for k in ("rac_gate_up", "rac_down"):
         ops[k]["hbm_frac"] = ops[k]["GB/s"] / PEAK_HBM_GBS
 
+    quant = quantizer_rate(np, torch, Q, synth, dev)
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         src = torch.ones(n, dtype=torch.float32, device=dev)
@@ -315,9 +317,65 @@ def main():
                      "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "ops": ops,
+        "quantizer": quant,
         "weight_qdq_ms": weight_qdq_ms,
     }
     print(json.dumps(line), flush=True)
+
+
+def quantizer_rate(np, torch, Q, synth, dev, reps=20):
+    """quads_nvfp4_quantize on the large-prefill gate/up input (16384 x 4096
+    bf16, Student-t body with outlier channels): algorithmic bytes (2 read +
+    0.5625 written per element) per call, with the dynamic tensor scale (a max
+    pass, then the quantize pass) and with a given tensor scale (one pass).
+    Calls go straight to the C ABI with buffers allocated once, so the rate is
+    the device's; a device-to-device copy of the same input is timed alongside
+    as context (it moves 4 bytes per element)."""
+    import ctypes
+    lib = Q.lib()
+    d = synth.make(5, with_weights=False)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    m, k = x.shape
+    nbytes = 2.5625 * m * k
+    nib = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    sc = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(4, dtype=torch.float32, device=dev)
+    ts_given = torch.empty(4, dtype=torch.float32, device=dev)
+    nws = lib.quads_nvfp4_quantize_ws(m, k)
+    ws = torch.empty(max(nws, 256), dtype=torch.uint8, device=dev)
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def P(t):
+        return ctypes.c_void_p(t.data_ptr())
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / reps
+
+    def call(ts_in):
+        st = lib.quads_nvfp4_quantize(P(x), m, k, ts_in, P(nib), P(sc), P(ts), P(ws), nws, stream)
+        if st != 0:
+            raise RuntimeError(f"quads_nvfp4_quantize failed with status {st}")
+
+    call(None)
+    ts_given.copy_(ts)
+    out = {"shape": [m, k], "algorithmic_bytes": nbytes}
+    for name, ts_in in (("dynamic_scale", None), ("given_scale", P(ts_given))):
+        us = timed(lambda: call(ts_in))
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"us": us, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+    y = torch.empty_like(x)
+    us = timed(lambda: y.copy_(x))
+    out["device_copy"] = {"us": us, "GB/s": 4.0 * m * k / (us * 1e-6) / 1e9,
+                          "hbm_frac": 4.0 * m * k / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return out
 
 
 def cpu_baseline(np, torch, data, w13q, w2q, cfg, t_sample, cores):

@@ -190,7 +190,8 @@ __device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, i
 // a code <= i and the smallest bf16 value above it to a code >= i + 1.  The
 // table builder tries mul = RN32(1 / (s_b s_t)) and its neighbours up to two
 // ulps away and checks exactly that, with the same instruction the kernels
-// use; codes where no candidate passes keep the exact compare path.
+// use, and that the largest finite bf16 gives code 7 (so that |x| * mul may
+// overflow); codes where no candidate passes keep the exact compare path.
 constexpr uint32_t kSlowPath = 0xFFFFFFFFu;
 
 __device__ __forceinline__ uint32_t fast_code(float a, float mul) {
@@ -211,7 +212,9 @@ __device__ __forceinline__ void build_table_row(int c, float s_t, bool allow_fas
             const int offs[5] = {0, -1, 1, -2, 2};
             for (int q = 0; q < 5 && mul == kSlowPath; ++q) {
                 const float r = __uint_as_float(__float_as_uint(r0) + offs[q]);
-                bool ok = true;
+                // the largest finite bf16 must give code 7 too (x * mul may
+                // overflow to inf under a caller-given tensor scale)
+                bool ok = fast_code(__uint_as_float(0x7F7F0000u), r) == 7u;
                 for (int i = 0; i < 7; ++i) {
                     const uint32_t lo = thr[i] & 0xFFFF0000u;   // largest bf16 <= threshold
                     const uint32_t hi = lo + 0x10000u;           // smallest bf16 above it

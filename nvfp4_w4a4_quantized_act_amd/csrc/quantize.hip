@@ -3,11 +3,12 @@
 // format of its section 2.2.
 //
 // Two passes over the tensor: a partial-max pass (one value per work-group)
-// and the quantize pass, whose work-groups first fold the partial maxima into
-// the tensor scale, then build a per-tensor table of element-code thresholds
-// for all 127 block-scale codes in LDS, then stream 16-element blocks: one
-// block per lane per iteration, two 16-byte loads, one 8-byte nibble store
-// and one scale byte.
+// and the quantize pass, after a one-work-group step that folds the partial
+// maxima into the tensor scale and builds the per-tensor table of
+// element-code thresholds for all 127 block-scale codes.  The quantize pass
+// streams half-blocks: one 16-byte load per lane (a wave reads 1 KB
+// contiguous), the block maximum shared with the neighbouring lane, one
+// 4-byte nibble store, one scale byte per block.
 #include "common.h"
 
 namespace quads {
@@ -54,45 +55,63 @@ __global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restri
     __syncthreads();
     const float s_t = s_st;
     if (threadIdx.x == 0) ts_out[seg] = s_t;
-    // a fixed caller scale may let |x| * mul overflow: keep the exact path then
     build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(table + (int64_t)seg * 1024),
-                          ts_in == nullptr);
+                          true);
 }
 
-// One 16-element block b of a segment: codes, scale byte, optional bf16 QDQ.
-__device__ __forceinline__ void quantize_block(const uint4 q0, const uint4 q1, int64_t b,
-                                               float s_t, double six_st, const uint4* s_tab,
-                                               uint8_t* ns, uint8_t* ss, uint16_t* ds) {
-    const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
-    uint32_t am = 0;
+constexpr int kQuantUnroll = 4;                 // half-block loads in flight per lane
+
+// Half-block h (8 elements) of a segment, the other half on the neighbouring
+// lane (h ^ 1): block maximum by one shuffle, then codes (4 bytes), the
+// block's scale byte (even lane) and the optional bf16 QDQ (16 bytes).
+template <bool kDq>
+__device__ __forceinline__ void quantize_half(const uint4 q, int64_t h, float s_t, double six_st,
+                                              const uint4* s_tab, uint8_t* ns, uint8_t* ss,
+                                              uint16_t* ds) {
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    uint32_t am = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
+                             pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
+    am = (am & 0xFFFFu) > (am >> 16) ? (am & 0xFFFFu) : (am >> 16);
+    const uint32_t o = __shfl_xor(am, 1, 64);
+    am = o > am ? o : am;
+    const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)bf16_to_f32(am) / six_st) : 0u;
+    const uint4 t1 = s_tab[2 * sb + 1];                       // word 7: fast-path multiplier
+    uint32_t codes = 0u;
+    if (t1.w != kSlowPath) {
+        const float mul = __uint_as_float(t1.w);
+#define QUADS_ENC_HALF(e, sel)                                                          \
+    codes = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(codes, __uint_as_float(w[e] << 16) * mul, \
+                                                     __uint_as_float(w[e] & 0xFFFF0000u) * mul, \
+                                                     1.0f, sel)
+        QUADS_ENC_HALF(0, 0); QUADS_ENC_HALF(1, 1); QUADS_ENC_HALF(2, 2); QUADS_ENC_HALF(3, 3);
+#undef QUADS_ENC_HALF
+    } else {
+        const uint4 t0 = s_tab[2 * sb];
+        const uint32_t thr[7] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
-    const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
-    const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
-    const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
-    const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
-    *reinterpret_cast<uint2*>(ns + b * 8) = packed;
-    ss[b] = (uint8_t)sb;
-    if (ds) {
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t hb = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            codes |= (e2m1_mag_code((hb & 0x7FFFu) << 16, thr) | ((hb >> 12) & 8u)) << (4 * e);
+        }
+    }
+    *reinterpret_cast<uint32_t*>(ns + h * 4) = codes;
+    if ((h & 1) == 0) ss[h >> 1] = (uint8_t)sb;
+    if (kDq) {
         const float s_b = e4m3_value(sb);
-        float v[16];
-        decode8(packed.x, v);
-        decode8(packed.y, v + 8);
-        uint32_t o[8];
+        float v[8];
+        decode8(codes, v);
+        uint32_t ob[4];
 #pragma unroll
-        for (int e = 0; e < 16; e += 2) {
+        for (int e = 0; e < 8; e += 2) {
             const uint32_t r0 = bf16_rne_from_f64((double)(v[e] * s_b) * (double)s_t);
             const uint32_t r1 = bf16_rne_from_f64((double)(v[e + 1] * s_b) * (double)s_t);
-            o[e >> 1] = r0 | (r1 << 16);                      // v*s_b exact; product exact
+            ob[e >> 1] = r0 | (r1 << 16);                    // v*s_b exact; product exact
         }
-        uint4* dp = reinterpret_cast<uint4*>(ds + b * kBlock);
-        dp[0] = make_uint4(o[0], o[1], o[2], o[3]);
-        dp[1] = make_uint4(o[4], o[5], o[6], o[7]);
+        *reinterpret_cast<uint4*>(ds + h * 8) = make_uint4(ob[0], ob[1], ob[2], ob[3]);
     }
 }
 
-// Quantize segment blockIdx.y (rows x K elements, contiguous) of bf16 x with
-// the tensor scale ts[seg] and code table of k_scale_finalize.
+template <bool kDq>
 __global__ __launch_bounds__(256) void k_quantize_bf16(
     const uint16_t* __restrict__ x, int64_t seg_elems, const float* __restrict__ ts,
     const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
@@ -104,28 +123,28 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
     const float s_t = ts[seg];
     __syncthreads();
 
-    const int64_t nblk = seg_elems / kBlock;
+    const int64_t nhalf = seg_elems / 8;                      // even: whole blocks
     const uint16_t* xs = x + (int64_t)seg * seg_elems;
     uint8_t* ns = nib + (int64_t)seg * (seg_elems / 2);
-    uint8_t* ss = scale + (int64_t)seg * nblk;
-    uint16_t* ds = dq ? dq + (int64_t)seg * seg_elems : nullptr;
+    uint8_t* ss = scale + (int64_t)seg * (seg_elems / kBlock);
+    uint16_t* ds = kDq ? dq + (int64_t)seg * seg_elems : nullptr;
     const double six_st = 6.0 * (double)s_t;                  // exact
-    // two blocks per thread per iteration (b and b + stride), loads first
+    // lane i of a wave reads 16 contiguous bytes (a wave: 1 KB); the two
+    // lanes of a block are neighbours; four reads in flight per lane.  A
+    // lane and its neighbour are both in range or both out (nhalf is even).
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t b0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b0 < nblk; b0 += 2 * stride) {
-        uint4 q[2][2];
+    for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h0 < nhalf;
+         h0 += kQuantUnroll * stride) {
+        uint4 q[kQuantUnroll];
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t b = b0 + u * stride;
-            const uint4* p = reinterpret_cast<const uint4*>(xs + (b < nblk ? b : b0) * kBlock);
-            q[u][0] = ld_stream16(p);
-            q[u][1] = ld_stream16(p + 1);
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t h = h0 + u * stride;
+            q[u] = ld_stream16(xs + (h < nhalf ? h : h0) * 8);
         }
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int64_t b = b0 + u * stride;
-            if (b >= nblk) break;
-            quantize_block(q[u][0], q[u][1], b, s_t, six_st, s_tab, ns, ss, ds);
+        for (int u = 0; u < kQuantUnroll; ++u) {
+            const int64_t h = h0 + u * stride;
+            if (h < nhalf) quantize_half<kDq>(q[u], h, s_t, six_st, s_tab, ns, ss, ds);
         }
     }
 }
@@ -153,8 +172,8 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 }
 
 int quant_grid(int64_t nblk) {
-    int64_t g = (nblk + 511) / 512;                           // two blocks per thread
-    if (g > 4096) g = 4096;
+    int64_t g = (2 * nblk + 256 * kQuantUnroll - 1) / (256 * kQuantUnroll);  // half-blocks
+    if (g > 8192) g = 8192;
     return (int)(g < 1 ? 1 : g);
 }
 
@@ -197,7 +216,7 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     }
     launch_scale_finalize(partial, groups, ts_in, 1, ts_out, table, s);
     QUADS_CHECK_LAUNCH();
-    hipLaunchKernelGGL(k_quantize_bf16, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
+    hipLaunchKernelGGL(k_quantize_bf16<false>, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
                        ts_out, table, nib, scale, (uint16_t*)nullptr);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
@@ -234,8 +253,12 @@ extern "C" int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, i
     int64_t qg = quant_grid(n / kBlock);
     int64_t cap = (4096 + E - 1) / E;
     if (qg > cap) qg = cap < 1 ? 1 : cap;
-    hipLaunchKernelGGL(k_quantize_bf16, dim3((unsigned)qg, (unsigned)E), dim3(256), 0, s, w, n,
-                       w_ts, table, w_nib, w_scale, w_dq);
+    if (w_dq)
+        hipLaunchKernelGGL(k_quantize_bf16<true>, dim3((unsigned)qg, (unsigned)E), dim3(256), 0, s,
+                           w, n, w_ts, table, w_nib, w_scale, w_dq);
+    else
+        hipLaunchKernelGGL(k_quantize_bf16<false>, dim3((unsigned)qg, (unsigned)E), dim3(256), 0,
+                           s, w, n, w_ts, table, w_nib, w_scale, w_dq);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }
