@@ -9,16 +9,18 @@
 // gfx950's block-scaled fp4 MFMA takes one power-of-two scale per 32
 // elements, which cannot express E4M3 scales over 16 elements exactly.
 //
-// Tiling: 256 threads, a 128 x 128 output tile, K staged 64 at a time.  Each
-// thread loads 32 fp4 codes (16 bytes) and their two scale bytes of one A row
-// and one W row, converts them to fp16 (hardware fp4 -> fp16 convert, then a
-// packed fp16 multiply by the block scale) and stores them to LDS.  Four
-// waves (2 x 2) each own a 64 x 64 sub-tile = 2 x 2 MFMA tiles.
+// Two kernels.  When K and k are multiples of 64 (every workload here), the
+// 256 x 256-tile kernel in namespace v2 below runs; its comment describes it.
+// Otherwise a plain 128 x 128-tile kernel does: 256 threads, K staged 64 at a
+// time; each thread dequantizes 32 codes of one A row and one W row to fp16
+// (hardware fp4 -> fp16 convert, then a packed fp16 multiply by the block
+// scale) into LDS, and four waves (2 x 2) each own a 64 x 64 sub-tile.
 //
-// Compensation: after the main K loop the same tile runs a second, short
-// loop over the k selected channels: A = the second-pass residual codes, B =
-// the weight columns sel[i] gathered per row.  It accumulates into its own
-// fp32 registers because its tensor scale differs; the epilogue forms
+// Compensation in the 128 x 128 kernel: after the main K loop the same tile
+// runs a second, short loop over the k selected channels: A = the
+// second-pass residual codes, B = the weight columns sel[i] gathered per row.
+// It accumulates into its own fp32 registers because its tensor scale
+// differs; the epilogue forms
 //   Y = acc_main * (s_tA s_tW[e]) + acc_comp * (s_tR s_tW[e]).
 #include "common.h"
 
@@ -338,6 +340,13 @@ __device__ __forceinline__ Raw load_raw(const uint8_t* nib_row, const uint8_t* s
     return r;
 }
 
+// Two fp32 values to packed bf16 (round to nearest even, hardware convert).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
 __device__ __forceinline__ f16x8 cvt8(uint32_t w, _Float16 s) {
     const f16x2 s2 = {s, s};
     const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
@@ -586,24 +595,20 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
     // end read R row 0 (src = 0); their results are never written.
     const uint8_t* r_nib_row = kc > 0 ? g.r_nib + src * (g.k / 2) : a_nib_row;
     const uint8_t* r_sc_row = kc > 0 ? g.r_scale + src * (g.k / kBlock) : a_sc_row;
-    {
-        const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, true);
-        store_slice(rb, smem + BM * BK, lr, lh);
-        if (ALIVE) {
-            const Raw ra = load_raw(a_nib_row, a_sc_row, 32 * lh, true);
-            store_slice(ra, smem, lr, lh);
-        }
-    }
-    Raw a0, b0;
+    // stages 0 and 1 are loaded together, then stage 0 is converted and stored
+    Raw ra, a0;
     if (!ALIVE) {
-        a0.n = make_uint4(0, 0, 0, 0);
-        a0.sc = 0;
-    } else if (nk > 1) {
-        a0 = load_raw(a_nib_row, a_sc_row, BK + 32 * lh, true);
+        ra.n = a0.n = make_uint4(0, 0, 0, 0);
+        ra.sc = a0.sc = 0;
     } else {
-        a0 = load_raw(r_nib_row, r_sc_row, 32 * lh, true);
+        ra = load_raw(a_nib_row, a_sc_row, 32 * lh, true);
+        a0 = nk > 1 ? load_raw(a_nib_row, a_sc_row, BK + 32 * lh, true)
+                    : load_raw(r_nib_row, r_sc_row, 32 * lh, true);
     }
-    b0 = load_raw(w_nib_row, w_sc_row, min(BK, klast) + 32 * lh, true);
+    const Raw rb = load_raw(w_nib_row, w_sc_row, 32 * lh, true);
+    Raw b0 = load_raw(w_nib_row, w_sc_row, min(BK, klast) + 32 * lh, true);
+    store_slice(rb, smem + BM * BK, lr, lh);
+    if (ALIVE) store_slice(ra, smem, lr, lh);
     __syncthreads();
     for (int it = 0; it < nk; ++it) {
         _Float16* cur = smem + (it & 1) * kStage;
@@ -630,6 +635,82 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
     const _Float16* rbuf = smem + (nk & 1) * kStage;
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) mma_kk<MACT>(rbuf, ws_s, fo[kk], wm, wn, acc);
+}
+
+// Epilogue of a 256 x 256 tile: acc scaled by ca; SwiGLU to bf16 or plain
+// fp32 / bf16 stores, four consecutive features per lane.
+template <int kEpi>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][2], float ca,
+                                         int m0, int mend, int f0, int wm, int wn, int mact,
+                                         int lane) {
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int prow_l = m0 + wm * 128 + (lane & 31);
+    const int nq = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= mact) continue;
+        const int prow = prow_l + mi * 32;
+        if (prow >= mend) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
+            if (swiglu) {
+                const int feat = f0 + wn * 32 + 8 * q + nq;      // features feat .. feat + 3
+                float hv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float gt = acc[mi][0][4 * q + u] * ca;
+                    const float up = acc[mi][1][4 * q + u] * ca;
+                    // silu(g) u with the hardware exp2 and reciprocal: relative
+                    // error a few 1e-6, far inside half a bf16 ulp (2^-9)
+                    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+                    hv[u] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+                }
+                const uint32_t p01 = pk_bf16(hv[0], hv[1]), p23 = pk_bf16(hv[2], hv[3]);
+                const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+                const int nh = g.N / 2;
+                uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
+                if (feat + 3 < nh && (nh & 3) == 0) {
+                    *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca;
+                    const int64_t o = (int64_t)prow * g.N + n;
+                    const bool vec = n + 3 < g.N && (g.N & 3) == 0;
+                    if (g.out_bf16) {
+                        uint16_t* ob = (uint16_t*)g.out + o;
+                        const uint32_t p01 = pk_bf16(y[0], y[1]), p23 = pk_bf16(y[2], y[3]);
+                        if (vec) {
+                            *reinterpret_cast<uint2*>(ob) = make_uint2(p01, p23);
+                        } else {
+                            const uint32_t b4[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu,
+                                                    p23 >> 16};
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) ob[u] = (uint16_t)b4[u];
+                        }
+                    } else {
+                        float* of = (float*)g.out + o;
+                        if (vec) {
+                            *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) of[u] = y[u];
+                        }
+                    }
+                }
+            }
+        }
+    }
 }
 
 template <int kEpi>
@@ -712,74 +793,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     }
 
     // epilogue
-    const float ca = cscale * g.w_ts[e];
-    const int prow_l = m0 + wm * 128 + (lane & 31);
-    const int nq = 4 * (lane >> 5);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-        if (mi >= mact) continue;
-        const int prow = prow_l + mi * 32;
-        if (prow >= mend) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
-            if (swiglu) {
-                const int feat = f0 + wn * 32 + 8 * q + nq;      // features feat .. feat + 3
-                uint32_t hb[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float gt = acc[mi][0][4 * q + u] * ca;
-                    const float up = acc[mi][1][4 * q + u] * ca;
-                    // silu(g) u with the hardware exp2 and reciprocal: relative
-                    // error a few 1e-6, far inside half a bf16 ulp (2^-9)
-                    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
-                    hb[u] = bf16_rne_from_f32(gt * __builtin_amdgcn_rcpf(1.0f + ex) * up);
-                }
-                const int nh = g.N / 2;
-                uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
-                if (feat + 3 < nh && (nh & 3) == 0) {
-                    *reinterpret_cast<uint2*>(o) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (feat + u < nh) o[u] = (uint16_t)hb[u];
-                }
-            } else {
-#pragma unroll
-                for (int nj = 0; nj < 2; ++nj) {
-                    const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
-                    float y[4];
-#pragma unroll
-                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca;
-                    const int64_t o = (int64_t)prow * g.N + n;
-                    const bool vec = n + 3 < g.N && (g.N & 3) == 0;
-                    if (g.out_bf16) {
-                        uint16_t* ob = (uint16_t*)g.out + o;
-                        if (vec) {
-                            *reinterpret_cast<uint2*>(ob) =
-                                make_uint2(bf16_rne_from_f32(y[0]) | (bf16_rne_from_f32(y[1]) << 16),
-                                           bf16_rne_from_f32(y[2]) | (bf16_rne_from_f32(y[3]) << 16));
-                        } else {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                if (n + u < g.N) ob[u] = (uint16_t)bf16_rne_from_f32(y[u]);
-                        }
-                    } else {
-                        float* of = (float*)g.out + o;
-                        if (vec) {
-                            *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
-                        } else {
-#pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                if (n + u < g.N) of[u] = y[u];
-                        }
-                    }
-                }
-            }
-        }
-    }
+    epilogue<kEpi>(g, acc, cscale * g.w_ts[e], m0, mend, f0, wm, wn, mact, lane);
 }
 
 }  // namespace v2
+
 
 }  // namespace quads
 
