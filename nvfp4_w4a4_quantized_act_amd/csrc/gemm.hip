@@ -474,13 +474,37 @@ __device__ __forceinline__ void stage(const _Float16* cur, _Float16* nxt, const 
     }
 }
 
-// find_tile_bm computed by each wave on its own (no LDS, no barrier): lane l
-// counts the tiles of experts l*per .. l*per + per - 1, a wave scan gives the
-// first tile of each lane's range, and the owning lane broadcasts the result.
-__device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int bm,
-                               int* e_out, int* m0_out, int* mend_out) {
+// Tile `tile` of the M-tile list, found by each wave on its own (no LDS, no
+// barrier).  An expert with n rows gets t = ceil(n / bm) tiles, its rows split
+// evenly over them in 32-row multiples (a 280-row expert gets 160 + 120 rows
+// rather than 256 + 24, so neither tile is a near-empty one).  The list is
+// ordered by tile height, tallest first (experts in index order within a
+// height): the hardware hands each next work-group to the first free CU, so
+// the short tiles, dispatched last, fill in the tail (longest-first list
+// scheduling).  Lane l looks after experts l*per .. l*per + per - 1; for each
+// height a wave scan gives the first tile of each lane's share, and the
+// owning lane broadcasts the result.
+__device__ __forceinline__ int tile_height(int n, int bm, int* t_out) {
+    const int t = (n + bm - 1) / bm;
+    *t_out = t;
+    return t > 0 ? ((n + t - 1) / t + 31) / 32 : 0;          // in 32-row blocks
+}
+
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+template <int BMT>
+__device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
+                               int* m0_out, int* mend_out) {
+    constexpr int kH = BMT / 32;                  // tile heights 1 .. kH blocks
     if (offsets == nullptr) {
-        const int64_t m0 = (int64_t)tile * bm;
+        const int64_t m0 = (int64_t)tile * BMT;
         *e_out = 0;
         *m0_out = (int)m0;
         *mend_out = (int)rows;
@@ -490,39 +514,51 @@ __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int 
     const int per = (E + 63) / 64;
     const int e0 = lane * per;
     const int e1 = e0 + per < E ? e0 + per : E;
-    int local = 0;
-    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-    int x = local;
+    int cnt[kH];                                  // this lane's tiles of each height
 #pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
+    for (int q = 0; q < kH; ++q) cnt[q] = 0;
+    for (int e = e0; e < e1; ++e) {
+        int t;
+        const int hgt = tile_height(offsets[e + 1] - offsets[e], BMT, &t);
+#pragma unroll
+        for (int q = 0; q < kH; ++q) cnt[q] += hgt == q + 1 ? t : 0;
     }
-    int run = x - local, fe = -1, fm0 = 0, fme = 0;
-    if (tile >= run && tile < x) {
-        for (int e = e0; e < e1; ++e) {
-            const int n = offsets[e + 1] - offsets[e];
-            const int t = (n + bm - 1) / bm;
-            if (tile < run + t) {
-                // the expert's rows split evenly over its t tiles, in 32-row
-                // multiples: a 280-row expert gets 160 + 120 rows rather than
-                // 256 + 24, so neither tile is a near-empty one
-                const int per_tile = ((n + t - 1) / t + 31) / 32 * 32;
-                fe = e;
-                fm0 = offsets[e] + (tile - run) * per_tile;
-                fme = fm0 + per_tile < offsets[e + 1] ? fm0 + per_tile : offsets[e + 1];
-                break;
+    int all = 0;
+#pragma unroll
+    for (int q = 0; q < kH; ++q) all += cnt[q];
+    // work-groups past the last tile leave after one scan
+    if (tile >= __builtin_amdgcn_readlane(wave_scan(all, lane), 63)) return false;
+    int base = 0;                                 // tiles of the taller heights
+#pragma unroll
+    for (int q = kH - 1; q >= 0; --q) {
+        const int hgt = q + 1;
+        const int x = wave_scan(cnt[q], lane);
+        const int total = __builtin_amdgcn_readlane(x, 63);       // uniform: scalar branches
+        if (tile < base + total) {
+            int run = base + x - cnt[q], fe = -1, fm0 = 0, fme = 0;
+            if (tile >= run && tile < run + cnt[q]) {
+                for (int e = e0; e < e1; ++e) {
+                    const int n = offsets[e + 1] - offsets[e];
+                    int t;
+                    if (tile_height(n, BMT, &t) != hgt) continue;
+                    if (tile < run + t) {
+                        fe = e;
+                        fm0 = offsets[e] + (tile - run) * hgt * 32;
+                        fme = fm0 + hgt * 32 < offsets[e + 1] ? fm0 + hgt * 32 : offsets[e + 1];
+                        break;
+                    }
+                    run += t;
+                }
             }
-            run += t;
+            const int src = __ffsll(__ballot(fe >= 0)) - 1;
+            *e_out = __builtin_amdgcn_readlane(fe, src);
+            *m0_out = __builtin_amdgcn_readlane(fm0, src);
+            *mend_out = __builtin_amdgcn_readlane(fme, src);
+            return true;
         }
+        base += total;
     }
-    const unsigned long long owners = __ballot(fe >= 0);
-    if (owners == 0ull) return false;
-    const int src = __ffsll(owners) - 1;
-    *e_out = __shfl(fe, src, 64);
-    *m0_out = __shfl(fm0, src, 64);
-    *mend_out = __shfl(fme, src, 64);
-    return true;
+    return false;
 }
 
 // Weight row of B-tile row r.  Plain: f0 + r.  SwiGLU: the tile holds 128
@@ -723,7 +759,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     const int tile = (slot / grp) * (kXcds * grp) + (h % kXcds) * grp + slot % grp;
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
-    if (!find_tile_wave(g.offsets, g.E, g.rows, tile_m, BM, &e, &m0, &mend)) return;
+    if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend)) return;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
