@@ -20,8 +20,10 @@ Inputs are seeded synthetic tensors (synth.py) already resident in HBM when
 the timed region starts.  `value` is the step's algorithmic GEMM work,
 2 * rows * N * (K + k) summed over both GEMMs, divided by the step time.
 `roofline` is for the dominant kernel, the gate/up GEMM: its algorithmic
-flops per launch over its mean launch time (HIP events on the launch stream),
-against the dense fp16 MFMA peak (the GEMM's operands are exact fp16);
+flops per launch over its mean launch time (a pair of HIP events on the
+launch stream around it in every timed step; an event record leaves the GPU
+idle for a few microseconds, so the other per-op times in `ops` come from
+extra steps after the timed region), against the dense fp16 MFMA peak (the GEMM's operands are exact fp16);
 `traffic` is its HBM-side bytes per launch from the FETCH_SIZE / WRITE_SIZE
 counter summary under profiles/ (null when that summary was taken on other
 GEMM sources).  `cpu_baseline` times the NumPy oracle on a bounded sample of
@@ -215,14 +217,17 @@ def main():
     weight_qdq_ms = ev[0].elapsed_time(ev[1]) / 3
     del w13, w2
 
-    nev = 12
-    timers = []
+    # Each event record costs the GPU a few microseconds of idle time, so the
+    # timed steps bracket only the gate/up GEMM (the roofline kernel); the
+    # per-op breakdown comes from extra steps after the timed region.
+    nev = 7
+    timers, gemm_timers = [], []
 
-    def step(record):
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)] if record else None
+    def step(mode):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)] if mode else None
 
         def mark(i):
-            if record:
+            if mode == "all" or (mode == "gemm" and i in (2, 3)):
                 evs[i].record()
         mark(0)
         a = Q.quads_rac_quantize(x, KR)
@@ -242,25 +247,33 @@ def main():
         mark(5)
         out = Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
         mark(6)
-        if record:
+        if mode == "all":
             timers.append(evs)
+        elif mode == "gemm":
+            gemm_timers.append(evs)
         return out
 
     for _ in range(args.warmup):
-        step(False)
+        step(None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        step("gemm")
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
+    for _ in range(max(3, min(args.steps, 10))):
+        step("all")
+    torch.cuda.synchronize()
 
     names = ["rac_gate_up", "pack", "gemm_gate_up_swiglu", "rac_down", "gemm_down", "combine"]
     per_op = {n: 0.0 for n in names}
     for evs in timers:
         for i, n in enumerate(names):
             per_op[n] += evs[i].elapsed_time(evs[i + 1]) / len(timers)
+    # the roofline kernel's duration: events of the timed steps
+    per_op["gemm_gate_up_swiglu"] = sum(e[2].elapsed_time(e[3]) for e in gemm_timers) / len(
+        gemm_timers)
 
     fl_gu = 2.0 * rows * (2 * I) * (H + KR)
     fl_dn = 2.0 * rows * H * (I + KR)
