@@ -1,0 +1,169 @@
+"""Accuracy sweep: the output error of W4A4 and W4A4+RAC as the number of
+compensated channels grows (QUADS, arXiv 2607.15810: section 4.3.3 with
+Table 3, and section 3.3 with Fig. 4(b)).
+
+The pages measure the training/inference gap on a model: the largest
+log-probability difference (Table 3, residual ratios 12.5 % to 100 %) and the
+per-layer MoE output distance (Fig. 4(b)).  With no model here, the same
+quantity is taken at one GEMM on the synthetic workloads, every step on the
+GPU through the library:
+
+  Y(k)   W4A4 GEMM (fp32 out) of RAC(X, k) with the NVFP4 weights;
+  Y_qat  X Wq^T in fp64, Wq = the library's NVFP4 QDQ of W in bf16: what the
+         learner computes under asymmetric W4A16 QAT (section 3.2, Eq. (12)),
+         so the gap left is the rollout's activation error that RAC targets
+         (and the bf16 rounding of Wq);
+  Y_16   X W^T in fp64 with the bf16 weights: no weight alignment.
+
+Reported per k (0, 12.5, 25, 50, 75 and 100 % of K, rounded to 64 channels):
+relative Frobenius distances |Y(k) - Y_qat| / |Y_qat| and |Y(k) - Y_16| /
+|Y_16|, and the largest element error relative to max |Y_qat|.
+
+Workloads: dense = X [4096, 4096] Student-t(3) with 41 outlier channels x20,
+W [4096, 4096] N(0, 0.02); moe = the gate/up GEMM of the MoE layer, X [4096,
+2048] with 20 outlier channels x20, 128 experts, top-8 softmax routing, W13
+[128, 1536, 2048].  The fp64 references run on the host CPU (numpy).
+
+    python -m nvfp4_w4a4_quantized_act_amd.sweep [--workloads dense,moe] [--tokens T]
+"""
+
+import argparse
+import json
+import os
+import sys
+
+import numpy as np
+
+FRACTIONS = (0.0, 0.125, 0.25, 0.5, 0.75, 1.0)
+
+
+def _f64(bits):
+    """bf16 bit patterns (uint16 / int16) -> float64."""
+    b = np.ascontiguousarray(bits).view(np.uint16).astype(np.uint32) << np.uint32(16)
+    return b.view(np.float32).astype(np.float64)
+
+
+def channels_for(frac, kdim):
+    """k for a ratio of K: a multiple of 64 (the GEMM's stage), at least 64 when frac > 0."""
+    if frac <= 0:
+        return 0
+    return int(min(kdim, max(64, round(frac * kdim / 64) * 64)))
+
+
+def _errors(y, y_qat, y_16):
+    d_qat = y - y_qat
+    return dict(rel_qat=float(np.linalg.norm(d_qat) / np.linalg.norm(y_qat)),
+                rel_bf16=float(np.linalg.norm(y - y_16) / np.linalg.norm(y_16)),
+                max_qat=float(np.abs(d_qat).max() / np.abs(y_qat).max()))
+
+
+def _gpu_gemm(Q, torch, x_t, k, wq, n, rows, offsets=None, row_token=None):
+    a = Q.quads_rac_quantize(x_t, k)
+    r = (a["r_nib"], a["r_scale"], a["r_ts"]) if k else None
+    y = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), wq, n, rows=rows, r=r,
+                              sel=a["sel"] if k else None, offsets=offsets,
+                              row_token=row_token, out_dtype=Q.OUT_F32)
+    torch.cuda.synchronize()
+    return y.cpu().numpy().astype(np.float64)
+
+
+def sweep_dense(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
+    """Rows of the sweep for the dense workload (synth config 2, sizes overridable)."""
+    d = synth.make(2, **overrides)
+    x, w = d["x"], d["w"]                         # bf16 bits [M, K], [1, N, K]
+    m, kdim = x.shape
+    n = w.shape[1]
+    x_t = torch.from_numpy(x.view(np.int16)).to(dev)
+    w_t = torch.from_numpy(w.view(np.int16)).to(dev)
+    nib, scale, ts, dq = Q.quads_nvfp4_weight_qdq(w_t, want_dq=True)
+    torch.cuda.synchronize()
+    xf = _f64(x)
+    y_qat = xf @ _f64(dq[0].cpu().numpy()).T
+    y_16 = xf @ _f64(w[0]).T
+    out = []
+    for f in fractions:
+        k = channels_for(f, kdim)
+        y = _gpu_gemm(Q, torch, x_t, k, (nib, scale, ts), n, m)
+        out.append(dict(workload="dense", M=m, K=kdim, N=n, frac=f, k=k,
+                        **_errors(y, y_qat, y_16)))
+    return out
+
+
+def sweep_moe(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
+    """Rows of the sweep for the MoE gate/up GEMM (synth config 3, sizes overridable)."""
+    d = synth.make(3, **overrides)
+    x, ids, w13 = d["x"], d["topk_ids"], d["w13"]   # [T, H], [T, top_k], [E, 2I, H]
+    t, kdim = x.shape
+    e, n, _ = w13.shape
+    x_t = torch.from_numpy(x.view(np.int16)).to(dev)
+    ids_t = torch.from_numpy(ids).to(dev)
+    w_t = torch.from_numpy(w13.view(np.int16)).to(dev)
+    nib, scale, ts, dq = Q.quads_nvfp4_weight_qdq(w_t, want_dq=True)
+    off_t, rt_t, _pos = Q.quads_moe_pack(ids_t, e)
+    torch.cuda.synchronize()
+    off = off_t.cpu().numpy()
+    rt = rt_t.cpu().numpy()
+    rows = int(off[-1])
+    xf = _f64(x)
+    y_qat = np.empty((rows, n))
+    y_16 = np.empty((rows, n))
+    for j in range(e):                             # packed rows of expert j
+        sl = slice(off[j], off[j + 1])
+        if off[j] == off[j + 1]:
+            continue
+        xa = xf[rt[sl]]
+        y_qat[sl] = xa @ _f64(dq[j].cpu().numpy()).T
+        y_16[sl] = xa @ _f64(w13[j]).T
+    del dq
+    out = []
+    for f in fractions:
+        k = channels_for(f, kdim)
+        y = _gpu_gemm(Q, torch, x_t, k, (nib, scale, ts), n, rows, off_t, rt_t)
+        out.append(dict(workload="moe_gate_up", T=t, E=e, K=kdim, N=n, rows=rows, frac=f, k=k,
+                        **_errors(y, y_qat, y_16)))
+    return out
+
+
+def table(rows):
+    lines = ["| workload | k / K | k | rel. Frobenius vs QAT ref. | rel. Frobenius vs bf16 | "
+             "max element vs QAT ref. |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        lines.append(f"| {r['workload']} | {100 * r['frac']:.1f} % | {r['k']} | "
+                     f"{r['rel_qat']:.5f} | {r['rel_bf16']:.5f} | {r['max_qat']:.5f} |")
+    return "\n".join(lines)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--workloads", default="dense,moe")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the token count (0: the workloads' own)")
+    args = ap.parse_args(argv)
+    import torch
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    if root not in sys.path:
+        sys.path.insert(0, root)
+    import synth
+
+    import nvfp4_w4a4_quantized_act_amd as Q
+    Q.lib()
+    dev = torch.device("cuda:0")
+    rows = []
+    for wl in args.workloads.split(","):
+        if wl == "dense":
+            kw = dict(m=args.tokens) if args.tokens else {}
+            got = sweep_dense(Q, torch, synth, dev, **kw)
+        elif wl == "moe":
+            kw = dict(t=args.tokens) if args.tokens else {}
+            got = sweep_moe(Q, torch, synth, dev, **kw)
+        else:
+            raise SystemExit(f"unknown workload {wl}")
+        for r in got:
+            print(json.dumps(r), flush=True)
+        rows += got
+    print(table(rows))
+
+
+if __name__ == "__main__":
+    main()
