@@ -27,7 +27,10 @@ extra steps after the timed region), against the dense fp16 MFMA peak (the GEMM'
 `traffic` is its HBM-side bytes per launch from the FETCH_SIZE / WRITE_SIZE
 counter summary under profiles/ (null when that summary was taken on other
 GEMM sources).  `cpu_baseline` times the NumPy oracle on a bounded sample of
-the same layer.
+the same layer.  `comparator` times the same gate/up GEMM as an MX
+block-scaled GEMM with FP8 and with FP4 elements (quads_moe_mx_gemm), the
+FP8 W8A8 baseline the paper's speed claim is measured against, next to the
+W4A4+RAC GEMM.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -215,7 +218,14 @@ def main():
     ev[1].record()
     torch.cuda.synchronize()
     weight_qdq_ms = ev[0].elapsed_time(ev[1]) / 3
-    del w13, w2
+    # the MX comparator's weights (FP8 and FP4 elements, E8M0 per 32), quantized
+    # once like the NVFP4 ones
+    w13_2d = w13.view(E * 2 * I, H)
+    w13_mx = {}
+    for fmt_name, fmt in (("mxfp8", Q.MX_FP8), ("mxfp4", Q.MX_FP4)):
+        c, sc = Q.quads_mx_quantize(w13_2d, fmt)
+        w13_mx[fmt_name] = (c.view(E, 2 * I, -1), sc.view(E, 2 * I, -1), fmt)
+    del w13, w2, w13_2d
 
     # Each event record costs the GPU a few microseconds of idle time, so the
     # timed steps bracket only the gate/up GEMM (the roofline kernel); the
@@ -296,6 +306,8 @@ def main():
         ops[k]["hbm_frac"] = ops[k]["GB/s"] / PEAK_HBM_GBS
 
     quant = quantizer_rate(np, torch, Q, synth, dev)
+    comparator = mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx,
+                               per_op["gemm_gate_up_swiglu"], fl_gu)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -331,6 +343,7 @@ def main():
         "cpu_baseline": cpu,
         "ops": ops,
         "quantizer": quant,
+        "comparator": comparator,
         "weight_qdq_ms": weight_qdq_ms,
     }
     print(json.dumps(line), flush=True)
@@ -388,6 +401,39 @@ def quantizer_rate(np, torch, Q, synth, dev, reps=20):
     us = timed(lambda: y.copy_(x))
     out["device_copy"] = {"us": us, "GB/s": 4.0 * m * k / (us * 1e-6) / 1e9,
                           "hbm_frac": 4.0 * m * k / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    return out
+
+
+def mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx, w4a4_ms, w4a4_flops, reps=20):
+    """The gate/up GEMM of the same layer (same tokens, routing and SwiGLU bf16
+    output) as an MX block-scaled GEMM (quads_moe_mx_gemm): FP8 E4M3 elements,
+    the FP8 W8A8 baseline of the paper's speed claim, and FP4 E2M1 elements
+    (power-of-two scales per 32: not NVFP4).  Activations are MX-quantized
+    from the same bf16 x; timed with events over `reps` launches.  Reported
+    beside the W4A4+RAC gate/up GEMM of the timed steps."""
+    off, rt, _ = Q.quads_moe_pack(ids, E)
+    out = {"workload": "gate/up GEMM, 32768 packed rows x 1536 x 2048, SwiGLU bf16 out",
+           "w4a4_rac": {"us": w4a4_ms * 1e3,
+                        "TFLOP/s": w4a4_flops / (w4a4_ms * 1e-3) / 1e12}}
+    for name, (wc, wsc, fmt) in w13_mx.items():
+        ac, asc = Q.quads_mx_quantize(x, fmt)
+
+        def run():
+            return Q.quads_moe_mx_gemm((ac, asc), (wc, wsc), 2 * I, rows=rows, offsets=off,
+                                       row_token=rt, fmt=fmt, epilogue=Q.EPI_SWIGLU,
+                                       out_dtype=Q.OUT_BF16)
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 2.0 * rows * (2 * I) * x.shape[1]
+        out[name] = {"us": us, "TFLOP/s": flops / (us * 1e-6) / 1e12,
+                     "w4a4_rac_time_ratio": w4a4_ms * 1e3 / us}
     return out
 
 

@@ -59,6 +59,9 @@ typedef enum {
 
 typedef enum { QUADS_OUT_F32 = 0, QUADS_OUT_BF16 = 1 } quads_out_dtype;
 typedef enum { QUADS_EPI_NONE = 0, QUADS_EPI_SWIGLU = 1 } quads_epilogue;
+/* MX element formats (the comparator GEMM); the values are the block-scaled
+   MFMA's own format codes. */
+typedef enum { QUADS_MX_FP8 = 0, QUADS_MX_FP4 = 4 } quads_mx_format;
 
 /* Human-readable text for a status code (thread-local detail for QUADS_EHIP). */
 const char* quads_status_string(int status);
@@ -175,6 +178,40 @@ int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale, const floa
  */
 int quads_moe_combine(const void* y, int y_dtype, const int32_t* pos, const float* topk_w,
                       int64_t T, int32_t topk, int64_t N, float* out, void* stream);
+
+/*
+ * MX block-scaled comparator (the FP8 W8A8 baseline of section 4.4.2 and
+ * Fig. 9(a), with the fine-grained block scaling of section 2.2's "FP8"
+ * paragraph in the form gfx950's block-scaled MFMA takes).  Not part of the
+ * NVFP4 method: it exists so the method's GEMM can be measured against FP8
+ * on the same hardware.
+ *
+ * MX quantization of bf16 x [M, K] (K % 32 == 0), per row, blocks of 32:
+ * E = floor(log2 max|x|) - emax (emax 8 for FP8 E4M3, 2 for FP4 E2M1),
+ * clamped to [-127, 127], -127 for an all-zero block; scale byte E + 127;
+ * element = RNE(x / 2^E) on the element grid, saturated (448 / 6), sign of
+ * x kept.
+ *   fmt     QUADS_MX_FP8: codes uint8 [M, K] (OCP E4M3FN bytes);
+ *           QUADS_MX_FP4: codes uint8 [M, K/2] (even element in the low nibble)
+ *   scales  uint8 [M, K/32]
+ */
+int quads_mx_quantize(const uint16_t* x, int64_t M, int64_t K, int fmt, uint8_t* codes,
+                      uint8_t* scales, void* stream);
+
+/*
+ * Grouped MX GEMM: Y[p, n] = sum_k a[row(p), k] w_e[n, k] with a and w the
+ * decoded MX values (products exact, fp32 accumulation in the MFMA).
+ *   a_codes, a_scale   quads_mx_quantize layout, [Ta, ...], [Ta, K/32]
+ *   row_token, rows, offsets, E, N, epilogue, out_dtype, out   as in
+ *              quads_moe_w4a4_gemm (same packed-row and output conventions)
+ *   w_codes, w_scale   [E, N, ...], [E, N, K/32]
+ *   fmt        QUADS_MX_FP8 or QUADS_MX_FP4 (both operands)
+ *   K % 128 == 0.  No workspace.
+ */
+int quads_moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scale, const int32_t* row_token,
+                      int64_t rows, int64_t K, const uint8_t* w_codes, const uint8_t* w_scale,
+                      const int32_t* offsets, int32_t E, int64_t N, int fmt, int epilogue,
+                      int out_dtype, void* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -18,11 +18,13 @@ __all__ = [
     "QuadsError", "lib", "library_path",
     "quads_nvfp4_quantize", "quads_rac_quantize", "quads_nvfp4_weight_qdq",
     "quads_moe_pack", "quads_moe_w4a4_gemm", "quads_moe_combine",
-    "EPI_NONE", "EPI_SWIGLU", "OUT_F32", "OUT_BF16",
+    "quads_mx_quantize", "quads_moe_mx_gemm",
+    "EPI_NONE", "EPI_SWIGLU", "OUT_F32", "OUT_BF16", "MX_FP8", "MX_FP4",
 ]
 
 EPI_NONE, EPI_SWIGLU = 0, 1
 OUT_F32, OUT_BF16 = 0, 1
+MX_FP8, MX_FP4 = 0, 4
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libquads.so")
@@ -50,6 +52,9 @@ _SIGNATURES = {
                                            _P, _P, _P, _P, _I32, _I64, ctypes.c_int,
                                            ctypes.c_int, _P, _P, _SZ, _P]),
     "quads_moe_combine": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _I64, _I32, _I64, _P, _P]),
+    "quads_mx_quantize": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P]),
+    "quads_moe_mx_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I32, _I64,
+                                         ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]),
 }
 
 
@@ -212,4 +217,40 @@ def quads_moe_combine(y, pos, topk_w, y_dtype=OUT_F32):
     _check("quads_moe_combine", lib().quads_moe_combine(
         _ptr(y), y_dtype, _ptr(pos), _ptr(topk_w.contiguous()), t, topk, n, _ptr(out),
         _stream(dev)))
+    return out
+
+
+def quads_mx_quantize(x, fmt=MX_FP8):
+    """MX quantization of bf16 x [..., K] (rows = the leading dims) ->
+    (codes uint8 [..., K] (FP8) or [..., K/2] (FP4), scales uint8 [..., K/32])."""
+    x = _bits16(x)
+    k = x.shape[-1]
+    m = x.numel() // k if k else 0
+    dev = x.device
+    cw = k if fmt == MX_FP8 else k // 2
+    codes = torch.empty(tuple(x.shape[:-1]) + (cw,), dtype=torch.uint8, device=dev)
+    scales = torch.empty(tuple(x.shape[:-1]) + (k // 32,), dtype=torch.uint8, device=dev)
+    _check("quads_mx_quantize", lib().quads_mx_quantize(
+        _ptr(x), m, k, fmt, _ptr(codes), _ptr(scales), _stream(dev)))
+    return codes, scales
+
+
+def quads_moe_mx_gemm(a, w, n, rows=None, offsets=None, row_token=None, fmt=MX_FP8,
+                      epilogue=EPI_NONE, out_dtype=OUT_F32, out=None):
+    """Grouped MX GEMM.  a = (codes, scales) [Ta, ...]; w = (codes [E, N, ...],
+    scales [E, N, K/32]).  Returns out [rows, N] (or [rows, N/2] for SwiGLU)."""
+    a_codes, a_scale = a
+    w_codes, w_scale = w
+    e = w_codes.shape[0]
+    kd = a_scale.shape[-1] * 32
+    if rows is None:
+        rows = row_token.shape[0] if row_token is not None else a_codes.shape[0]
+    dev = a_codes.device
+    ncols = n // 2 if epilogue == EPI_SWIGLU else n
+    if out is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.int16
+        out = torch.empty((rows, ncols), dtype=dt, device=dev)
+    _check("quads_moe_mx_gemm", lib().quads_moe_mx_gemm(
+        _ptr(a_codes), _ptr(a_scale), _ptr(row_token), rows, kd, _ptr(w_codes), _ptr(w_scale),
+        _ptr(offsets), e, n, fmt, epilogue, out_dtype, _ptr(out), _stream(dev)))
     return out

@@ -1,0 +1,213 @@
+// Pieces shared by the 256 x 256-tile grouped GEMM kernels (the NVFP4
+// W4A4 GEMM and the MX block-scaled comparator): the argument block, the
+// MoE tile lookup and the epilogue of a 256 x 256 output tile whose waves
+// each own 128 x 64 outputs as 4 x 2 transposed 32 x 32 MFMA blocks.
+#pragma once
+
+#include "common.h"
+
+namespace quads {
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct GemmArgs {
+    const uint8_t* a_nib; const uint8_t* a_scale; const float* a_ts;
+    const int32_t* row_token; int64_t rows; int K;
+    const uint8_t* r_nib; const uint8_t* r_scale; const float* r_ts; const int32_t* sel; int k;
+    const uint8_t* w_nib; const uint8_t* w_scale; const float* w_ts;
+    const int32_t* offsets; int E; int N;
+    int epilogue; int out_bf16; void* out;
+};
+
+namespace v2 {
+
+constexpr int kXcds = 8;                // XCDs of an MI355X (work-group ids dealt round-robin)
+
+// Two fp32 values to packed bf16 (round to nearest even, hardware convert).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+    const bf16x2_t v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Tile `tile` of the M-tile list, found by each wave on its own (no LDS, no
+// barrier).  An expert with n rows gets t = ceil(n / bm) tiles, its rows split
+// evenly over them in 32-row multiples (a 280-row expert gets 160 + 120 rows
+// rather than 256 + 24, so neither tile is a near-empty one).  The list is
+// ordered by tile height, tallest first (experts in index order within a
+// height): the hardware hands each next work-group to the first free CU, so
+// the short tiles, dispatched last, fill in the tail (longest-first list
+// scheduling).  Lane l looks after experts l*per .. l*per + per - 1; for each
+// height a wave scan gives the first tile of each lane's share, and the
+// owning lane broadcasts the result.
+__device__ __forceinline__ int tile_height(int n, int bm, int* t_out) {
+    const int t = (n + bm - 1) / bm;
+    *t_out = t;
+    return t > 0 ? ((n + t - 1) / t + 31) / 32 : 0;          // in 32-row blocks
+}
+
+__device__ __forceinline__ int wave_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+template <int BMT>
+__device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
+                               int* m0_out, int* mend_out) {
+    constexpr int kH = BMT / 32;                  // tile heights 1 .. kH blocks
+    if (offsets == nullptr) {
+        const int64_t m0 = (int64_t)tile * BMT;
+        *e_out = 0;
+        *m0_out = (int)m0;
+        *mend_out = (int)rows;
+        return m0 < rows;
+    }
+    const int lane = threadIdx.x & 63;
+    const int per = (E + 63) / 64;
+    const int e0 = lane * per;
+    const int e1 = e0 + per < E ? e0 + per : E;
+    int cnt[kH];                                  // this lane's tiles of each height
+#pragma unroll
+    for (int q = 0; q < kH; ++q) cnt[q] = 0;
+    for (int e = e0; e < e1; ++e) {
+        int t;
+        const int hgt = tile_height(offsets[e + 1] - offsets[e], BMT, &t);
+#pragma unroll
+        for (int q = 0; q < kH; ++q) cnt[q] += hgt == q + 1 ? t : 0;
+    }
+    int all = 0;
+#pragma unroll
+    for (int q = 0; q < kH; ++q) all += cnt[q];
+    // work-groups past the last tile leave after one scan
+    if (tile >= __builtin_amdgcn_readlane(wave_scan(all, lane), 63)) return false;
+    int base = 0;                                 // tiles of the taller heights
+#pragma unroll
+    for (int q = kH - 1; q >= 0; --q) {
+        const int hgt = q + 1;
+        const int x = wave_scan(cnt[q], lane);
+        const int total = __builtin_amdgcn_readlane(x, 63);       // uniform: scalar branches
+        if (tile < base + total) {
+            int run = base + x - cnt[q], fe = -1, fm0 = 0, fme = 0;
+            if (tile >= run && tile < run + cnt[q]) {
+                for (int e = e0; e < e1; ++e) {
+                    const int n = offsets[e + 1] - offsets[e];
+                    int t;
+                    if (tile_height(n, BMT, &t) != hgt) continue;
+                    if (tile < run + t) {
+                        fe = e;
+                        fm0 = offsets[e] + (tile - run) * hgt * 32;
+                        fme = fm0 + hgt * 32 < offsets[e + 1] ? fm0 + hgt * 32 : offsets[e + 1];
+                        break;
+                    }
+                    run += t;
+                }
+            }
+            const int src = __ffsll(__ballot(fe >= 0)) - 1;
+            *e_out = __builtin_amdgcn_readlane(fe, src);
+            *m0_out = __builtin_amdgcn_readlane(fm0, src);
+            *mend_out = __builtin_amdgcn_readlane(fme, src);
+            return true;
+        }
+        base += total;
+    }
+    return false;
+}
+
+// Epilogue of a 256 x 256 tile: acc scaled by ca; SwiGLU to bf16 or plain
+// fp32 / bf16 stores, four consecutive features per lane.
+template <int kEpi>
+__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][2], float ca,
+                                         int m0, int mend, int f0, int wm, int wn, int mact,
+                                         int lane) {
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int prow_l = m0 + wm * 128 + (lane & 31);
+    const int nq = 4 * (lane >> 5);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= mact) continue;
+        const int prow = prow_l + mi * 32;
+        if (prow >= mend) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
+            if (swiglu) {
+                const int feat = f0 + wn * 32 + 8 * q + nq;      // features feat .. feat + 3
+                float hv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const float gt = acc[mi][0][4 * q + u] * ca;
+                    const float up = acc[mi][1][4 * q + u] * ca;
+                    // silu(g) u with the hardware exp2 and reciprocal: relative
+                    // error a few 1e-6, far inside half a bf16 ulp (2^-9)
+                    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+                    hv[u] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+                }
+                const uint32_t p01 = pk_bf16(hv[0], hv[1]), p23 = pk_bf16(hv[2], hv[3]);
+                const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+                const int nh = g.N / 2;
+                uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
+                if (feat + 3 < nh && (nh & 3) == 0) {
+                    *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                }
+            } else {
+#pragma unroll
+                for (int nj = 0; nj < 2; ++nj) {
+                    const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
+                    float y[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca;
+                    const int64_t o = (int64_t)prow * g.N + n;
+                    const bool vec = n + 3 < g.N && (g.N & 3) == 0;
+                    if (g.out_bf16) {
+                        uint16_t* ob = (uint16_t*)g.out + o;
+                        const uint32_t p01 = pk_bf16(y[0], y[1]), p23 = pk_bf16(y[2], y[3]);
+                        if (vec) {
+                            *reinterpret_cast<uint2*>(ob) = make_uint2(p01, p23);
+                        } else {
+                            const uint32_t b4[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu,
+                                                    p23 >> 16};
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) ob[u] = (uint16_t)b4[u];
+                        }
+                    } else {
+                        float* of = (float*)g.out + o;
+                        if (vec) {
+                            *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
+                        } else {
+#pragma unroll
+                            for (int u = 0; u < 4; ++u)
+                                if (n + u < g.N) of[u] = y[u];
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+
+// Weight row of B-tile row r.  Plain: f0 + r.  SwiGLU: the tile holds 128
+// output features; in each wave's 64 rows, rows 0-31 are gate and 32-63 up
+// for the same 32 features.
+__device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool* valid) {
+    if (!swiglu) {
+        const int n = f0 + r;
+        *valid = n < N;
+        return n;
+    }
+    const int feat = f0 + (r >> 6) * 32 + (r & 31);
+    *valid = feat < N / 2;
+    return ((r >> 5) & 1) * (N / 2) + feat;
+}
+
+}  // namespace v2
+
+}  // namespace quads

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 13
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 15
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -110,3 +110,24 @@ def test_combine_validation():
     assert f(FAKE, 0, FAKE, FAKE, 4, 2, 12, FAKE, None) == -2     # N % 8
     assert f(FAKE, 5, FAKE, FAKE, 4, 2, 16, FAKE, None) == -1     # dtype
     assert f(None, 0, FAKE, FAKE, 4, 2, 16, FAKE, None) == -1
+
+
+def test_mx_validation():
+    lib = Q.lib()
+    q = lib.quads_mx_quantize
+    assert q(FAKE, 4, 48, 0, FAKE, FAKE, None) == -2              # K % 32
+    assert q(FAKE, 4, 64, 1, FAKE, FAKE, None) == -1              # format
+    assert q(FAKE, 4, 64, 4, MIS, FAKE, None) == -1
+    assert q(None, 0, 64, 0, None, None, None) == 0               # empty: no-op
+    g = lib.quads_moe_mx_gemm
+
+    def call(rows=64, k_dim=256, e=4, n=64, fmt=0, epi=0, odt=0, offsets=FAKE, out=FAKE):
+        return g(FAKE, FAKE, None, rows, k_dim, FAKE, FAKE, offsets, e, n, fmt, epi, odt, out,
+                 None)
+    assert call(k_dim=192) == -2                                  # K % 128
+    assert call(fmt=2) == -1
+    assert call(epi=1, odt=0) == -1
+    assert call(n=63, epi=1, odt=1) == -2
+    assert call(offsets=None) == -1
+    assert call(out=MIS) == -1
+    assert call(rows=0) == 0
