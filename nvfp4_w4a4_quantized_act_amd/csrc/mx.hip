@@ -139,14 +139,24 @@ __device__ __forceinline__ int lds_pos(int r, int c) {
     return FMT == kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
+// Direct HBM -> LDS loads (lane i's bytes land at LDS address m0 + i * size).
+// Written as inline assembly so that the compiler does not see an LDS write:
+// its conservative wait (every LDS read after such a load waits for it) would
+// make each stage wait for the next stage's prefetch.  The kernel waits for
+// its own loads explicitly (s_waitcnt vmcnt(0)) before each barrier.
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
-typedef const __attribute__((address_space(1))) void* glb_ptr_t;
 
-__device__ __forceinline__ void g2l16(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(void* l) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
 }
-__device__ __forceinline__ void g2l4(const void* g, void* l) {
-    __builtin_amdgcn_global_load_lds((glb_ptr_t)g, (lds_ptr_t)l, 4, 0, 0);
+// `l` is an LDS byte address (wave-uniform)
+__device__ __forceinline__ void g2l16(const void* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void g2l4(const void* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(l), "v"(g)
+                 : "memory", "m0");
 }
 
 struct MxArgs {
@@ -159,11 +169,12 @@ struct MxArgs {
 // operand per thread) and scale rows (one 4-byte load per thread: waves 0-3
 // take A rows 64 w .., waves 4-7 W rows).
 template <int FMT>
-__device__ __forceinline__ void load_stage(const MxArgs& g, uint8_t* buf, int s,
+__device__ __forceinline__ void load_stage(const MxArgs& g, uint32_t buf, int s,
                                            const int32_t a_row[], const int64_t w_row[],
                                            int64_t sc_row, bool sc_is_a) {
     using C = Cfg<FMT>;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t a_len = FMT == kFp8 ? g.K : g.K / 2;           // bytes per code row
 #pragma unroll
     for (int q = 0; q < C::kLoads; ++q) {
@@ -171,7 +182,7 @@ __device__ __forceinline__ void load_stage(const MxArgs& g, uint8_t* buf, int s,
         const int r = slot / C::kChunks, pos = slot % C::kChunks;
         const int c = lds_pos<FMT>(r, pos);                       // involution
         const int64_t off = (int64_t)s * C::kRowBytes + 16 * c;
-        uint8_t* dst_a = buf + (q * 8 + wave) * 64 * 16;
+        const uint32_t dst_a = buf + (q * 8 + wave) * 64 * 16;
         g2l16(g.a + (int64_t)a_row[q] * a_len + off, dst_a);
         g2l16(g.w + w_row[q] * a_len + off, dst_a + C::kTile);
     }
@@ -224,13 +235,14 @@ __device__ __forceinline__ void main_loop(const MxArgs& g, uint8_t* smem, const 
     using C = Cfg<FMT>;
     const int ns = g.K / BK;
     const int r = threadIdx.x & 31;
-    load_stage<FMT>(g, smem, 0, a_row, w_row, sc_row, sc_is_a);
+    const uint32_t smem_lds = lds_addr(smem);
+    load_stage<FMT>(g, smem_lds, 0, a_row, w_row, sc_row, sc_is_a);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
     for (int s = 0; s < ns; ++s) {
         uint8_t* cur = smem + (s & 1) * C::kStage;
         if (s + 1 < ns)
-            load_stage<FMT>(g, smem + ((s + 1) & 1) * C::kStage, s + 1, a_row, w_row, sc_row,
+            load_stage<FMT>(g, smem_lds + ((s + 1) & 1) * C::kStage, s + 1, a_row, w_row, sc_row,
                             sc_is_a);
         const uint32_t* sca = reinterpret_cast<const uint32_t*>(cur + 2 * C::kTile);
         uint32_t sa_w[4], sw_w[2];
