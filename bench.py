@@ -47,7 +47,7 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_gemm_gate_up_traffic.md")
 GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_quantized_act_amd", "csrc", f)
-                for f in ("gemm.hip", "common.h")]
+                for f in ("gemm.hip", "gemm_tiles.h", "common.h")]
 GEMM_KERNEL_KEY = "k_gemm_w4a4_v2<1>"     # the gate/up (SwiGLU) GEMM kernel
 
 
