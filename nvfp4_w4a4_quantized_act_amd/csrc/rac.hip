@@ -7,8 +7,10 @@
 //          fused multiply-add, staged in LDS, then per channel the in-order
 //          fp64 sum of r^2 over the chunk's 64 tokens and max |r|.
 //  levels  the 64-ary fixed-order tree over those per-tile partials, one
-//          launch per level, until one score per channel is left (Eq. (23)).
-//  select  one work-group: radix select of the k largest scores (Eq. (24)),
+//          launch per level, until at most 16 partial rows per channel are
+//          left (Eq. (23)); none when neither S nor the scores are wanted.
+//  select  one work-group: the tree's last level (at most 16 rows, summed in
+//          order), then radix select of the k largest scores (Eq. (24)),
 //          ties to the lower index, written ascending; the tensor scale of
 //          the gathered residual from the per-channel maxima, and its code
 //          table (exact compare path: the residual is fp32, not bf16).
@@ -21,6 +23,7 @@ namespace quads {
 
 constexpr int kTileRows = 64;          // == kScoreFanin: one level-0 group
 constexpr int kRacMaxK = 8192;         // channels handled by the select kernel
+constexpr int kSelectFold = 16;        // partial rows the select kernel sums itself
 
 // ------------------------------------------------------------------ pass 1 --
 // Tile: 64 tokens x 256 channels.  Thread t quantizes 4 blocks (tile rows
@@ -169,7 +172,8 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_tmp, int* tota
 }
 
 __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ score,
-                                                     const uint32_t* __restrict__ colmax, int K,
+                                                     const uint32_t* __restrict__ colmax,
+                                                     int nrows, int K,
                                                      int k, int32_t* __restrict__ sel,
                                                      float* __restrict__ r_ts,
                                                      double* __restrict__ score_out,
@@ -183,8 +187,11 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     __shared__ uint32_t s_amax[16];
     __shared__ float s_rts;
     const int tid = threadIdx.x;
+    // the last level of the fixed-order tree: nrows (<= kSelectFold) partial
+    // rows summed in order from +0
     for (int j = tid; j < K; j += 1024) {
-        const double v = score[j];
+        double v = 0.0;
+        for (int r = 0; r < nrows; ++r) v = v + score[(int64_t)r * K + j];
         s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
         if (score_out) score_out[j] = v;
     }
@@ -265,8 +272,10 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
             const unsigned long long key = s_key[j] & mask;
             if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) {
                 sel[o++] = j;
-                const uint32_t c = colmax[j];
-                am = c > am ? c : am;
+                for (int r = 0; r < nrows; ++r) {
+                    const uint32_t c = colmax[(int64_t)r * K + j];
+                    am = c > am ? c : am;
+                }
             }
         }
     }
@@ -416,11 +425,16 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
     hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)gx, (unsigned)ctiles), dim3(256), 0, s, x, M,
                        (int)K, ts, w.table, nib, scale, w.pa, w.ca);
     QUADS_CHECK_LAUNCH();
-    // fixed-order tree over the level-0 partials
+    if (k == 0 && score_out == nullptr) {          // neither S nor the scores are wanted
+        launch_fill_f32(r_ts, 1, 0.0f, s);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    // fixed-order tree over the level-0 partials (its last level runs in select)
     double* pin = w.pa; uint32_t* cin = w.ca;
     double* pout = w.pb; uint32_t* cout = w.cb;
     int64_t n = c0;
-    while (n > 1) {
+    while (n > kSelectFold) {
         const int64_t g = (n + kScoreFanin - 1) / kScoreFanin;
         hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((K + 255) / 256), (unsigned)g), dim3(256),
                            0, s, pin, cin, n, (int)K, pout, cout);
@@ -429,13 +443,8 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
         double* tp = pin; pin = pout; pout = tp;
         uint32_t* tc = cin; cin = cout; cout = tc;
     }
-    if (k == 0 && score_out == nullptr) {
-        launch_fill_f32(r_ts, 1, 0.0f, s);
-        QUADS_CHECK_LAUNCH();
-        return QUADS_OK;
-    }
-    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)K, (int)k, sel,
-                       r_ts, score_out, w.r_table);
+    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)n, (int)K, (int)k,
+                       sel, r_ts, score_out, w.r_table);
     QUADS_CHECK_LAUNCH();
     if (k > 0) {
         const int64_t nel = M * (int64_t)k;
