@@ -30,7 +30,9 @@ GEMM sources).  `cpu_baseline` times the NumPy oracle on a bounded sample of
 the same layer.  `comparator` times the same gate/up GEMM as an MX
 block-scaled GEMM with FP8 and with FP4 elements (quads_moe_mx_gemm), the
 FP8 W8A8 baseline the paper's speed claim is measured against, next to the
-W4A4+RAC GEMM.
+W4A4+RAC GEMM.  `decode` runs the same layer at the decode step (64 tokens,
+Zipf routing, most experts with 0-2 rows), where the GEMMs are bound by the
+active experts' weight bytes.
 
     python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -306,6 +308,7 @@ def main():
         ops[k]["hbm_frac"] = ops[k]["GB/s"] / PEAK_HBM_GBS
 
     quant = quantizer_rate(np, torch, Q, synth, dev)
+    decode = decode_layer(np, torch, Q, synth, dev, w13q, w2q)
     comparator = mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx,
                                per_op["gemm_gate_up_swiglu"], fl_gu)
 
@@ -344,6 +347,7 @@ def main():
         "ops": ops,
         "quantizer": quant,
         "comparator": comparator,
+        "decode": decode,
         "weight_qdq_ms": weight_qdq_ms,
     }
     print(json.dumps(line), flush=True)
@@ -402,6 +406,107 @@ def quantizer_rate(np, torch, Q, synth, dev, reps=20):
     out["device_copy"] = {"us": us, "GB/s": 4.0 * m * k / (us * 1e-6) / 1e9,
                           "hbm_frac": 4.0 * m * k / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
     return out
+
+
+def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
+    """The decode-step layer (64 tokens, Zipf(1.2) routing over the same 128
+    experts, hidden 2048, intermediate 768, top-8, RAC k = 64 at both GEMM
+    inputs): the same six library calls as the prefill step, here in the
+    few-rows-per-expert regime (512 packed rows, most experts with 0-2 rows).
+    The weights are the prefill layer's NVFP4 weights (same shapes and
+    distribution).  Reported: the layer time (back-to-back layers, no events
+    inside), the per-op times from a separate pass with events, and the two
+    GEMMs' rates as the bytes of the active experts' NVFP4 weights (0.5625 B
+    per weight) per second against the 8 TB/s HBM peak."""
+    d = synth.make(4, with_weights=False)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    ids = torch.from_numpy(d["topk_ids"]).to(dev)
+    tw = torch.from_numpy(d["topk_w"]).to(dev)
+    T, TOPK, KR = x.shape[0], ids.shape[1], d["rac_k"]
+    E, N13, H = w13q[0].shape[0], w13q[0].shape[1], w13q[0].shape[2] * 2
+    I = N13 // 2
+    rows = T * TOPK
+    keep = {}
+
+    def layer(evs=None):
+        def mark(i):
+            if evs is not None:
+                evs[i].record()
+        mark(0)
+        a = Q.quads_rac_quantize(x, KR)
+        mark(1)
+        off, rt, pos = Q.quads_moe_pack(ids, E)
+        mark(2)
+        h = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), w13q, N13, rows=rows,
+                                  r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"],
+                                  offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
+                                  out_dtype=Q.OUT_BF16)
+        mark(3)
+        b = Q.quads_rac_quantize(h, KR)
+        mark(4)
+        y2 = Q.quads_moe_w4a4_gemm((b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
+                                   r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"],
+                                   offsets=off, out_dtype=Q.OUT_BF16)
+        mark(5)
+        out = Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
+        mark(6)
+        keep.update(a=a, b=b, off=off, rt=rt)
+        return out
+
+    for _ in range(5):
+        layer()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        layer()
+    torch.cuda.synchronize()
+    layer_ms = (time.perf_counter() - t0) * 1e3 / reps
+    names = ["rac_gate_up", "pack", "gemm_gate_up_swiglu", "rac_down", "gemm_down", "combine"]
+    per_op = np.zeros(len(names))
+    n_ev = 10
+    for _ in range(n_ev):
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+        layer(evs)
+        torch.cuda.synchronize()
+        per_op += [evs[i].elapsed_time(evs[i + 1]) for i in range(len(names))]
+    per_op /= n_ev
+    a, b, off, rt = keep["a"], keep["b"], keep["off"], keep["rt"]
+    counts = np.diff(off.cpu().numpy())
+    active = int((counts > 0).sum())
+    wb_gu = 0.5625 * active * N13 * H
+    wb_dn = 0.5625 * active * H * I
+    ops = {n: {"ms": float(v)} for n, v in zip(names, per_op)}
+    # each GEMM alone, back to back on the last layer's inputs (no event
+    # between launches): its rate on the active experts' weight bytes
+    gemms = {
+        "gemm_gate_up_swiglu": (wb_gu, lambda: Q.quads_moe_w4a4_gemm(
+            (a["nib"], a["scale"], a["ts"]), w13q, N13, rows=rows,
+            r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"], offsets=off, row_token=rt,
+            epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)),
+        "gemm_down": (wb_dn, lambda: Q.quads_moe_w4a4_gemm(
+            (b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
+            r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"], offsets=off,
+            out_dtype=Q.OUT_BF16)),
+    }
+    for n, (wb, fn) in gemms.items():
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / 20
+        gbs = wb / (us * 1e-6) / 1e9
+        ops[n].update({"alone_us": us, "weight_bytes": wb, "GB/s": gbs,
+                       "hbm_frac": gbs / PEAK_HBM_GBS})
+    return {"workload": "moe_decode_e128_h2048_i768_top8_t64_zipf1.2_rac64", "tokens": T,
+            "packed_rows": rows, "active_experts": active,
+            "max_rows_per_expert": int(counts.max()), "layer_ms": layer_ms,
+            "tokens_per_s": T / (layer_ms * 1e-3), "ops": ops,
+            "note": "per-op ms carry an event record each (a few microseconds of idle GPU); "
+                    "layer_ms has none; the GEMM rates use alone_us (20 back-to-back calls)"}
 
 
 def mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx, w4a4_ms, w4a4_flops, reps=20):

@@ -39,7 +39,8 @@ constexpr int kGemmMaxE = 4096;
 // tiles of kBM; tiles are numbered expert by expert.  Returns false (for the
 // whole work-group) when `tile` is past the last tile.
 __device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int tile, int bm,
-                             int* s_scan, int* s_res, int* e_out, int* m0_out, int* mend_out) {
+                             int* s_scan, int* s_res, int* e_out, int* m0_out, int* mend_out,
+                             int skip) {
     if (offsets == nullptr) {                      // one expert, all rows
         const int64_t m0 = (int64_t)tile * bm;
         *e_out = 0;
@@ -52,7 +53,7 @@ __device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int ti
     const int e0 = threadIdx.x * per;
     const int e1 = e0 + per < E ? e0 + per : E;
     int local = 0;
-    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+    for (int e = e0; e < e1; ++e) local += (v2::rows_of(offsets, e, skip) + bm - 1) / bm;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int x = local;
     for (int off = 1; off < 64; off <<= 1) {
@@ -66,7 +67,7 @@ __device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int ti
     for (int i = 0; i < wid; ++i) base += s_scan[i];
     int run = x - local + base;
     for (int e = e0; e < e1; ++e) {
-        const int t = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+        const int t = (v2::rows_of(offsets, e, skip) + bm - 1) / bm;
         if (tile >= run && tile < run + t) {     // exactly one thread matches
             s_res[0] = e;
             s_res[1] = offsets[e] + (tile - run) * bm;
@@ -161,7 +162,8 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     __shared__ int s_scan[8];
     __shared__ int s_res[4];
     int e, m0, mend;
-    if (!find_tile_bm(g.offsets, g.E, g.rows, blockIdx.y, kBM, s_scan, s_res, &e, &m0, &mend))
+    if (!find_tile_bm(g.offsets, g.E, g.rows, blockIdx.y, kBM, s_scan, s_res, &e, &m0, &mend,
+                      g.dec_rows))
         return;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
@@ -568,7 +570,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     const int tile = (slot / grp) * (kXcds * grp) + (h % kXcds) * grp + slot % grp;
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
-    if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend)) return;
+    if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows)) return;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -682,12 +684,23 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
     if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
-               out_dtype == QUADS_OUT_BF16, out};
+               out_dtype == QUADS_OUT_BF16, out, 0};
     hipStream_t st = (hipStream_t)stream;
+    if (gemm_decode_fits(g)) {
+        // few rows per expert: the decode kernel takes every expert with at
+        // most kDecodeMaxRows rows; when some expert may have more (rows >
+        // kDecodeMaxRows), the tiled kernel below takes those
+        g.dec_rows = kDecodeMaxRows;
+        const int rc = launch_gemm_decode(g, st);
+        if (rc != QUADS_OK || rows <= kDecodeMaxRows) return rc;
+    }
     if (K % v2::BK == 0 && k % v2::BK == 0) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
                                                           : (N + v2::BN - 1) / v2::BN;
-        const int64_t nt_m = (rows + v2::BM - 1) / v2::BM + (offsets ? E : 0);
+        // M-tiles: at most rows / BM + one partial tile per expert that has
+        // tiles (with a decode share, only experts above g.dec_rows rows)
+        const int64_t big = g.dec_rows > 0 ? rows / (g.dec_rows + 1) : E;
+        const int64_t nt_m = (rows + v2::BM - 1) / v2::BM + (offsets ? (big < E ? big : E) : 0);
         const int64_t grp = 2 * nt_n;
         const int64_t span = grp * v2::kXcds;
         const dim3 grid2((unsigned)((nt_m * nt_n + span - 1) / span * span));
@@ -702,7 +715,8 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
     }
     const int64_t ntiles_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + kBN / 2 - 1) / (kBN / 2)
                                                           : (N + kBN - 1) / kBN;
-    int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? E : 0);
+    const int64_t big = g.dec_rows > 0 ? rows / (g.dec_rows + 1) : E;
+    int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? (big < E ? big : E) : 0);
     const dim3 grid((unsigned)ntiles_n, (unsigned)ntiles_m);
     if (epilogue == QUADS_EPI_SWIGLU)
         hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_SWIGLU>, grid, dim3(256), 0, st, g);

@@ -1,0 +1,377 @@
+// Grouped W4A4 GEMM for experts with few rows (the decode step): the same
+// product as the tiled kernels in gemm.hip -- arXiv 2607.15810, Eq. (6) on
+// the compensated activation of Eq. (21) -- laid out for the regime where an
+// expert holds a handful of token rows and the weight stream is the cost.
+//
+// A 256-row tile with four rows in it spends its MFMA work on empty rows and
+// converts and stages a full weight tile through LDS per K step.  Here a
+// work-group of two waves owns one expert and a 128-row slab of its weight
+// matrix (SwiGLU: per wave 32 gate rows and the 32 matching up rows, so the
+// epilogue pairs them in registers) and streams it from HBM once per 32 token
+// rows of the expert (later passes find it in L2); a work-group of an expert
+// without rows leaves at once, so only active experts' weights are read.  An
+// expert with more than kDecodeMaxRows rows is left to the tiled kernel, which
+// the caller launches after this one (gemm.hip).
+//
+// Streaming.  A lane (row r = lane % 32, half h = lane / 32) of a wave holds,
+// per 128-deep chunk of K, codes 64h .. 64h + 63 of one weight row in each of
+// the wave's two 32-row blocks and of one token row, with the block scales
+// that cover them.  The loads go straight to registers in that layout, three
+// chunks ahead of the MFMAs (a ring of three buffers, unrolled so the buffer of
+// each chunk is fixed and the compiler's waits are plain counts).  A chunk is
+// converted exactly to fp16 (hardware fp4 -> fp16 convert, then a packed
+// multiply by the E4M3 block scale; every v * s_b is an fp16 number) and fed
+// to 32x32x16 fp16 MFMAs, weights as the first operand.  MFMA step j of a
+// chunk contracts codes 8j .. 8j + 7 of each half, channels k0 + 8j + u and
+// k0 + 64 + 8j + u: both operands take the same channels in the same slots,
+// so the MFMAs sum exactly the products of Eq. (6).
+//
+// Compensation.  The weight columns W[n, sel[i]] are taken from the chunks as
+// they stream by (sel ascending: chunk c holds the selected channels in
+// [128c, 128c + 128), a uniform range), converted to fp16 and parked in LDS,
+// row by row; after the main loop they are the first MFMA operand against the
+// residual codes R (second pass of Eq. (21)), in registers of their own since
+// the tensor scale differs:
+//   Y = acc * s_tA s_tW[e] + accc * s_tR s_tW[e].
+#include "common.h"
+#include "gemm_tiles.h"
+
+namespace quads {
+namespace dec {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWaves = 2;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kChunk = 128;          // channels per chunk: 64 codes per lane
+constexpr int kRows = 32;            // token rows per pass (one MFMA operand)
+constexpr int kRing = 3;             // chunks in flight per wave
+constexpr int kCapMax = 64;          // compensation channels kept in LDS
+constexpr int kCapLd = kCapMax + 8;  // halfs per LDS row (conflict-free 16-byte reads)
+
+// One lane's share of a chunk of one row: codes 64h .. 64h + 63 and the E4M3
+// scales of blocks 4h .. 4h + 3.
+struct Piece {
+    uint4 lo, hi;
+    uint32_t sc;
+};
+
+// Rows are addressed as a uniform base plus a 32-bit byte offset per lane.
+// The loads are unconditional: a lane without a row reads a valid row and its
+// values are zeroed at conversion time through a zero block scale (v * 0 = 0
+// for every code), so no branch makes the compiler drain the loads in flight.
+__device__ __forceinline__ Piece load_piece(const uint8_t* nib, const uint8_t* sc,
+                                            uint32_t nib_off, uint32_t sc_off) {
+    const uint4* q = reinterpret_cast<const uint4*>(nib + nib_off);
+    Piece p;
+    p.lo = q[0];
+    p.hi = q[1];
+    p.sc = *reinterpret_cast<const uint32_t*>(sc + sc_off);
+    return p;
+}
+
+__device__ __forceinline__ uint32_t word(const Piece& p, int j) {
+    const uint4 v = j < 4 ? p.lo : p.hi;
+    const int i = j & 3;
+    return i == 0 ? v.x : (i == 1 ? v.y : (i == 2 ? v.z : v.w));
+}
+
+// 8 codes (one dword) times an fp16 block scale -> 8 exact fp16 values.
+__device__ __forceinline__ f16x8 cvt8(uint32_t w, _Float16 s) {
+    const f16x2 s2 = {s, s};
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// The four block scales of a piece as fp16 (E4M3 -> fp16 is exact).
+__device__ __forceinline__ void scales4(uint32_t sc, _Float16 s[4]) {
+    const f16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, false);
+    const f16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc, 1.0f, true);
+    s[0] = lo[0]; s[1] = lo[1]; s[2] = hi[0]; s[3] = hi[1];
+}
+
+// The 8 MFMA steps of one chunk: both weight row blocks against the rows (a
+// piece whose row does not exist converts with zero scales).
+__device__ __forceinline__ void chunk_mma(const Piece& w0, const Piece& w1, const Piece& a,
+                                          const bool wv[2], bool av, f32x16 acc[2]) {
+    _Float16 sw0[4], sw1[4], sa[4];
+    scales4(wv[0] ? w0.sc : 0u, sw0);
+    scales4(wv[1] ? w1.sc : 0u, sw1);
+    scales4(av ? a.sc : 0u, sa);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        // convert one step at a time: the empty asm pins the step's codes
+        // here, so the conversions of all eight steps are not hoisted ahead
+        // (about 70 registers); the MFMAs still overlap the next conversions
+        uint32_t xa = word(a, j), x0 = word(w0, j), x1 = word(w1, j);
+        asm volatile("" : "+v"(xa), "+v"(x0), "+v"(x1));
+        const f16x8 af = cvt8(xa, sa[j >> 1]);
+        const f16x8 f0 = cvt8(x0, sw0[j >> 1]);
+        const f16x8 f1 = cvt8(x1, sw1[j >> 1]);
+        acc[0] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f0, af, acc[0], 0, 0, 0);
+        acc[1] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f1, af, acc[1], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ float silu_mul(float gt, float up) {
+    // silu(g) u with the hardware exp2 and reciprocal, as in the tiled kernel
+    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
+    return gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+}
+
+// Grid: E x slabs work-groups, block b = slab * E + e (consecutive blocks go
+// to different XCDs and experts; with E a multiple of 8, all slabs of an
+// expert share one XCD's L2, where its activation rows stay).
+template <int kEpi>
+__global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    // compensation weight columns, per wave and row block: [row][channel]
+    __shared__ __align__(16) _Float16 capt[kWaves][2][32][kCapLd];
+    // a chunk's weight pieces, word-major, while its compensation columns are taken
+    __shared__ uint32_t stage[kWaves][2][9][64];
+
+    const int e = (int)(blockIdx.x % (unsigned)g.E);
+    const int slab = (int)(blockIdx.x / (unsigned)g.E);
+    int p0 = 0, cnt = (int)g.rows;
+    if (g.offsets) {
+        p0 = g.offsets[e];
+        cnt = g.offsets[e + 1] - p0;
+    }
+    if (cnt <= 0 || cnt > g.dec_rows) return;        // uniform: no rows (no weight reads),
+                                                      // or the tiled kernel's expert
+
+    // the wave index as a scalar, so that every branch on it is uniform
+    const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int r = lane & 31, h = lane >> 5;
+    const uint32_t kn = (uint32_t)g.K / 2, ks = (uint32_t)g.K / kBlock;
+
+    // the expert's weights (uniform base) and the lane's rows in the wave's
+    // two 32-row blocks
+    const uint8_t* wnib = g.w_nib + (int64_t)e * g.N * kn;
+    const uint8_t* wsc = g.w_scale + (int64_t)e * g.N * ks;
+    uint32_t wrow_n[2], wrow_s[2];
+    bool wv[2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        int row;
+        if (swiglu) {
+            const int feat = slab * 64 + wave * 32 + r;
+            wv[q] = feat < g.N / 2;
+            row = q * (g.N / 2) + feat;
+        } else {
+            row = slab * 128 + wave * 64 + 32 * q + r;
+            wv[q] = row < g.N;
+        }
+        row = wv[q] ? row : 0;
+        wrow_n[q] = (uint32_t)row * kn + 32 * h;
+        wrow_s[q] = (uint32_t)row * ks + 4 * h;
+    }
+
+    const int nch = g.K / kChunk;
+    const int ncs = g.k / kBlock;                     // compensation steps of 16
+    const float s_tw = g.w_ts[e];
+    const float ca = g.a_ts[0] * s_tw;
+    const float cr = g.k > 0 ? g.r_ts[0] * s_tw : 0.0f;
+
+    // the selected channels, one per lane, read back one at a time as scalars
+    int sel_lo = 0;
+    if (g.k > 0) {                                    // a column never captured reads as 0
+        for (int i = lane; i < 2 * 32 * kCapLd / 8; i += 64)
+            reinterpret_cast<uint4*>(&capt[wave][0][0][0])[i] = make_uint4(0, 0, 0, 0);
+        sel_lo = lane < g.k ? g.sel[lane] : 0;
+    }
+
+    for (int c0 = 0; c0 < cnt; c0 += kRows) {
+        const bool rv = c0 + r < cnt;
+        const int p = p0 + c0 + r;
+        f32x16 acc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
+
+        // The ring: chunk c lives in slot c % 3 (three named slots, no array,
+        // so everything stays in registers); loads past the last chunk repeat
+        // it (no branch) and are never used.  The first weight chunks are
+        // requested before the token rows, whose addresses wait for
+        // row_token: the weight stream starts one memory latency earlier.
+        auto ldw = [&](Piece& w0, Piece& w1, int c) {
+            const uint32_t cl = (uint32_t)(c < nch ? c : nch - 1);
+            w0 = load_piece(wnib, wsc, wrow_n[0] + 64 * cl, wrow_s[0] + 8 * cl);
+            w1 = load_piece(wnib, wsc, wrow_n[1] + 64 * cl, wrow_s[1] + 8 * cl);
+        };
+        Piece w0a, w1a, aa, w0b, w1b, ab, w0c, w1c, ac;
+        ldw(w0a, w1a, 0);
+        ldw(w0b, w1b, 1);
+        ldw(w0c, w1c, 2);
+        const int64_t src = rv ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
+        // the token row: a per-lane base (the activation tensor may exceed 4 GB)
+        const uint8_t* an = g.a_nib + src * kn + 32 * h;
+        const uint8_t* as = g.a_scale + src * ks + 4 * h;
+        auto lda = [&](Piece& a, int c) {
+            const uint32_t cl = (uint32_t)(c < nch ? c : nch - 1);
+            a = load_piece(an, as, 64 * cl, 8 * cl);
+        };
+        lda(aa, 0);
+        lda(ab, 1);
+        lda(ac, 2);
+        int ci = 0;                                   // next compensation channel to capture
+        auto step = [&](Piece& w0, Piece& w1, Piece& a, int c) {
+            if (c < nch) {
+                if (c0 == 0 && ci < g.k &&
+                    __builtin_amdgcn_readlane(sel_lo, ci) < kChunk * (c + 1)) {
+                    // capture W[:, sel[i]] for the selected channels in this
+                    // chunk: channel j of the chunk is code j % 64 of half
+                    // j / 64, in dword (j % 64) / 8.  The pieces go to LDS
+                    // word-major, so a uniform word index is one LDS read.
+#pragma unroll
+                    for (int d = 0; d < 8; ++d) {
+                        stage[wave][0][d][lane] = word(w0, d);
+                        stage[wave][1][d][lane] = word(w1, d);
+                    }
+                    stage[wave][0][8][lane] = wv[0] ? w0.sc : 0u;
+                    stage[wave][1][8][lane] = wv[1] ? w1.sc : 0u;
+                    // channels ci .. cend - 1 lie in this chunk (sel ascending)
+                    const int cend = __popcll(__ballot(lane < g.k && sel_lo < kChunk * (c + 1)));
+#pragma unroll 4
+                    for (; ci < cend; ++ci) {
+                        const int j = __builtin_amdgcn_readlane(sel_lo, ci) - kChunk * c;
+                        if (j < 0 || j >= kChunk) continue;   // not ascending: skipped (reads 0)
+                        const int hh = j >> 6, jj = j & 63, sh = 4 * (jj & 7), sb = 8 * (jj >> 4);
+                        const uint32_t y0 = stage[wave][0][jj >> 3][lane];
+                        const uint32_t y1 = stage[wave][1][jj >> 3][lane];
+                        const uint32_t b0 = (stage[wave][0][8][lane] >> sb) & 0xFFu;
+                        const uint32_t b1 = (stage[wave][1][8][lane] >> sb) & 0xFFu;
+                        const _Float16 v0 =
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((y0 >> sh) & 0xFu, 1.0f, 0)[0] *
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 1.0f, false)[0];
+                        const _Float16 v1 =
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((y1 >> sh) & 0xFu, 1.0f, 0)[0] *
+                            __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 1.0f, false)[0];
+                        if (h == hh) {
+                            capt[wave][0][r][ci] = v0;
+                            capt[wave][1][r][ci] = v1;
+                        }
+                    }
+                }
+                chunk_mma(w0, w1, a, wv, rv, acc);
+            }
+            ldw(w0, w1, c + kRing);
+            lda(a, c + kRing);
+        };
+        for (int cb = 0; cb < nch; cb += kRing) {
+            step(w0a, w1a, aa, cb);
+            step(w0b, w1b, ab, cb + 1);
+            step(w0c, w1c, ac, cb + 2);
+        }
+
+        // compensation: captured columns against this pass's residual rows
+        f32x16 accc[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) accc[q][v] = 0.0f;
+        for (int t = 0; t < ncs; ++t) {
+            const uint32_t rw = *reinterpret_cast<const uint32_t*>(
+                g.r_nib + src * (g.k / 2) + 8 * t + 4 * h);
+            const uint32_t rs = g.r_scale[src * ncs + t];
+            const f16x8 rf = cvt8(rv ? rw : 0u, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                    rv ? rs : 0u, 1.0f, false)[0]);
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const f16x8 wf = *reinterpret_cast<const f16x8*>(&capt[wave][q][r][16 * t + 8 * h]);
+                accc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, rf, accc[q], 0, 0, 0);
+            }
+        }
+
+        // epilogue: lane holds output row c0 + r; registers 4g .. 4g + 3 are
+        // features 8g + 4h .. 8g + 4h + 3 of each 32-row block
+        if (rv) {
+            const int nq = 4 * h;
+#pragma unroll
+            for (int grp = 0; grp < 4; ++grp) {
+                float y[2][4];
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        y[q][u] = acc[q][4 * grp + u] * ca + accc[q][4 * grp + u] * cr;
+                if (swiglu) {
+                    const int nh = g.N / 2;
+                    const int feat = slab * 64 + wave * 32 + 8 * grp + nq;
+                    const uint32_t p01 = v2::pk_bf16(silu_mul(y[0][0], y[1][0]),
+                                                     silu_mul(y[0][1], y[1][1]));
+                    const uint32_t p23 = v2::pk_bf16(silu_mul(y[0][2], y[1][2]),
+                                                     silu_mul(y[0][3], y[1][3]));
+                    uint16_t* o = (uint16_t*)g.out + (int64_t)p * nh + feat;
+                    if (feat + 3 < nh && (nh & 3) == 0) {
+                        *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                    } else {
+                        const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu,
+                                                p23 >> 16};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                    }
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        const int n = slab * 128 + wave * 64 + 32 * q + 8 * grp + nq;
+                        const int64_t o = (int64_t)p * g.N + n;
+                        const bool vec = n + 3 < g.N && (g.N & 3) == 0;
+                        if (g.out_bf16) {
+                            uint16_t* ob = (uint16_t*)g.out + o;
+                            const uint32_t p01 = v2::pk_bf16(y[q][0], y[q][1]);
+                            const uint32_t p23 = v2::pk_bf16(y[q][2], y[q][3]);
+                            if (vec) {
+                                *reinterpret_cast<uint2*>(ob) = make_uint2(p01, p23);
+                            } else {
+                                const uint32_t b4[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu,
+                                                        p23 >> 16};
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    if (n + u < g.N) ob[u] = (uint16_t)b4[u];
+                            }
+                        } else {
+                            float* of = (float*)g.out + o;
+                            if (vec) {
+                                *reinterpret_cast<float4*>(of) =
+                                    make_float4(y[q][0], y[q][1], y[q][2], y[q][3]);
+                            } else {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    if (n + u < g.N) of[u] = y[q][u];
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+}  // namespace dec
+
+bool gemm_decode_fits(const GemmArgs& g) {
+    const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
+    return g.K % dec::kChunk == 0 && g.k <= dec::kCapMax &&
+           g.rows <= (int64_t)kDecodeRowsPerExpert * g.E && slabs * g.E < ((int64_t)1 << 31) &&
+           (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+}
+
+int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
+    const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
+    const dim3 grid((unsigned)(slabs * g.E)), block(dec::kThreads);
+    if (g.epilogue == QUADS_EPI_SWIGLU)
+        hipLaunchKernelGGL(dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU>, grid, block, 0, st, g);
+    else
+        hipLaunchKernelGGL(dec::k_gemm_w4a4_decode<QUADS_EPI_NONE>, grid, block, 0, st, g);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+}  // namespace quads

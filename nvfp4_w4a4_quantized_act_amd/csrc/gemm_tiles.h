@@ -17,6 +17,10 @@ struct GemmArgs {
     const uint8_t* w_nib; const uint8_t* w_scale; const float* w_ts;
     const int32_t* offsets; int E; int N;
     int epilogue; int out_bf16; void* out;
+    // Experts with at most this many rows belong to the decode kernel
+    // (gemm_decode.hip); the tiled kernels skip them.  0: the tiled kernel
+    // takes every expert.
+    int dec_rows;
 };
 
 namespace v2 {
@@ -55,9 +59,15 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
     return x;
 }
 
+// Experts with at most `skip` rows get no tiles (another kernel takes them).
+__device__ __forceinline__ int rows_of(const int32_t* offsets, int e, int skip) {
+    const int n = offsets[e + 1] - offsets[e];
+    return n > skip ? n : 0;
+}
+
 template <int BMT>
 __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
-                               int* m0_out, int* mend_out) {
+                               int* m0_out, int* mend_out, int skip = 0) {
     constexpr int kH = BMT / 32;                  // tile heights 1 .. kH blocks
     if (offsets == nullptr) {
         const int64_t m0 = (int64_t)tile * BMT;
@@ -75,7 +85,7 @@ __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int 
     for (int q = 0; q < kH; ++q) cnt[q] = 0;
     for (int e = e0; e < e1; ++e) {
         int t;
-        const int hgt = tile_height(offsets[e + 1] - offsets[e], BMT, &t);
+        const int hgt = tile_height(rows_of(offsets, e, skip), BMT, &t);
 #pragma unroll
         for (int q = 0; q < kH; ++q) cnt[q] += hgt == q + 1 ? t : 0;
     }
@@ -94,7 +104,7 @@ __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int 
             int run = base + x - cnt[q], fe = -1, fm0 = 0, fme = 0;
             if (tile >= run && tile < run + cnt[q]) {
                 for (int e = e0; e < e1; ++e) {
-                    const int n = offsets[e + 1] - offsets[e];
+                    const int n = rows_of(offsets, e, skip);
                     int t;
                     if (tile_height(n, BMT, &t) != hgt) continue;
                     if (tile < run + t) {
@@ -209,5 +219,14 @@ __device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool*
 }
 
 }  // namespace v2
+
+// Grouped GEMM for experts with few rows (gemm_decode.hip): used when K is a
+// multiple of 128, k <= 64 and there are at most kDecodeRowsPerExpert packed
+// rows per expert on average; it takes the experts with at most
+// kDecodeMaxRows rows, the tiled kernel the others.
+constexpr int kDecodeRowsPerExpert = 32;
+constexpr int kDecodeMaxRows = 128;
+bool gemm_decode_fits(const GemmArgs& g);
+int launch_gemm_decode(const GemmArgs& g, hipStream_t st);
 
 }  // namespace quads
