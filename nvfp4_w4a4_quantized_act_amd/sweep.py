@@ -17,7 +17,14 @@ GPU through the library:
 
 Reported per k (0, 12.5, 25, 50, 75 and 100 % of K, rounded to 64 channels):
 relative Frobenius distances |Y(k) - Y_qat| / |Y_qat| and |Y(k) - Y_16| /
-|Y_16|, and the largest element error relative to max |Y_qat|.
+|Y_16|, and the largest element error relative to max |Y_qat| (and to
+max |Y_16|).
+
+Beside them, the approximate MX modes of gfx950's block-scaled MFMA (one
+power-of-two E8M0 scale per 32 elements instead of an E4M3 scale per 16; FP4
+E2M1 and FP8 E4M3 elements, both operands quantized by quads_mx_quantize, the
+product by quads_moe_mx_gemm): their distance to Y_16, the same product
+format-for-format, with no trainer-side reference of their own.
 
 Workloads: dense = X [4096, 4096] Student-t(3) with 41 outlier channels x20,
 W [4096, 4096] N(0, 0.02); moe = the gate/up GEMM of the MoE layer, X [4096,
@@ -54,7 +61,30 @@ def _errors(y, y_qat, y_16):
     d_qat = y - y_qat
     return dict(rel_qat=float(np.linalg.norm(d_qat) / np.linalg.norm(y_qat)),
                 rel_bf16=float(np.linalg.norm(y - y_16) / np.linalg.norm(y_16)),
-                max_qat=float(np.abs(d_qat).max() / np.abs(y_qat).max()))
+                max_qat=float(np.abs(d_qat).max() / np.abs(y_qat).max()),
+                max_bf16=float(np.abs(y - y_16).max() / np.abs(y_16).max()))
+
+
+def _mx_errors(y, y_16):
+    return dict(rel_qat=None, rel_bf16=float(np.linalg.norm(y - y_16) / np.linalg.norm(y_16)),
+                max_qat=None, max_bf16=float(np.abs(y - y_16).max() / np.abs(y_16).max()))
+
+
+def _mx_rows(Q, torch, x_t, w_t, n, rows, y_16, meta, offsets=None, row_token=None):
+    """Rows of the MX modes: x and w quantized to MX, the block-scaled GEMM
+    (fp32 out), its distance to the bf16 product."""
+    out = []
+    e, _, kdim = w_t.shape
+    for name, fmt in (("mxfp4", Q.MX_FP4), ("mxfp8", Q.MX_FP8)):
+        a = Q.quads_mx_quantize(x_t, fmt)
+        wc, wsc = Q.quads_mx_quantize(w_t.reshape(e * n, kdim), fmt)
+        y = Q.quads_moe_mx_gemm(a, (wc.view(e, n, -1), wsc.view(e, n, -1)), n, rows=rows,
+                                offsets=offsets, row_token=row_token, fmt=fmt,
+                                out_dtype=Q.OUT_F32)
+        torch.cuda.synchronize()
+        out.append(dict(meta, format=name, frac=0.0, k=0,
+                        **_mx_errors(y.cpu().numpy().astype(np.float64), y_16)))
+    return out
 
 
 def _gpu_gemm(Q, torch, x_t, k, wq, n, rows, offsets=None, row_token=None):
@@ -84,8 +114,9 @@ def sweep_dense(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
     for f in fractions:
         k = channels_for(f, kdim)
         y = _gpu_gemm(Q, torch, x_t, k, (nib, scale, ts), n, m)
-        out.append(dict(workload="dense", M=m, K=kdim, N=n, frac=f, k=k,
+        out.append(dict(workload="dense", M=m, K=kdim, N=n, format="nvfp4", frac=f, k=k,
                         **_errors(y, y_qat, y_16)))
+    out += _mx_rows(Q, torch, x_t, w_t, n, m, y_16, dict(workload="dense", M=m, K=kdim, N=n))
     return out
 
 
@@ -119,17 +150,23 @@ def sweep_moe(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
     for f in fractions:
         k = channels_for(f, kdim)
         y = _gpu_gemm(Q, torch, x_t, k, (nib, scale, ts), n, rows, off_t, rt_t)
-        out.append(dict(workload="moe_gate_up", T=t, E=e, K=kdim, N=n, rows=rows, frac=f, k=k,
-                        **_errors(y, y_qat, y_16)))
+        out.append(dict(workload="moe_gate_up", T=t, E=e, K=kdim, N=n, rows=rows, format="nvfp4",
+                        frac=f, k=k, **_errors(y, y_qat, y_16)))
+    out += _mx_rows(Q, torch, x_t, w_t, n, rows, y_16,
+                    dict(workload="moe_gate_up", T=t, E=e, K=kdim, N=n, rows=rows),
+                    offsets=off_t, row_token=rt_t)
     return out
 
 
 def table(rows):
-    lines = ["| workload | k / K | k | rel. Frobenius vs QAT ref. | rel. Frobenius vs bf16 | "
-             "max element vs QAT ref. |", "|---|---|---|---|---|---|"]
+    def f5(v):
+        return "—" if v is None else f"{v:.5f}"
+    lines = ["| workload | format | k / K | k | rel. Frobenius vs QAT ref. | rel. Frobenius vs bf16 | "
+             "max element vs QAT ref. | max element vs bf16 |", "|---|---|---|---|---|---|---|---|"]
     for r in rows:
-        lines.append(f"| {r['workload']} | {100 * r['frac']:.1f} % | {r['k']} | "
-                     f"{r['rel_qat']:.5f} | {r['rel_bf16']:.5f} | {r['max_qat']:.5f} |")
+        lines.append(f"| {r['workload']} | {r.get('format', 'nvfp4')} | {100 * r['frac']:.1f} % | "
+                     f"{r['k']} | {f5(r['rel_qat'])} | {f5(r['rel_bf16'])} | {f5(r['max_qat'])} | "
+                     f"{f5(r.get('max_bf16'))} |")
     return "\n".join(lines)
 
 

@@ -1,7 +1,8 @@
 """GPU accuracy sweep (QUADS section 4.3.3, Table 3; section 3.3, Fig. 4(b))
 at reduced sizes: the error figures the sweep reports from the library's RAC
 and GEMM equal the oracle's figures for the same inputs, for every k, and
-fall with k."""
+fall with k; the figures of the approximate MX modes (FP4 and FP8 elements,
+E8M0 per 32) equal the oracle's MX figures."""
 
 import numpy as np
 import pytest
@@ -11,6 +12,7 @@ import synth
 from nvfp4_w4a4_quantized_act_amd import sweep as S
 from oracle import formats as F
 from oracle import moe as OM
+from oracle import mx as OX
 from oracle import nvfp4 as ON
 from oracle import rac as OR
 
@@ -52,7 +54,45 @@ def _oracle_rows(x_bits, w_bits, offsets, row_token, kdim):
     return out
 
 
+def _oracle_mx(x_bits, w_bits, offsets, row_token):
+    """rel_bf16 and max_bf16 of the MX modes, with the oracle's MX quantizer
+    and GEMM (fp64)."""
+    x = F.bf16_to_f64(x_bits)
+    e, n, kdim = w_bits.shape
+    wf = F.bf16_to_f64(w_bits)
+    rows = int(offsets[-1])
+    xa = x[row_token] if row_token is not None else x
+    y_16 = np.empty((rows, n))
+    for j in range(e):
+        sl = slice(offsets[j], offsets[j + 1])
+        y_16[sl] = xa[sl] @ wf[j].T
+    out = {}
+    for fmt in ("fp4", "fp8"):
+        a = OX.quantize(x, fmt)
+        wc, wsc = OX.quantize(wf.reshape(e * n, kdim), fmt)
+        y, _ = OX.grouped_gemm(a, (wc.reshape(e, n, -1), wsc.reshape(e, n, -1)), offsets,
+                               row_token, fmt)
+        out["mx" + fmt] = (np.linalg.norm(y - y_16) / np.linalg.norm(y_16),
+                           np.abs(y - y_16).max() / np.abs(y_16).max())
+    return out
+
+
+def _compare_mx(got, exp):
+    rows = [g for g in got if g["format"] != "nvfp4"]
+    assert [g["format"] for g in rows] == ["mxfp4", "mxfp8"]
+    for g in rows:
+        rel, mx = exp[g["format"]]
+        assert abs(g["rel_bf16"] - rel) <= 1e-3 * rel + 1e-6, (g, rel)
+        assert abs(g["max_bf16"] - mx) <= 1e-3 * mx + 1e-6, (g, mx)
+    # the exact NVFP4 path without RAC, against the same bf16 product
+    nv = [g for g in got if g["format"] == "nvfp4" and g["k"] == 0][0]
+    print("rel. error vs bf16: nvfp4 %.5f, mxfp4 %.5f, mxfp8 %.5f"
+          % (nv["rel_bf16"], rows[0]["rel_bf16"], rows[1]["rel_bf16"]))
+
+
 def _compare(got, exp):
+    got = [g for g in got if g["format"] == "nvfp4"]
+    assert len(got) == len(exp)
     for g, e in zip(got, exp):
         for key in ("rel_qat", "rel_bf16", "max_qat"):
             assert abs(g[key] - e[key]) <= 2e-5 * max(1.0, e[key]), (g, e)
@@ -65,8 +105,9 @@ def test_sweep_dense_matches_oracle(Q):
     got = S.sweep_dense(Q, torch, synth, torch.device("cuda:0"), **DENSE)
     d = synth.make(2, **DENSE)
     exp = _oracle_rows(d["x"], d["w"], np.array([0, DENSE["m"]]), None, DENSE["k_dim"])
-    assert [g["k"] for g in got] == [0, 128, 256, 512, 768, 1024]
+    assert [g["k"] for g in got if g["format"] == "nvfp4"] == [0, 128, 256, 512, 768, 1024]
     _compare(got, exp)
+    _compare_mx(got, _oracle_mx(d["x"], d["w"], np.array([0, DENSE["m"]]), None))
 
 
 def test_sweep_moe_matches_oracle(Q):
@@ -77,3 +118,4 @@ def test_sweep_moe_matches_oracle(Q):
     exp = _oracle_rows(d["x"], d["w13"], off, rt, MOE["h"])
     assert got[0]["rows"] == MOE["t"] * 8
     _compare(got, exp)
+    _compare_mx(got, _oracle_mx(d["x"], d["w13"], off, rt))
