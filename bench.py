@@ -78,7 +78,8 @@ def _gemm_source_hash():
 
 
 def _counter_per_dispatch(directory, counter):
-    """{kernel name: [value per dispatch]} from a rocprofv3 counter_collection.csv."""
+    """{kernel name: [(grid size, value) per dispatch]} from a rocprofv3
+    counter_collection.csv."""
     import csv
     import glob
     out = {}
@@ -88,10 +89,10 @@ def _counter_per_dispatch(directory, counter):
             for r in csv.DictReader(fh):
                 if r["Counter_Name"] != counter:
                     continue
-                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                key = (r["Dispatch_Id"], r["Kernel_Name"], int(r["Grid_Size"]))
                 per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
-        for (_, name), v in per.items():
-            out.setdefault(name, []).append(v)
+        for (_, name, grid), v in per.items():
+            out.setdefault(name, []).append((grid, v))
     return out
 
 
@@ -103,13 +104,16 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
 
     def pick(d, key):
-        vals = [v for n, vs in d.items() if key in n for v in vs]
+        # the prefill layer's launches: the largest grid of that kernel (the
+        # decode layer launches the same kernel on a small grid)
+        vals = [gv for n, vs in d.items() if key in n for gv in vs]
         if not vals:
             raise SystemExit(f"no dispatch of a kernel matching {key!r}")
-        return vals
+        big = max(g for g, _ in vals)
+        return [v for g, v in vals if g == big]
 
     def copy_val(d):
-        vals = [v for n, vs in d.items() if "copy" in n.lower() for v in vs]
+        vals = [v for n, vs in d.items() if "copy" in n.lower() for _, v in vs]
         if not vals:
             raise SystemExit("no copy kernel dispatch found (run with --copy-probe-mib)")
         return max(vals)

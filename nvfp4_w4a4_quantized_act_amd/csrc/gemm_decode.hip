@@ -17,8 +17,9 @@
 // per 128-deep chunk of K, codes 64h .. 64h + 63 of one weight row in each of
 // the wave's two 32-row blocks and of one token row, with the block scales
 // that cover them.  The loads go straight to registers in that layout, three
-// chunks ahead of the MFMAs (a ring of three buffers, unrolled so the buffer of
-// each chunk is fixed and the compiler's waits are plain counts).  A chunk is
+// or four chunks ahead of the MFMAs (a ring of named register slots, unrolled
+// so the slot of each chunk is fixed and the compiler's waits are plain
+// counts).  A chunk is
 // converted exactly to fp16 (hardware fp4 -> fp16 convert, then a packed
 // multiply by the E4M3 block scale; every v * s_b is an fp16 number) and fed
 // to 32x32x16 fp16 MFMAs, weights as the first operand.  MFMA step j of a
@@ -30,9 +31,9 @@
 // they stream by (sel ascending: chunk c holds the selected channels in
 // [128c, 128c + 128), a uniform range), converted to fp16 and parked in LDS,
 // row by row; after the main loop they are the first MFMA operand against the
-// residual codes R (second pass of Eq. (21)), in registers of their own since
-// the tensor scale differs:
-//   Y = acc * s_tA s_tW[e] + accc * s_tR s_tW[e].
+// residual codes R (second pass of Eq. (21)), accumulated apart from the main
+// product since the tensor scale differs:
+//   Y = acc_main * s_tA s_tW[e] + acc_comp * s_tR s_tW[e].
 #include "common.h"
 #include "gemm_tiles.h"
 
@@ -46,7 +47,6 @@ constexpr int kWaves = 2;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kChunk = 128;          // channels per chunk: 64 codes per lane
 constexpr int kRows = 32;            // token rows per pass (one MFMA operand)
-constexpr int kRing = 3;             // chunks in flight per wave
 constexpr int kCapMax = 64;          // compensation channels kept in LDS
 constexpr int kCapLd = kCapMax + 8;  // halfs per LDS row (conflict-free 16-byte reads)
 
@@ -126,13 +126,19 @@ __device__ __forceinline__ float silu_mul(float gt, float up) {
 // Grid: E x slabs work-groups, block b = slab * E + e (consecutive blocks go
 // to different XCDs and experts; with E a multiple of 8, all slabs of an
 // expert share one XCD's L2, where its activation rows stay).
-template <int kEpi>
+// kRing (3 or 4): chunks in flight per wave, chosen so that the chunk count
+// is a multiple of it where it can be (the loads past the last chunk are
+// wasted work).
+template <int kEpi, int kRing>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     // compensation weight columns, per wave and row block: [row][channel]
     __shared__ __align__(16) _Float16 capt[kWaves][2][32][kCapLd];
     // a chunk's weight pieces, word-major, while its compensation columns are taken
     __shared__ uint32_t stage[kWaves][2][9][64];
+    // the selected channels, per wave (read by lane-dependent index in code
+    // where some lanes are inactive: no cross-lane reads there)
+    __shared__ int s_sel[kWaves][kCapMax];
 
     const int e = (int)(blockIdx.x % (unsigned)g.E);
     const int slab = (int)(blockIdx.x / (unsigned)g.E);
@@ -183,6 +189,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         for (int i = lane; i < 2 * 32 * kCapLd / 8; i += 64)
             reinterpret_cast<uint4*>(&capt[wave][0][0][0])[i] = make_uint4(0, 0, 0, 0);
         sel_lo = lane < g.k ? g.sel[lane] : 0;
+        s_sel[wave][lane] = sel_lo;
     }
 
     for (int c0 = 0; c0 < cnt; c0 += kRows) {
@@ -194,7 +201,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
 
-        // The ring: chunk c lives in slot c % 3 (three named slots, no array,
+        // The ring: chunk c lives in slot c % kRing (named slots, no array,
         // so everything stays in registers); loads past the last chunk repeat
         // it (no branch) and are never used.  The first weight chunks are
         // requested before the token rows, whose addresses wait for
@@ -204,10 +211,11 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             w0 = load_piece(wnib, wsc, wrow_n[0] + 64 * cl, wrow_s[0] + 8 * cl);
             w1 = load_piece(wnib, wsc, wrow_n[1] + 64 * cl, wrow_s[1] + 8 * cl);
         };
-        Piece w0a, w1a, aa, w0b, w1b, ab, w0c, w1c, ac;
+        Piece w0a, w1a, aa, w0b, w1b, ab, w0c, w1c, ac, w0d, w1d, ad;
         ldw(w0a, w1a, 0);
         ldw(w0b, w1b, 1);
         ldw(w0c, w1c, 2);
+        if (kRing == 4) ldw(w0d, w1d, 3);
         const int64_t src = rv ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
         // the token row: a per-lane base (the activation tensor may exceed 4 GB)
         const uint8_t* an = g.a_nib + src * kn + 32 * h;
@@ -219,6 +227,19 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         lda(aa, 0);
         lda(ab, 1);
         lda(ac, 2);
+        if (kRing == 4) lda(ad, 3);
+        // the residual codes of this pass's rows (k <= 64: at most 4 steps of
+        // 16 channels, a dword of codes and a scale byte each), requested now
+        // so the compensation after the main loop waits for nothing
+        uint32_t rw[kCapMax / kBlock], rs[kCapMax / kBlock];
+#pragma unroll
+        for (int t = 0; t < kCapMax / kBlock; ++t) {
+            const int tt = t < ncs ? t : 0;
+            rw[t] = ncs > 0 ? *reinterpret_cast<const uint32_t*>(g.r_nib + src * (g.k / 2) +
+                                                                 8 * tt + 4 * h)
+                            : 0u;
+            rs[t] = ncs > 0 ? g.r_scale[src * ncs + tt] : 0u;
+        }
         int ci = 0;                                   // next compensation channel to capture
         auto step = [&](Piece& w0, Piece& w1, Piece& a, int c) {
             if (c < nch) {
@@ -235,31 +256,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
                     }
                     stage[wave][0][8][lane] = wv[0] ? w0.sc : 0u;
                     stage[wave][1][8][lane] = wv[1] ? w1.sc : 0u;
-                    // channels ci .. cend - 1 lie in this chunk (sel ascending)
+                    // channels ci .. cend - 1 lie in this chunk (sel ascending);
+                    // the (row, channel) pairs are spread over the 64 lanes,
+                    // each reading the staged word of the lane that holds it
                     const int cend = __popcll(__ballot(lane < g.k && sel_lo < kChunk * (c + 1)));
-#pragma unroll 4
-                    for (; ci < cend; ++ci) {
-                        const int j = __builtin_amdgcn_readlane(sel_lo, ci) - kChunk * c;
+                    for (int idx = lane; idx < 32 * (cend - ci); idx += 64) {
+                        const int rr = idx & 31, ch = ci + (idx >> 5);
+                        const int j = s_sel[wave][ch] - kChunk * c;
                         if (j < 0 || j >= kChunk) continue;   // not ascending: skipped (reads 0)
-                        const int hh = j >> 6, jj = j & 63, sh = 4 * (jj & 7), sb = 8 * (jj >> 4);
-                        const uint32_t y0 = stage[wave][0][jj >> 3][lane];
-                        const uint32_t y1 = stage[wave][1][jj >> 3][lane];
-                        const uint32_t b0 = (stage[wave][0][8][lane] >> sb) & 0xFFu;
-                        const uint32_t b1 = (stage[wave][1][8][lane] >> sb) & 0xFFu;
-                        const _Float16 v0 =
+                        const int src = rr + 32 * (j >> 6), jj = j & 63;
+                        const int sh = 4 * (jj & 7), sb = 8 * (jj >> 4);
+                        const uint32_t y0 = stage[wave][0][jj >> 3][src];
+                        const uint32_t y1 = stage[wave][1][jj >> 3][src];
+                        const uint32_t b0 = (stage[wave][0][8][src] >> sb) & 0xFFu;
+                        const uint32_t b1 = (stage[wave][1][8][src] >> sb) & 0xFFu;
+                        capt[wave][0][rr][ch] =
                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((y0 >> sh) & 0xFu, 1.0f, 0)[0] *
                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b0, 1.0f, false)[0];
-                        const _Float16 v1 =
+                        capt[wave][1][rr][ch] =
                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp4((y1 >> sh) & 0xFu, 1.0f, 0)[0] *
                             __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b1, 1.0f, false)[0];
-                        if (h == hh) {
-                            capt[wave][0][r][ci] = v0;
-                            capt[wave][1][r][ci] = v1;
-                        }
                     }
+                    ci = cend;
                 }
                 chunk_mma(w0, w1, a, wv, rv, acc);
             }
+            // the slot's next chunk is requested after this chunk's work, so
+            // it reuses the slot's registers (hoisting it would need a second
+            // set)
+            __builtin_amdgcn_sched_barrier(0);
             ldw(w0, w1, c + kRing);
             lda(a, c + kRing);
         };
@@ -267,24 +292,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             step(w0a, w1a, aa, cb);
             step(w0b, w1b, ab, cb + 1);
             step(w0c, w1c, ac, cb + 2);
+            if (kRing == 4) step(w0d, w1d, ad, cb + 3);
         }
 
-        // compensation: captured columns against this pass's residual rows
-        f32x16 accc[2];
+        // compensation: captured columns against this pass's residual rows,
+        // in the same accumulators once the main product, scaled, has moved
+        // to registers the ring no longer needs
+        float ym[2][16];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) accc[q][v] = 0.0f;
-        for (int t = 0; t < ncs; ++t) {
-            const uint32_t rw = *reinterpret_cast<const uint32_t*>(
-                g.r_nib + src * (g.k / 2) + 8 * t + 4 * h);
-            const uint32_t rs = g.r_scale[src * ncs + t];
-            const f16x8 rf = cvt8(rv ? rw : 0u, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
-                                                    rv ? rs : 0u, 1.0f, false)[0]);
+            for (int v = 0; v < 16; ++v) {
+                ym[q][v] = acc[q][v] * ca;
+                acc[q][v] = 0.0f;
+            }
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                const f16x8 wf = *reinterpret_cast<const f16x8*>(&capt[wave][q][r][16 * t + 8 * h]);
-                accc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, rf, accc[q], 0, 0, 0);
+        for (int t = 0; t < kCapMax / kBlock; ++t) {
+            if (t < ncs) {
+                const f16x8 rf = cvt8(rv ? rw[t] : 0u, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                                                           rv ? rs[t] : 0u, 1.0f, false)[0]);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const f16x8 wf =
+                        *reinterpret_cast<const f16x8*>(&capt[wave][q][r][16 * t + 8 * h]);
+                    acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf, rf, acc[q], 0, 0, 0);
+                }
             }
         }
 
@@ -299,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
                 for (int q = 0; q < 2; ++q)
 #pragma unroll
                     for (int u = 0; u < 4; ++u)
-                        y[q][u] = acc[q][4 * grp + u] * ca + accc[q][4 * grp + u] * cr;
+                        y[q][u] = ym[q][4 * grp + u] + acc[q][4 * grp + u] * cr;
                 if (swiglu) {
                     const int nh = g.N / 2;
                     const int feat = slab * 64 + wave * 32 + 8 * grp + nq;
@@ -366,10 +398,17 @@ bool gemm_decode_fits(const GemmArgs& g) {
 int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
     const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
     const dim3 grid((unsigned)(slabs * g.E)), block(dec::kThreads);
-    if (g.epilogue == QUADS_EPI_SWIGLU)
-        hipLaunchKernelGGL(dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU>, grid, block, 0, st, g);
+    const int nch = g.K / dec::kChunk;
+    const bool ring3 = nch % 4 != 0 && nch % 3 == 0;
+    const bool sw = g.epilogue == QUADS_EPI_SWIGLU;
+    if (sw && ring3)
+        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU, 3>), grid, block, 0, st, g);
+    else if (sw)
+        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU, 4>), grid, block, 0, st, g);
+    else if (ring3)
+        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_NONE, 3>), grid, block, 0, st, g);
     else
-        hipLaunchKernelGGL(dec::k_gemm_w4a4_decode<QUADS_EPI_NONE>, grid, block, 0, st, g);
+        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_NONE, 4>), grid, block, 0, st, g);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }
