@@ -51,7 +51,9 @@ def pack_routes(topk_ids, num_experts):
 def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
     """Grouped W4A4 GEMM with the residual compensation term, in fp64.
 
-    a   = (packed [Ta, K/2], scales [Ta, K/16], s_tA)   activation NVFP4
+    a   = (packed [Ta, K/2], scales [Ta, K/16], s_tA)   activation NVFP4; s_tA
+          is a scalar, or an array [Ta] of per-row (per-token) scales, in
+          which case packed row p takes s_tA[row(p)] (compensation: k = 0)
     r   = (packed [Ta, k/2], scales [Ta, k/16], s_tR) or None   second pass
     sel = int array [k] of selected channels (ascending)
     w   = (packed [E, N, K/2], scales [E, N, K/16], s_tW [E])   weights
@@ -73,7 +75,10 @@ def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
     k = 0 if r is None else len(sel)
     y = np.zeros((rows, n), dtype=np.float64)
     bound = np.zeros((rows, n), dtype=np.float64) if want_bound else None
-    sa = np.float64(np.float32(a_ts))
+    sa_arr = np.asarray(a_ts, dtype=np.float32).astype(np.float64)
+    per_row = sa_arr.ndim > 0
+    if per_row and k:
+        raise ValueError("per-row activation scales take no compensation term")
     sr = np.float64(np.float32(r[2])) if k else 0.0
     for e in range(e_count):
         p0, p1 = int(offsets[e]), int(offsets[e + 1])
@@ -83,6 +88,7 @@ def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
         ah = dequantize_unscaled(a_nib[src], a_sc[src])               # [m, K] exact
         wh = dequantize_unscaled(w_nib[e], w_sc[e])                   # [N, K] exact
         sw = np.float64(np.float32(w_ts[e]))
+        sa = sa_arr[src][:, None] if per_row else sa_arr
         y[p0:p1] = (sa * sw) * (ah @ wh.T)
         if want_bound:
             bound[p0:p1] = (sa * sw) * (np.abs(ah) @ np.abs(wh).T)

@@ -109,6 +109,28 @@ def quantize(x, ts=None):
     return pack_nibbles(nib), sb, s_t
 
 
+def quantize_rows(x):
+    """NVFP4 with one FP32 scale per row (per token) instead of per tensor:
+    steps 1-3 above with A taken over each row alone, i.e. quantize() applied
+    to every row as a tensor of its own.
+
+    Reading (a variant, not the pages' default): the pages' tensor scale is
+    one number per tensor; the per-token form trades one FP32 value per row
+    for rows whose magnitudes differ widely.  Returns (packed [rows, K/2],
+    scale bytes [rows, K/16], s_t float32 [rows]).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, k = x.shape
+    if k % BLOCK:
+        raise ValueError("K must be a multiple of 16")
+    packed = np.empty((rows, k // 2), np.uint8)
+    scales = np.empty((rows, k // BLOCK), np.uint8)
+    ts = np.empty(rows, np.float32)
+    for i in range(rows):
+        packed[i], scales[i], ts[i] = quantize(x[i:i + 1])
+    return packed, scales, ts
+
+
 def quantize_bf16(bits, ts=None):
     """quantize() of bf16 bit patterns."""
     return quantize(bf16_to_f64(bits), ts)

@@ -114,3 +114,27 @@ def test_combine_loop():
         for s in range(topk):
             acc = acc + np.float64(w[tt, s]) * y2[pos[tt * topk + s]]
         assert np.array_equal(out[tt], acc)
+
+
+def test_gemm_per_row_scales_exact_rational():
+    """Per-row activation scales: y[p, n] = s_t[row(p)] s_tW sum_j a w, against
+    a Fraction triple loop; with all scales equal it is the per-tensor GEMM."""
+    rng = np.random.default_rng(74)
+    x = rng.standard_normal((4, 32)) * np.exp2(rng.integers(-5, 6, (4, 1)))
+    x = F.bf16_to_f64(F.f64_to_bf16_rne(x))
+    ap, asc, ats = Q.quantize_rows(x)
+    w = synth.weights(rng, 1, 3, 32, std=0.5)
+    wp, ws, wt, _ = Q.weight_qdq(w)
+    row_token = np.array([2, 0, 3, 1, 2])
+    y, bound = M.grouped_gemm((ap, asc, ats), None, None, (wp, ws, wt), [0, 5], row_token)
+    wd = Q.dequantize(wp[0], ws[0], wt[0])
+    for p in range(5):
+        t = row_token[p]
+        ad = Q.dequantize(ap[t:t + 1], asc[t:t + 1], ats[t])[0]
+        for nn in range(3):
+            acc = sum(Fraction(float(ad[j])) * Fraction(float(wd[nn, j])) for j in range(32))
+            assert abs(Fraction(float(y[p, nn])) - acc) <= abs(acc) * Fraction(1, 2 ** 50)
+    same = np.full(4, ats[0], np.float32)
+    y1, _ = M.grouped_gemm((ap, asc, same), None, None, (wp, ws, wt), [0, 5], row_token)
+    y2, _ = M.grouped_gemm((ap, asc, ats[0]), None, None, (wp, ws, wt), [0, 5], row_token)
+    assert np.array_equal(y1, y2)

@@ -207,3 +207,58 @@ def test_quantize_error_bound(cfg):
     dq = Q.dequantize(nib, sb, ts)
     step = np.repeat(F.E4M3_GRID[sb], 16, -1) * np.float64(ts)
     assert np.all(np.abs(x - dq) <= step * 1.0 + 1e-300)
+
+
+# ---------------------------------------------------------------------------
+# per-token (per-row) FP32 scales: a variant where every row is its own tensor
+
+def test_quantize_rows_bruteforce():
+    """Each row against the exhaustive rational quantizer run on that row alone."""
+    rng = np.random.default_rng(71)
+    x = rng.standard_normal((5, 32)) * np.exp2(rng.integers(-6, 7, (5, 1)))
+    x = F.bf16_to_f64(F.f64_to_bf16_rne(x))
+    packed, scales, ts = Q.quantize_rows(x)
+    for i in range(5):
+        bp, bs, bt = _bruteforce_quantize([list(map(float, x[i]))])
+        assert np.array_equal(packed[i], bp[0]) and np.array_equal(scales[i], bs[0])
+        assert ts[i] == bt
+
+
+def test_quantize_rows_power_of_two_and_independence():
+    """Scaling one row by 2^j scales its s_t by 2^j exactly and leaves its codes,
+    its block scales and every other row unchanged."""
+    rng = np.random.default_rng(72)
+    x = F.bf16_to_f64(F.f64_to_bf16_rne(rng.standard_normal((6, 64))))
+    p0, s0, t0 = Q.quantize_rows(x)
+    for j in (-20, -3, 5, 40):
+        y = x.copy()
+        y[2] *= 2.0 ** j
+        p1, s1, t1 = Q.quantize_rows(y)
+        assert np.array_equal(p1, p0) and np.array_equal(s1, s0)
+        assert t1[2] == np.float32(t0[2] * 2.0 ** j)
+        assert np.array_equal(np.delete(t1, 2), np.delete(t0, 2))
+
+
+def test_quantize_rows_equal_maxima_match_tensor_scale():
+    """When every row has the same max |x|, per-row and per-tensor agree."""
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal((7, 48))
+    x[:, 5] = 3.5
+    x = np.clip(x, -3.5, 3.5)
+    x = F.bf16_to_f64(F.f64_to_bf16_rne(x))
+    pr, sr, tr = Q.quantize_rows(x)
+    pt, st, tt = Q.quantize(x)
+    assert np.array_equal(pr, pt) and np.array_equal(sr, st) and np.all(tr == tt)
+
+
+def test_quantize_rows_row_holding_2688():
+    """A row whose max is 2688 * 2^j gets s_t = 2^j, scale byte 0x7E (448) and
+    code 7 (6) for that element."""
+    x = np.zeros((2, 16))
+    x[0, 3] = 2688.0 * 2.0 ** -7
+    x[1, 9] = -2688.0 * 2.0 ** 4
+    packed, scales, ts = Q.quantize_rows(x)
+    assert list(ts) == [np.float32(2.0 ** -7), np.float32(2.0 ** 4)]
+    assert scales[0, 0] == 0x7E and scales[1, 0] == 0x7E
+    nib = Q.unpack_nibbles(packed)
+    assert nib[0, 3] == 7 and nib[1, 9] == 0xF
