@@ -85,6 +85,21 @@ int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* t
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Per-row (per-token) variant of the NVFP4 activation quantization: each
+ * row of x is quantized as a tensor of its own, with its own dynamic tensor
+ * scale s_t[m] = RN32(max_j |x[m, j]| / 2688) and then the block and element
+ * rules of section 2.2's "FP4" paragraph unchanged.  The pages define one
+ * FP32 scale per tensor; this form keeps one FP32 value per row so that rows
+ * of very different magnitude each use the full E4M3 block-scale range.
+ *   x       bf16 [M, K], K % 16 == 0
+ *   nib     out uint8 [M, K/2];  scale out uint8 [M, K/16]
+ *   ts      out fp32 [M]: the row scales (0 for an all-zero row)
+ * No workspace.  M == 0 is a no-op.
+ */
+int quads_nvfp4_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* nib,
+                              uint8_t* scale, float* ts, void* stream);
+
+/*
  * Residual Activation Compensation (section 3.3).
  *   x        bf16 [M, K], K % 16 == 0;  k % 16 == 0, 0 <= k <= K
  *   nib, scale, ts    main NVFP4 of x, identical to quads_nvfp4_quantize
@@ -169,6 +184,22 @@ int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale, const floa
                         const int32_t* offsets, int32_t E, int64_t N,
                         int epilogue, int out_dtype, void* out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped W4A4 GEMM with per-row activation tensor scales (the activations
+ * of quads_nvfp4_quantize_rows), no compensation term:
+ *   Y[p,n] = s_tA[row(p)] s_tW[e] sum_{j<K} a[row(p), j] w_e[n, j]
+ *   a_ts_rows  fp32 [Ta]: the scale of each A row
+ *   every other argument, the workspace and the rules as in
+ *   quads_moe_w4a4_gemm with k == 0 (query quads_moe_w4a4_gemm_ws with k = 0)
+ */
+int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t* a_scale,
+                                 const float* a_ts_rows, const int32_t* row_token,
+                                 int64_t rows, int64_t K,
+                                 const uint8_t* w_nib, const uint8_t* w_scale, const float* w_ts,
+                                 const int32_t* offsets, int32_t E, int64_t N,
+                                 int epilogue, int out_dtype, void* out,
+                                 void* ws, size_t ws_bytes, void* stream);
 
 /*
  * MoE combine: out[t, n] = sum over slots in order of topk_w[t, slot] *

@@ -16,8 +16,9 @@ import torch
 
 __all__ = [
     "QuadsError", "lib", "library_path",
-    "quads_nvfp4_quantize", "quads_rac_quantize", "quads_nvfp4_weight_qdq",
-    "quads_moe_pack", "quads_moe_w4a4_gemm", "quads_moe_combine",
+    "quads_nvfp4_quantize", "quads_nvfp4_quantize_rows", "quads_rac_quantize",
+    "quads_nvfp4_weight_qdq", "quads_moe_pack", "quads_moe_w4a4_gemm",
+    "quads_moe_w4a4_gemm_rowscale", "quads_moe_combine",
     "quads_mx_quantize", "quads_moe_mx_gemm",
     "EPI_NONE", "EPI_SWIGLU", "OUT_F32", "OUT_BF16", "MX_FP8", "MX_FP4",
 ]
@@ -39,6 +40,7 @@ _SIGNATURES = {
     "quads_version": (ctypes.c_char_p, []),
     "quads_nvfp4_quantize_ws": (_SZ, [_I64, _I64]),
     "quads_nvfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "quads_nvfp4_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "quads_rac_quantize_ws": (_SZ, [_I64, _I64, _I32]),
     "quads_rac_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _SZ, _P]),
@@ -51,6 +53,9 @@ _SIGNATURES = {
     "quads_moe_w4a4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _I32,
                                            _P, _P, _P, _P, _I32, _I64, ctypes.c_int,
                                            ctypes.c_int, _P, _P, _SZ, _P]),
+    "quads_moe_w4a4_gemm_rowscale": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P,
+                                                    _I32, _I64, ctypes.c_int, ctypes.c_int, _P,
+                                                    _P, _SZ, _P]),
     "quads_moe_combine": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _I64, _I32, _I64, _P, _P]),
     "quads_mx_quantize": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P]),
     "quads_moe_mx_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I32, _I64,
@@ -119,6 +124,20 @@ def quads_nvfp4_quantize(x, ts_in=None):
     _check("quads_nvfp4_quantize", lib().quads_nvfp4_quantize(
         _ptr(x), m, k, _ptr(ts_in), _ptr(nib), _ptr(scale), _ptr(ts), _ptr(ws), nws,
         _stream(dev)))
+    return nib, scale, ts
+
+
+def quads_nvfp4_quantize_rows(x):
+    """NVFP4 of bf16 x [M, K] with one tensor scale per row -> (nib uint8 [M, K/2],
+    scale uint8 [M, K/16], ts fp32 [M])."""
+    x = _bits16(x)
+    m, k = x.shape
+    dev = x.device
+    nib = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    scale = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(max(m, 1), dtype=torch.float32, device=dev)[:m]
+    _check("quads_nvfp4_quantize_rows", lib().quads_nvfp4_quantize_rows(
+        _ptr(x), m, k, _ptr(nib), _ptr(scale), _ptr(ts), _stream(dev)))
     return nib, scale, ts
 
 
@@ -205,6 +224,29 @@ def quads_moe_w4a4_gemm(a, w, n, rows=None, r=None, sel=None, offsets=None, row_
         _ptr(rn) if k else None, _ptr(rs) if k else None, _ptr(rt) if k else None,
         _ptr(sel) if k else None, k, _ptr(w_nib), _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e,
         n, epilogue, out_dtype, _ptr(out), _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def quads_moe_w4a4_gemm_rowscale(a, w, n, rows=None, offsets=None, row_token=None,
+                                 epilogue=EPI_NONE, out_dtype=OUT_F32, out=None):
+    """Grouped W4A4 GEMM with one activation tensor scale per A row:
+    a = (nib, scale, ts [Ta]) as from quads_nvfp4_quantize_rows; no RAC."""
+    a_nib, a_scale, a_ts = a
+    w_nib, w_scale, w_ts = w
+    e = w_nib.shape[0]
+    kd = a_nib.shape[1] * 2
+    if rows is None:
+        rows = row_token.shape[0] if row_token is not None else a_nib.shape[0]
+    dev = a_nib.device
+    ncols = n // 2 if epilogue == EPI_SWIGLU else n
+    if out is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.int16
+        out = torch.empty((rows, ncols), dtype=dt, device=dev)
+    ws, nws = _ws(lib().quads_moe_w4a4_gemm_ws(rows, kd, 0, e, n), dev)
+    _check("quads_moe_w4a4_gemm_rowscale", lib().quads_moe_w4a4_gemm_rowscale(
+        _ptr(a_nib), _ptr(a_scale), _ptr(a_ts), _ptr(row_token), rows, kd, _ptr(w_nib),
+        _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e, n, epilogue, out_dtype, _ptr(out),
+        _ptr(ws), nws, _stream(dev)))
     return out
 
 

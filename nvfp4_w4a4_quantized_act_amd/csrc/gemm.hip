@@ -237,7 +237,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     }
 
     // epilogue
-    const float s_ta = g.a_ts[0], s_tw = g.w_ts[e];
+    const float s_ta = tensor_scale_a(g), s_tw = g.w_ts[e];
     const float ca = s_ta * s_tw;
     const float cr = g.k > 0 ? g.r_ts[0] * s_tw : 0.0f;
 #pragma unroll
@@ -247,20 +247,18 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
             const int row_t = wm * 64 + mi * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
             const int prow = m0 + row_t;
             if (prow >= mend) continue;
+            const float ca_row = row_scale(g, prow, ca);
             float y[2];
 #pragma unroll
             for (int nj = 0; nj < 2; ++nj) {
-                y[nj] = acc[mi][nj][v] * ca;
+                y[nj] = acc[mi][nj][v] * ca_row;
                 if (g.k > 0) y[nj] = fmaf(accc[mi][nj][v], cr, y[nj]);
             }
             if (swiglu) {
                 const int feat = f0 + wn * 32 + (lane & 31);
                 if (feat < g.N / 2) {
                     const float gt = y[0], up = y[1];
-                    // silu(g) u with the hardware exp2 and reciprocal: relative
-                    // error a few 1e-6, far inside half a bf16 ulp (2^-9)
-                    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
-                    const float hval = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+                    const float hval = silu_mul(gt, up);
                     ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] =
                         (uint16_t)bf16_rne_from_f32(hval);
                 }
@@ -606,7 +604,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     // (<= 2^80, so |acc| stays below 2^120).  Otherwise it runs first with
     // gathered weight columns and acc *= s_tR / s_tA.  s_tR = 0 means every
     // residual code is 0 and the compensation is skipped.
-    const float s_ta = g.a_ts[0];
+    const float s_ta = tensor_scale_a(g);
     const float s_tr = g.k > 0 ? g.r_ts[0] : 0.0f;
     const bool comp = g.k > 0 && s_tr > 0.0f;
     const bool capture_path = !comp || (g.k == BK && s_tr >= s_ta * 0x1p-80f);
@@ -656,14 +654,15 @@ extern "C" size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int
     return 0;
 }
 
-extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
-                                   const float* a_ts, const int32_t* row_token, int64_t rows,
-                                   int64_t K, const uint8_t* r_nib, const uint8_t* r_scale,
-                                   const float* r_ts, const int32_t* sel, int32_t k,
-                                   const uint8_t* w_nib, const uint8_t* w_scale,
-                                   const float* w_ts, const int32_t* offsets, int32_t E,
-                                   int64_t N, int epilogue, int out_dtype, void* out, void* ws,
-                                   size_t ws_bytes, void* stream) {
+// Both entry points: a_ts_rows is null (one tensor scale a_ts[0]) or the
+// per-row scales [Ta] (then a_ts == a_ts_rows and k == 0).
+static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
+                     const float* a_ts_rows, const int32_t* row_token, int64_t rows, int64_t K,
+                     const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
+                     const int32_t* sel, int32_t k, const uint8_t* w_nib,
+                     const uint8_t* w_scale, const float* w_ts, const int32_t* offsets,
+                     int32_t E, int64_t N, int epilogue, int out_dtype, void* out, void* ws,
+                     size_t ws_bytes, void* stream) {
     (void)ws;
     if (epilogue != QUADS_EPI_NONE && epilogue != QUADS_EPI_SWIGLU) return QUADS_EINVAL;
     if (out_dtype != QUADS_OUT_F32 && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
@@ -684,7 +683,7 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
     if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
-               out_dtype == QUADS_OUT_BF16, out, 0};
+               out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows};
     hipStream_t st = (hipStream_t)stream;
     if (gemm_decode_fits(g)) {
         // few rows per expert: the decode kernel takes every expert with at
@@ -724,4 +723,30 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
         hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_NONE>, grid, dim3(256), 0, st, g);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
+}
+
+extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
+                                   const float* a_ts, const int32_t* row_token, int64_t rows,
+                                   int64_t K, const uint8_t* r_nib, const uint8_t* r_scale,
+                                   const float* r_ts, const int32_t* sel, int32_t k,
+                                   const uint8_t* w_nib, const uint8_t* w_scale,
+                                   const float* w_ts, const int32_t* offsets, int32_t E,
+                                   int64_t N, int epilogue, int out_dtype, void* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+    return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, row_token, rows, K, r_nib, r_scale, r_ts,
+                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out, ws,
+                     ws_bytes, stream);
+}
+
+extern "C" int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t* a_scale,
+                                            const float* a_ts_rows, const int32_t* row_token,
+                                            int64_t rows, int64_t K, const uint8_t* w_nib,
+                                            const uint8_t* w_scale, const float* w_ts,
+                                            const int32_t* offsets, int32_t E, int64_t N,
+                                            int epilogue, int out_dtype, void* out, void* ws,
+                                            size_t ws_bytes, void* stream) {
+    if (!ok_ptr(a_ts_rows)) return QUADS_EINVAL;
+    return gemm_w4a4(a_nib, a_scale, a_ts_rows, a_ts_rows, row_token, rows, K, nullptr, nullptr,
+                     nullptr, nullptr, 0, w_nib, w_scale, w_ts, offsets, E, N, epilogue,
+                     out_dtype, out, ws, ws_bytes, stream);
 }

@@ -117,12 +117,6 @@ __device__ __forceinline__ void chunk_mma(const Piece& w0, const Piece& w1, cons
     }
 }
 
-__device__ __forceinline__ float silu_mul(float gt, float up) {
-    // silu(g) u with the hardware exp2 and reciprocal, as in the tiled kernel
-    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
-    return gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
-}
-
 // Grid: E x slabs work-groups, block b = slab * E + e (consecutive blocks go
 // to different XCDs and experts; with E a multiple of 8, all slabs of an
 // expert share one XCD's L2, where its activation rows stay).
@@ -180,7 +174,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     const int nch = g.K / kChunk;
     const int ncs = g.k / kBlock;                     // compensation steps of 16
     const float s_tw = g.w_ts[e];
-    const float ca = g.a_ts[0] * s_tw;
+    const float ca = tensor_scale_a(g) * s_tw;
     const float cr = g.k > 0 ? g.r_ts[0] * s_tw : 0.0f;
 
     // the selected channels, one per lane, read back one at a time as scalars
@@ -298,12 +292,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         // compensation: captured columns against this pass's residual rows,
         // in the same accumulators once the main product, scaled, has moved
         // to registers the ring no longer needs
+        const float ca_row = g.a_ts_rows ? g.a_ts_rows[src] * ca : ca;   // per-row scales
         float ym[2][16];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                ym[q][v] = acc[q][v] * ca;
+                ym[q][v] = acc[q][v] * ca_row;
                 acc[q][v] = 0.0f;
             }
 #pragma unroll

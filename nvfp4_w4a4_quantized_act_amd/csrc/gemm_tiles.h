@@ -21,7 +21,39 @@ struct GemmArgs {
     // (gemm_decode.hip); the tiled kernels skip them.  0: the tiled kernel
     // takes every expert.
     int dec_rows;
+    // Per-row activation scales [Ta] (one per activation row, indexed through
+    // row_token), or null for the single tensor scale a_ts[0].  Only with
+    // k == 0.
+    const float* a_ts_rows;
 };
+
+// The activation tensor scale that multiplies a packed row's output: the
+// tensor's, or (per-row scales) 1, the row's own scale being applied in the
+// epilogue by row_scale().
+__device__ __forceinline__ float tensor_scale_a(const GemmArgs& g) {
+    return g.a_ts_rows ? 1.0f : g.a_ts[0];
+}
+
+// ca for packed row p: the epilogue's ca (s_tA s_tW, or s_tW with per-row
+// scales) times the row's own scale.
+__device__ __forceinline__ float row_scale(const GemmArgs& g, int p, float ca) {
+    if (!g.a_ts_rows) return ca;
+    const int64_t src = g.row_token ? (int64_t)g.row_token[p] : (int64_t)p;
+    return g.a_ts_rows[src] * ca;
+}
+
+// SwiGLU's product silu(g) u = g u / (1 + e^-g), within a few 1e-6 relative
+// (half a bf16 ulp is 2^-9) wherever the result and g u are finite in fp32.
+// With a = -g log2(e): up to a = 64 the hardware exp2 and reciprocal; above
+// it 1 + 2^a rounds to 2^a in fp32, so the result is g u 2^-a, formed as
+// (g 2^(c-a) u) 2^-c with c = ceil(a), so that a gate far below -88 (where
+// 2^a overflows) still gives the small product instead of 0.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+    const float a = g * -1.4426950408889634f;
+    if (a <= 64.0f) return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a)) * u;
+    const float c = fminf(ceilf(a), 400.0f);         // beyond 400 the result is 0
+    return __builtin_amdgcn_ldexpf(g * __builtin_amdgcn_exp2f(c - a) * u, -(int)c);
+}
 
 namespace v2 {
 
@@ -141,6 +173,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
         if (mi >= mact) continue;
         const int prow = prow_l + mi * 32;
         if (prow >= mend) continue;
+        const float ca_row = row_scale(g, prow, ca);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
             if (swiglu) {
@@ -148,12 +181,9 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
                 float hv[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u) {
-                    const float gt = acc[mi][0][4 * q + u] * ca;
-                    const float up = acc[mi][1][4 * q + u] * ca;
-                    // silu(g) u with the hardware exp2 and reciprocal: relative
-                    // error a few 1e-6, far inside half a bf16 ulp (2^-9)
-                    const float ex = __builtin_amdgcn_exp2f(gt * -1.4426950408889634f);
-                    hv[u] = gt * __builtin_amdgcn_rcpf(1.0f + ex) * up;
+                    const float gt = acc[mi][0][4 * q + u] * ca_row;
+                    const float up = acc[mi][1][4 * q + u] * ca_row;
+                    hv[u] = silu_mul(gt, up);
                 }
                 const uint32_t p01 = pk_bf16(hv[0], hv[1]), p23 = pk_bf16(hv[2], hv[3]);
                 const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
@@ -172,7 +202,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
                     const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
                     float y[4];
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca;
+                    for (int u = 0; u < 4; ++u) y[u] = acc[mi][nj][4 * q + u] * ca_row;
                     const int64_t o = (int64_t)prow * g.N + n;
                     const bool vec = n + 3 < g.N && (g.N & 3) == 0;
                     if (g.out_bf16) {

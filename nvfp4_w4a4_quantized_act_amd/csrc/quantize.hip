@@ -149,6 +149,60 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
     }
 }
 
+// Per-row variant: one wave per row, the row's own tensor scale.  Lane l
+// takes half-blocks l, l + 64, ... of the row (8 elements each; the other half
+// of its block is on lane l ^ 1): a max pass over the row, then the block
+// scale from the pair's maximum and the exact threshold compares.
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t* __restrict__ x,
+                                                       int64_t M, int K,
+                                                       uint8_t* __restrict__ nib,
+                                                       uint8_t* __restrict__ scale,
+                                                       float* __restrict__ ts) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= M) return;                            // whole wave
+    const int nh = K / 8;                            // half-blocks in the row
+    const uint4* xr = reinterpret_cast<const uint4*>(x + row * K);
+    uint32_t m = 0;
+    for (int hb = lane; hb < nh; hb += 64) {
+        const uint4 q = xr[hb];
+        m = pk_max_u16(m, q.x & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.y & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.z & 0x7FFF7FFFu);
+        m = pk_max_u16(m, q.w & 0x7FFF7FFFu);
+    }
+    const uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+    const uint32_t am_row = wave_max_u32(lo > hi ? lo : hi);
+    const float s_t = tensor_scale_from_amax(bf16_to_f32(am_row));
+    if (lane == 0) ts[row] = s_t;
+    const double six_st = 6.0 * (double)s_t;                     // exact
+    // nh is even, so a lane and its pair partner are both in range or both out
+    for (int hb0 = 0; hb0 < nh; hb0 += 64) {
+        const int hb = hb0 + lane;
+        const bool live = hb < nh;
+        const uint4 q = xr[live ? hb : 0];
+        const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+        uint32_t am = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
+                                 pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
+        am = (am & 0xFFFFu) > (am >> 16) ? (am & 0xFFFFu) : (am >> 16);
+        const uint32_t o = __shfl_xor(am, 1, 64);
+        am = o > am ? o : am;
+        const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)bf16_to_f32(am) / six_st) : 0u;
+        uint32_t thr[7];
+        e2m1_thresholds(e4m3_value(sb), s_t, thr);
+        uint32_t codes = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const uint32_t hbits = (w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+            codes |= (e2m1_mag_code((hbits & 0x7FFFu) << 16, thr) | ((hbits >> 12) & 8u)) << (4 * e);
+        }
+        if (live) {
+            *reinterpret_cast<uint32_t*>(nib + row * (K / 2) + (int64_t)hb * 4) = codes;
+            if ((hb & 1) == 0) scale[row * (K / kBlock) + hb / 2] = (uint8_t)sb;
+        }
+    }
+}
+
 __global__ void k_fill_f32(float* p, int n, float v) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = v;
@@ -218,6 +272,19 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     QUADS_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_quantize_bf16<false>, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
                        ts_out, table, nib, scale, (uint16_t*)nullptr);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+extern "C" int quads_nvfp4_quantize_rows(const uint16_t* x, int64_t M, int64_t K, uint8_t* nib,
+                                         uint8_t* scale, float* ts, void* stream) {
+    if (M < 0 || K <= 0 || K % kBlock || K >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
+    if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale) || !ok_ptr(ts)))
+        return QUADS_EINVAL;
+    if (M == 0) return QUADS_OK;
+    if (M > ((int64_t)1 << 33)) return QUADS_ESHAPE;
+    hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)((M + 3) / 4)), dim3(256), 0,
+                       (hipStream_t)stream, x, M, (int)K, nib, scale, ts);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

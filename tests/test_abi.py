@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 15
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 17
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -48,6 +48,15 @@ def test_quantize_validation():
     assert f(MIS, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ws, None) == -1       # misaligned
     assert f(FAKE, 4, 32, None, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == -3  # workspace
     assert f(FAKE, 4, 32, None, FAKE, FAKE, FAKE, None, ws, None) == -3
+
+
+def test_quantize_rows_validation():
+    f = Q.lib().quads_nvfp4_quantize_rows
+    assert f(FAKE, 4, 24, FAKE, FAKE, FAKE, None) == -2        # K % 16
+    assert f(FAKE, -1, 32, FAKE, FAKE, FAKE, None) == -2       # M < 0
+    assert f(FAKE, 4, 32, FAKE, FAKE, None, None) == -1        # ts missing
+    assert f(FAKE, 4, 32, MIS, FAKE, FAKE, None) == -1         # misaligned
+    assert f(None, 0, 32, None, None, None, None) == 0         # empty: no-op
 
 
 def test_rac_validation():
@@ -101,6 +110,21 @@ def test_gemm_validation():
     assert call(epi=7) == -1
     assert call(offsets=None) == -1            # offsets required for E > 1
     assert call(sel=None) == -1                # sel required for k > 0
+    assert call(out=MIS) == -1
+
+
+def test_gemm_rowscale_validation():
+    f = Q.lib().quads_moe_w4a4_gemm_rowscale
+    ws = Q.lib().quads_moe_w4a4_gemm_ws(64, 256, 0, 4, 64)
+
+    def call(k_dim=256, e=4, ts=FAKE, offsets=FAKE, epi=0, odt=0, out=FAKE):
+        return f(FAKE, FAKE, ts, None, 64, k_dim, FAKE, FAKE, FAKE, offsets, e, 64, epi, odt,
+                 out, FAKE, ws, None)
+    assert call(ts=None) == -1                 # per-row scales required
+    assert call(ts=MIS) == -1
+    assert call(k_dim=250) == -2
+    assert call(offsets=None) == -1
+    assert call(epi=1, odt=0) == -1
     assert call(out=MIS) == -1
 
 
