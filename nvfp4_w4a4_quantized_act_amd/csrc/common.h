@@ -293,8 +293,9 @@ inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 // Launchers shared between translation units (defined in quantize.hip).
 // Partial maxima of |x| over nseg contiguous segments of seg_elems elements
 // each, `groups` values per segment into partial[seg * groups + g].
+// The first segment's work-groups also zero clear[0 .. nclear).
 void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_t* partial,
-                         int groups, hipStream_t s);
+                         int groups, hipStream_t s, uint32_t* clear = nullptr, int nclear = 0);
 void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 // Tensor scale and code table per segment (1024 words of `table` each).
 void launch_scale_finalize(const uint32_t* partial, int groups, const float* ts_in, int nseg,

@@ -1,10 +1,11 @@
 // Token-to-expert packing and the MoE combine.
 //
 // Packing is a stable counting sort of the T*topk (token, slot) pairs by
-// expert id, in three launches: per-chunk histograms, one work-group that
-// turns them into expert offsets and per-chunk bases, and a scatter in which
-// one wave walks its chunk 64 entries at a time, ranking equal ids with
-// ballots so that equal ids keep their flattened order.
+// expert id.  Up to 4096 pairs and 512 experts: one work-group, one launch
+// (k_pack_small).  Otherwise three launches: per-chunk histograms, one
+// work-group that turns them into expert offsets and per-chunk bases, and a
+// scatter in which one wave walks its chunk 64 entries at a time, ranking
+// equal ids with ballots so that equal ids keep their flattened order.
 //
 // Combine: out[t] = sum over slots (in order) of w[t, slot] * y[pos[t, slot]],
 // eight output features per thread, fp32 fused multiply-adds.
@@ -174,6 +175,99 @@ __global__ __launch_bounds__(64) void k_pack_scatter(const int32_t* __restrict__
     }
 }
 
+// Small inputs (n <= kPackOneMaxN entries, E <= kPackOneMaxE) in one
+// work-group of 16 waves and one launch.  Wave w owns the contiguous entries
+// [w S, w S + S) (S a multiple of 64, at most 4 steps of 64, all ids held in
+// registers): per-wave expert counts; per expert the exclusive scan over the
+// waves plus the expert's offset (the scan over experts); then each wave
+// walks its entries 64 at a time, ranking equal ids with ballots.  Entries of
+// one expert thus keep their flattened order, as in the three-launch path.
+constexpr int kPackOneMaxN = 4096;        // above it the three launches are faster
+constexpr int kPackOneMaxE = 512;
+constexpr int kPackOneSteps = kPackOneMaxN / 16 / 64;     // 4
+
+__global__ __launch_bounds__(1024) void k_pack_small(const int32_t* __restrict__ ids, int n,
+                                                     int topk, int E,
+                                                     int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ row_token,
+                                                     int32_t* __restrict__ pos) {
+    __shared__ int s_h[16][kPackOneMaxE];    // per-wave counts, then next packed row
+    __shared__ int s_tot[kPackOneMaxE];
+    __shared__ int s_wave[16];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    for (int i = tid; i < 16 * kPackOneMaxE; i += 1024) (&s_h[0][0])[i] = 0;
+    const int S = ((n + 15) / 16 + 63) / 64 * 64;
+    const int steps = S / 64;                             // <= kPackOneSteps
+    const int b0 = w * S;
+    int ev[kPackOneSteps];                                // this lane's ids, -1 = none
+#pragma unroll
+    for (int it = 0; it < kPackOneSteps; ++it) {          // every load in flight at once
+        const int idx = b0 + it * 64 + lane;
+        const bool ok = it < steps && idx < n;
+        const int e = ids[ok ? idx : 0];
+        ev[it] = ok && e >= 0 && e < E ? e : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < kPackOneSteps; ++it)
+        if (ev[it] >= 0) atomicAdd(&s_h[w][ev[it]], 1);
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024) {                 // exclusive over waves, totals
+        int run = 0;
+        for (int q = 0; q < 16; ++q) {
+            const int c = s_h[q][e];
+            s_h[q][e] = run;
+            run += c;
+        }
+        s_tot[e] = run;
+    }
+    __syncthreads();
+    const int v = tid < E ? s_tot[tid] : 0;               // exclusive scan over experts
+    int x = v;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int wb = 0;
+    for (int q = 0; q < w; ++q) wb += s_wave[q];
+    const int off_e = x - v + wb;
+    if (tid < E) {
+        offsets[tid] = off_e;
+        s_tot[tid] = off_e;
+    }
+    if (tid == 0) offsets[E] = n;
+    __syncthreads();
+    for (int e = tid; e < E; e += 1024)
+        for (int q = 0; q < 16; ++q) s_h[q][e] += s_tot[e];
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+#pragma unroll
+    for (int it = 0; it < kPackOneSteps; ++it) {
+        if (it >= steps) break;                           // uniform
+        const int e = ev[it];
+        uint64_t peers = __ballot(e >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
+            peers &= (e >= 0 && ((e >> b) & 1)) ? m : ~m;
+        }
+        if (e >= 0) {
+            const int idx = b0 + it * 64 + lane;
+            const int p = s_h[w][e] + __popcll(peers & lt);
+            row_token[p] = idx / topk;
+            pos[idx] = p;
+        }
+        // every lane has read its expert's next row before the first peer moves it
+        __builtin_amdgcn_wave_barrier();
+        if (e >= 0 && __popcll(peers & lt) == 0) s_h[w][e] += __popcll(peers);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // ---------------------------------------------------------------- combine --
 template <bool kBf16>
 __global__ __launch_bounds__(256) void k_combine(const void* __restrict__ y,
@@ -234,6 +328,12 @@ extern "C" int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, 
     const int64_t n = T * topk;
     const int nchunks = (int)((n + kPackChunk - 1) / kPackChunk);
     int32_t* cnt = static_cast<int32_t*>(ws);
+    if (n > 0 && n <= kPackOneMaxN && E <= kPackOneMaxE) {
+        hipLaunchKernelGGL(k_pack_small, dim3(1), dim3(1024), 0, s, topk_ids, (int)n, (int)topk,
+                           (int)E, offsets, row_token, pos);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
     if (nchunks > 0) {
         hipLaunchKernelGGL(k_pack_count, dim3(nchunks), dim3(256), 0, s, topk_ids, n, (int)E, cnt);
         QUADS_CHECK_LAUNCH();

@@ -15,9 +15,14 @@ namespace quads {
 
 // Max of |x| (as bf16 bit patterns) over segment blockIdx.y of seg_elems
 // elements; one result per work-group into partial[blockIdx.y * gridDim.x + x].
+// `clear` (optional): nclear words zeroed by the first segment's work-groups
+// (counters of a kernel that runs after this one on the same stream).
 __global__ __launch_bounds__(256) void k_amax_partial(const uint16_t* __restrict__ x,
                                                       int64_t seg_elems,
-                                                      uint32_t* __restrict__ partial) {
+                                                      uint32_t* __restrict__ partial,
+                                                      uint32_t* __restrict__ clear, int nclear) {
+    if (blockIdx.y == 0)
+        for (int i = blockIdx.x * 256 + threadIdx.x; i < nclear; i += gridDim.x * 256) clear[i] = 0u;
     const int64_t nvec = seg_elems / 8;
     const uint4* v = reinterpret_cast<const uint4*>(x + (int64_t)blockIdx.y * seg_elems);
     uint32_t m = 0;
@@ -209,8 +214,9 @@ __global__ void k_fill_f32(float* p, int n, float v) {
 }
 
 void launch_amax_partial(const uint16_t* x, int64_t seg_elems, int nseg, uint32_t* partial,
-                         int groups, hipStream_t s) {
-    hipLaunchKernelGGL(k_amax_partial, dim3(groups, nseg), dim3(256), 0, s, x, seg_elems, partial);
+                         int groups, hipStream_t s, uint32_t* clear, int nclear) {
+    hipLaunchKernelGGL(k_amax_partial, dim3(groups, nseg), dim3(256), 0, s, x, seg_elems, partial,
+                       clear, nclear);
 }
 
 void launch_scale_finalize(const uint32_t* partial, int groups, const float* ts_in, int nseg,
@@ -265,7 +271,8 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     int groups = 1;
     if (!ts_in) {
         groups = amax_groups(n);
-        hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial);
+        hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial,
+                           (uint32_t*)nullptr, 0);
         QUADS_CHECK_LAUNCH();
     }
     launch_scale_finalize(partial, groups, ts_in, 1, ts_out, table, s);
@@ -313,7 +320,8 @@ extern "C" int quads_nvfp4_weight_qdq(const uint16_t* w, int64_t E, int64_t N, i
     int groups = amax_groups(n);
     uint32_t* partial = static_cast<uint32_t*>(ws);
     uint32_t* table = partial + align_up((size_t)E * kAmaxGroups * 4, 256) / 4;
-    hipLaunchKernelGGL(k_amax_partial, dim3(groups, (unsigned)E), dim3(256), 0, s, w, n, partial);
+    hipLaunchKernelGGL(k_amax_partial, dim3(groups, (unsigned)E), dim3(256), 0, s, w, n, partial,
+                       (uint32_t*)nullptr, 0);
     QUADS_CHECK_LAUNCH();
     launch_scale_finalize(partial, groups, nullptr, (int)E, w_ts, table, s);
     QUADS_CHECK_LAUNCH();

@@ -1,11 +1,14 @@
 // Residual Activation Compensation (arXiv 2607.15810, section 3.3).
 //
-//  scale   the tensor scale and code table of x, once (as in the quantizer).
-//  pass 1  (64-token x 256-channel tiles; a work-group walks several token
-//          chunks of one channel slice): NVFP4 of x as in the quantizer, the
-//          fp32 residual r = x - DQ(Q(x)) (Eq. (20), sign flipped) with one
-//          fused multiply-add, staged in LDS, then per channel the in-order
-//          fp64 sum of r^2 over the chunk's 64 tokens and max |r|.
+//  max     partial maxima of |x| (the quantizer's pass).
+//  pass 1  every work-group folds the partial maxima into the tensor scale
+//          and builds the code table in LDS (as the quantizer's finalize step
+//          does once), then (64-token x 256-channel tiles; a work-group walks
+//          several token chunks of one channel slice) NVFP4 of x as in the
+//          quantizer, the fp32 residual r = x - DQ(Q(x)) (Eq. (20), sign
+//          flipped) with one fused multiply-add, staged in LDS, then per
+//          channel the in-order fp64 sum of r^2 over the chunk's 64 tokens and
+//          max |r|.
 //  levels  the 64-ary fixed-order tree over those per-tile partials, one
 //          launch per level, until at most 16 partial rows per channel are
 //          left (Eq. (23)); none when neither S nor the scores are wanted.
@@ -27,45 +30,60 @@ constexpr int kSelectFold = 16;        // partial rows the select kernel sums it
 
 // ------------------------------------------------------------------ pass 1 --
 // Tile: 64 tokens x 256 channels.  Thread t quantizes 4 blocks (tile rows
-// t/16 + 16 q, channel block t%16), keeps the fp32 residuals in LDS, then
-// owns channel t of the tile for the in-order sum over the 64 tokens.
+// t/16 + 16 q, channel block t%16; the eight 16-byte loads issued together),
+// keeps the fp32 residuals in LDS, then owns channel t of the tile for the
+// in-order sum over the 64 tokens.
 constexpr int kP1Cols = 256;
 
 __global__ __launch_bounds__(256) void k_rac_pass1(
-    const uint16_t* __restrict__ x, int64_t M, int K, const float* __restrict__ ts,
-    const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
+    const uint16_t* __restrict__ x, int64_t M, int K, const uint32_t* __restrict__ partial,
+    int groups, float* __restrict__ ts, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
     double* __restrict__ p0, uint32_t* __restrict__ cm0) {
-    __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
+    __shared__ __align__(16) uint32_t s_tab[kE4m3MaxCode + 2][8];
     __shared__ float s_r[kTileRows][kP1Cols + 4];
-    for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x)
-        s_tab[i] = reinterpret_cast<const uint4*>(table)[i];
-    const float s_t = ts[0];
+    __shared__ float s_st;
+    __shared__ uint32_t s_red[4];
+    tensor_scale_prologue(partial, groups, nullptr, 0, &s_st, s_red);   // groups <= 8 * 256
+    __syncthreads();
+    const float s_t = s_st;
+    build_threshold_table(s_t, s_tab, true);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) ts[0] = s_t;
     const double six_st = 6.0 * (double)s_t;
     __syncthreads();
 
-    const int cb = threadIdx.x & 15;                 // 16-channel block in the tile
+    const int tid = threadIdx.x;
+    const int cb = tid & 15;                          // 16-channel block in the tile
     const int c0 = blockIdx.y * kP1Cols + cb * kBlock;
-    const int gc = blockIdx.y * kP1Cols + threadIdx.x;
+    const int gc = blockIdx.y * kP1Cols + tid;
     const int64_t nchunk = (M + kTileRows - 1) / kTileRows;
     for (int64_t ch = blockIdx.x; ch < nchunk; ch += gridDim.x) {
+        uint4 q0[4], q1[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                 // loads first, addresses clamped
+            const int64_t row = ch * kTileRows + (tid >> 4) + 16 * q;
+            const bool ok = row < M && c0 < K;
+            const uint4* p = reinterpret_cast<const uint4*>(x + (ok ? row * K + c0 : 0));
+            q0[q] = ld_stream16(p);
+            q1[q] = ld_stream16(p + 1);
+        }
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int rl = (threadIdx.x >> 4) + 16 * q;
+            const int rl = (tid >> 4) + 16 * q;
             const int64_t row = ch * kTileRows + rl;
             float r[16];
             if (row < M && c0 < K) {
                 const int64_t b = (row * K + c0) / kBlock;
-                const uint4* p = reinterpret_cast<const uint4*>(x + row * K + c0);
-                const uint4 q0 = ld_stream16(p);
-                const uint4 q1 = ld_stream16(p + 1);
-                const uint32_t w[8] = {q0.x, q0.y, q0.z, q0.w, q1.x, q1.y, q1.z, q1.w};
+                const uint32_t w[8] = {q0[q].x, q0[q].y, q0[q].z, q0[q].w,
+                                       q1[q].x, q1[q].y, q1[q].z, q1[q].w};
                 uint32_t am = 0;
 #pragma unroll
                 for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
                 const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
                 const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
                 const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
-                const uint2 packed = encode_block_bf16(w, s_tab[2 * sb], s_tab[2 * sb + 1]);
+                const uint4 t0 = *reinterpret_cast<const uint4*>(&s_tab[sb][0]);
+                const uint4 t1 = *reinterpret_cast<const uint4*>(&s_tab[sb][4]);
+                const uint2 packed = encode_block_bf16(w, t0, t1);
                 *reinterpret_cast<uint2*>(nib + b * 8) = packed;
                 scale[b] = (uint8_t)sb;
                 const float s_b = e4m3_value(sb);
@@ -88,19 +106,21 @@ __global__ __launch_bounds__(256) void k_rac_pass1(
                     make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
         }
         __syncthreads();
-        double acc = 0.0;
-        uint32_t m = 0;
+        if (p0 != nullptr) {                           // scores wanted
+            double acc = 0.0;
+            uint32_t m = 0;
 #pragma unroll 16
-        for (int i = 0; i < kTileRows; ++i) {                 // token order
-            const float rv = s_r[i][threadIdx.x];
-            const double rd = (double)rv;
-            acc = acc + rd * rd;                              // r^2 exact in fp64
-            const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
-            m = ab > m ? ab : m;
-        }
-        if (gc < K) {
-            p0[ch * K + gc] = acc;
-            cm0[ch * K + gc] = m;
+            for (int i = 0; i < kTileRows; ++i) {             // token order
+                const float rv = s_r[i][tid];
+                const double rd = (double)rv;
+                acc = acc + rd * rd;                          // r^2 exact in fp64
+                const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
+                m = ab > m ? ab : m;
+            }
+            if (gc < K) {
+                p0[ch * K + gc] = acc;
+                cm0[ch * K + gc] = m;
+            }
         }
         __syncthreads();
     }
@@ -355,7 +375,6 @@ __global__ void k_fill_f64(double* p, int n, double v) {
 
 struct RacWs {
     uint32_t* partial;
-    uint32_t* table;       // code table of x
     uint32_t* r_table;     // code table of the gathered residual
     double* pa;
     uint32_t* ca;
@@ -370,7 +389,6 @@ RacWs rac_ws_layout(char* base, int64_t M, int64_t K) {
     RacWs w;
     size_t off = 0;
     w.partial = (uint32_t*)(base + off); off += align_up(kAmaxGroups * 4, 256);
-    w.table = (uint32_t*)(base + off); off += 1024 * 4;
     w.r_table = (uint32_t*)(base + off); off += 1024 * 4;
     w.pa = (double*)(base + off); off += align_up((size_t)(c0 > 1 ? c0 : 1) * K * 8, 256);
     w.ca = (uint32_t*)(base + off); off += align_up((size_t)(c0 > 1 ? c0 : 1) * K * 4, 256);
@@ -416,16 +434,16 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
     const int groups = amax_groups(M * K);
     launch_amax_partial(x, M * K, 1, w.partial, groups, s);
     QUADS_CHECK_LAUNCH();
-    launch_scale_finalize(w.partial, groups, nullptr, 1, ts, w.table, s);
-    QUADS_CHECK_LAUNCH();
+    const bool want_scores = k > 0 || score_out != nullptr;
     const int64_t c0 = (M + kTileRows - 1) / kTileRows;
     const int64_t ctiles = (K + kP1Cols - 1) / kP1Cols;
     int64_t gx = 2048 / ctiles;
     gx = gx < 1 ? 1 : (gx > c0 ? c0 : gx);
     hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)gx, (unsigned)ctiles), dim3(256), 0, s, x, M,
-                       (int)K, ts, w.table, nib, scale, w.pa, w.ca);
+                       (int)K, w.partial, groups, ts, nib, scale,
+                       want_scores ? w.pa : nullptr, want_scores ? w.ca : nullptr);
     QUADS_CHECK_LAUNCH();
-    if (k == 0 && score_out == nullptr) {          // neither S nor the scores are wanted
+    if (!want_scores) {                            // neither S nor the scores are wanted
         launch_fill_f32(r_ts, 1, 0.0f, s);
         QUADS_CHECK_LAUNCH();
         return QUADS_OK;

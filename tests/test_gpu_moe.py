@@ -36,8 +36,11 @@ def test_pack_configs(Q, cfg):
 
 
 @pytest.mark.parametrize("t,e,topk", [(1, 1, 1), (3, 5, 2), (1000, 7, 3), (513, 4096, 8),
-                                      (2000, 1, 1)])
+                                      (2000, 1, 1), (512, 128, 8), (455, 300, 9), (513, 128, 8)])
 def test_pack_small_and_edge(Q, t, e, topk):
+    """Both packing paths: one work-group up to 4096 pairs and 512 experts
+    (512 x 8 is the largest such case, 455 x 9 has 300 experts), three
+    launches above (513 x 8; 4096 experts)."""
     rng = np.random.default_rng(t + e)
     ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
     _pack_check(Q, ids, e)
