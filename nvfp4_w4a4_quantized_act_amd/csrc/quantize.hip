@@ -3,9 +3,11 @@
 // format of its section 2.2.
 //
 // Two passes over the tensor: a partial-max pass (one value per work-group)
-// and the quantize pass, after a one-work-group step that folds the partial
-// maxima into the tensor scale and builds the per-tensor table of
-// element-code thresholds for all 127 block-scale codes.  The quantize pass
+// and the quantize pass.  The partial maxima give the tensor scale, and the
+// scale the per-tensor table of element-code thresholds for all 127
+// block-scale codes: for one activation tensor every quantize work-group
+// does this itself; for the per-expert weight tensors one work-group per
+// expert does it in a launch of its own.  The quantize pass
 // streams half-blocks: one 16-byte load per lane (a wave reads 1 KB
 // contiguous), the block maximum shared with the neighbouring lane, one
 // 4-byte nibble store, one scale byte per block.
@@ -116,16 +118,32 @@ __device__ __forceinline__ void quantize_half(const uint4 q, int64_t h, float s_
     }
 }
 
-template <bool kDq>
+// kFold: one segment with a dynamic tensor scale; every work-group folds the
+// partial maxima (`table` is then the partial-max array, `ts` the output
+// scale, written by work-group 0) and builds the code table itself, so no
+// finalize launch runs in between.  Otherwise the table and the scale come
+// from k_scale_finalize.
+template <bool kDq, bool kFold = false>
 __global__ __launch_bounds__(256) void k_quantize_bf16(
-    const uint16_t* __restrict__ x, int64_t seg_elems, const float* __restrict__ ts,
+    const uint16_t* __restrict__ x, int64_t seg_elems, float* __restrict__ ts,
     const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
-    uint16_t* __restrict__ dq) {
+    uint16_t* __restrict__ dq, int groups = 0) {
     __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
     const int seg = blockIdx.y;
-    const uint4* tg = reinterpret_cast<const uint4*>(table + (int64_t)seg * 1024);
-    for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x) s_tab[i] = tg[i];
-    const float s_t = ts[seg];
+    float s_t;
+    if (kFold) {
+        __shared__ float s_st;
+        __shared__ uint32_t s_red[4];
+        tensor_scale_prologue(table, groups, nullptr, 0, &s_st, s_red);   // groups <= 8 * 256
+        __syncthreads();
+        s_t = s_st;
+        build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(s_tab), true);
+        if (blockIdx.x == 0 && threadIdx.x == 0) ts[0] = s_t;
+    } else {
+        const uint4* tg = reinterpret_cast<const uint4*>(table + (int64_t)seg * 1024);
+        for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x) s_tab[i] = tg[i];
+        s_t = ts[seg];
+    }
     __syncthreads();
 
     const int64_t nhalf = seg_elems / 8;                      // even: whole blocks
@@ -270,10 +288,19 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     uint32_t* table = partial + align_up(kAmaxGroups * 4, 256) / 4;
     int groups = 1;
     if (!ts_in) {
+        // dynamic scale: the partial maxima, then the quantize pass folds
+        // them itself, with at most one work-group per resident slot (2048 =
+        // 8 per CU) so that the per-work-group table build is paid once
         groups = amax_groups(n);
         hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial,
                            (uint32_t*)nullptr, 0);
         QUADS_CHECK_LAUNCH();
+        const int qg = quant_grid(n / kBlock);
+        hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < 2048 ? qg : 2048, 1),
+                           dim3(256), 0, s, x, n, ts_out, partial, nib, scale, (uint16_t*)nullptr,
+                           groups);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
     }
     launch_scale_finalize(partial, groups, ts_in, 1, ts_out, table, s);
     QUADS_CHECK_LAUNCH();
