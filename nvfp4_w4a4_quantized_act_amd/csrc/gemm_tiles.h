@@ -44,15 +44,29 @@ __device__ __forceinline__ float row_scale(const GemmArgs& g, int p, float ca) {
 
 // SwiGLU's product silu(g) u = g u / (1 + e^-g), within a few 1e-6 relative
 // (half a bf16 ulp is 2^-9) wherever the result and g u are finite in fp32.
-// With a = -g log2(e): up to a = 64 the hardware exp2 and reciprocal; above
-// it 1 + 2^a rounds to 2^a in fp32, so the result is g u 2^-a, formed as
-// (g 2^(c-a) u) 2^-c with c = ceil(a), so that a gate far below -88 (where
-// 2^a overflows) still gives the small product instead of 0.
+// Short form (a = -g log2(e) <= 64, i.e. g >= -44.36): the hardware exp2 and
+// reciprocal.  Full form: with the integer c = ceil(max(a - 64, 0)),
+// g u / (1 + 2^a) = (g u / (1 + 2^(a-c))) 2^-c, since 1 + 2^a rounds to 2^a
+// in fp32 once a > 64; exp2 and the reciprocal then never overflow, and a
+// gate far below -88 still gives the small product instead of 0.  With c = 0
+// the full form gives the short form's value exactly.
+constexpr float kSiluShortMaxA = 64.0f;
+__device__ __forceinline__ float silu_a(float g) { return g * -1.4426950408889634f; }
+__device__ __forceinline__ float silu_mul_short(float g, float u) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(silu_a(g))) * u;
+}
+__device__ __forceinline__ float silu_mul_full(float g, float u) {
+    const float a = silu_a(g);
+    const float c = fminf(ceilf(fmaxf(a - kSiluShortMaxA, 0.0f)), 400.0f);   // beyond: 0
+    const float r = __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a - c));
+    return __builtin_amdgcn_ldexpf(g * r * u, -(int)c);
+}
+// Per element: a wave takes the full form only when one of its active lanes
+// needs it (the result does not depend on the neighbours).
 __device__ __forceinline__ float silu_mul(float g, float u) {
-    const float a = g * -1.4426950408889634f;
-    if (a <= 64.0f) return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(a)) * u;
-    const float c = fminf(ceilf(a), 400.0f);         // beyond 400 the result is 0
-    return __builtin_amdgcn_ldexpf(g * __builtin_amdgcn_exp2f(c - a) * u, -(int)c);
+    if (__builtin_expect(__ballot(silu_a(g) > kSiluShortMaxA) == 0ull, 1))
+        return silu_mul_short(g, u);
+    return silu_mul_full(g, u);
 }
 
 namespace v2 {
@@ -159,6 +173,52 @@ __device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int 
     return false;
 }
 
+// SwiGLU outputs of the tile: the short form everywhere (kFull false; *need
+// set when a gate needs the full form), or the full form everywhere.
+template <bool kFull>
+__device__ __forceinline__ void swiglu_store(const GemmArgs& g, const f32x16 acc[4][2], float ca,
+                                             int m0, int mend, int f0, int wm, int wn, int mact,
+                                             int lane, bool* need) {
+    const int prow_l = m0 + wm * 128 + (lane & 31);
+    const int nq = 4 * (lane >> 5);
+    bool nd = false;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        if (mi >= mact) continue;
+        const int prow = prow_l + mi * 32;
+        if (prow >= mend) continue;
+        const float ca_row = row_scale(g, prow, ca);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
+            const int feat = f0 + wn * 32 + 8 * q + nq;          // features feat .. feat + 3
+            float hv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float gt = acc[mi][0][4 * q + u] * ca_row;
+                const float up = acc[mi][1][4 * q + u] * ca_row;
+                if (kFull) {
+                    hv[u] = silu_mul_full(gt, up);
+                } else {
+                    hv[u] = silu_mul_short(gt, up);
+                    nd = nd || silu_a(gt) > kSiluShortMaxA;
+                }
+            }
+            const uint32_t p01 = pk_bf16(hv[0], hv[1]), p23 = pk_bf16(hv[2], hv[3]);
+            const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+            const int nh = g.N / 2;
+            uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
+            if (feat + 3 < nh && (nh & 3) == 0) {
+                *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (feat + u < nh) o[u] = (uint16_t)hb[u];
+            }
+        }
+    }
+    *need = nd;
+}
+
 // Epilogue of a 256 x 256 tile: acc scaled by ca; SwiGLU to bf16 or plain
 // fp32 / bf16 stores, four consecutive features per lane.
 template <int kEpi>
@@ -166,6 +226,15 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
                                          int m0, int mend, int f0, int wm, int wn, int mact,
                                          int lane) {
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    if (swiglu) {
+        // rare: a gate below -44.36 somewhere in the wave's tile -- the same
+        // outputs again with the full form (equal values elsewhere)
+        bool need;
+        swiglu_store<false>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need);
+        if (__ballot(need) != 0ull)
+            swiglu_store<true>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need);
+        return;
+    }
     const int prow_l = m0 + wm * 128 + (lane & 31);
     const int nq = 4 * (lane >> 5);
 #pragma unroll
@@ -176,27 +245,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
         const float ca_row = row_scale(g, prow, ca);
 #pragma unroll
         for (int q = 0; q < 4; ++q) {                 // registers 4q .. 4q + 3
-            if (swiglu) {
-                const int feat = f0 + wn * 32 + 8 * q + nq;      // features feat .. feat + 3
-                float hv[4];
-#pragma unroll
-                for (int u = 0; u < 4; ++u) {
-                    const float gt = acc[mi][0][4 * q + u] * ca_row;
-                    const float up = acc[mi][1][4 * q + u] * ca_row;
-                    hv[u] = silu_mul(gt, up);
-                }
-                const uint32_t p01 = pk_bf16(hv[0], hv[1]), p23 = pk_bf16(hv[2], hv[3]);
-                const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
-                const int nh = g.N / 2;
-                uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
-                if (feat + 3 < nh && (nh & 3) == 0) {
-                    *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
-                } else {
-#pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        if (feat + u < nh) o[u] = (uint16_t)hb[u];
-                }
-            } else {
+            {
 #pragma unroll
                 for (int nj = 0; nj < 2; ++nj) {
                     const int n = f0 + wn * 64 + nj * 32 + 8 * q + nq;  // features n .. n + 3
