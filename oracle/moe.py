@@ -55,7 +55,10 @@ def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
           is a scalar, or an array [Ta] of per-row (per-token) scales, in
           which case packed row p takes s_tA[row(p)] (compensation: k = 0)
     r   = (packed [Ta, k/2], scales [Ta, k/16], s_tR) or None   second pass
-    sel = int array [k] of selected channels (ascending)
+    sel = int array [k] of selected channels (ascending), shared by every
+          expert; or [E, k] with s_tR an array [E]: one selection and one
+          residual tensor scale per expert (rac_quantize_experts; the rows
+          are then the packed rows, row_token None)
     w   = (packed [E, N, K/2], scales [E, N, K/16], s_tW [E])   weights
     offsets [E+1]: packed rows of expert e are offsets[e] .. offsets[e+1]-1
     row_token [rows] or None: activation row feeding each packed row
@@ -69,17 +72,21 @@ def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
     e_count = len(offsets) - 1
     rows = int(offsets[-1])
     n = w_nib.shape[1]
+    sel_arr = None if r is None else np.asarray(sel, dtype=np.int64)
+    per_expert = sel_arr is not None and sel_arr.ndim == 2
+    if per_expert and row_token is not None:
+        raise ValueError("per-expert selection needs activations in packed order")
     if row_token is None:
         row_token = np.arange(rows)
     row_token = np.asarray(row_token, dtype=np.int64)
-    k = 0 if r is None else len(sel)
+    k = 0 if r is None else sel_arr.shape[-1]
     y = np.zeros((rows, n), dtype=np.float64)
     bound = np.zeros((rows, n), dtype=np.float64) if want_bound else None
     sa_arr = np.asarray(a_ts, dtype=np.float32).astype(np.float64)
     per_row = sa_arr.ndim > 0
     if per_row and k:
         raise ValueError("per-row activation scales take no compensation term")
-    sr = np.float64(np.float32(r[2])) if k else 0.0
+    sr_arr = np.asarray(r[2], dtype=np.float32).astype(np.float64) if k else None
     for e in range(e_count):
         p0, p1 = int(offsets[e]), int(offsets[e + 1])
         if p1 == p0:
@@ -94,7 +101,8 @@ def grouped_gemm(a, r, sel, w, offsets, row_token=None, want_bound=True):
             bound[p0:p1] = (sa * sw) * (np.abs(ah) @ np.abs(wh).T)
         if k:
             rh = dequantize_unscaled(r[0][src], r[1][src])            # [m, k]
-            ws = wh[:, np.asarray(sel, dtype=np.int64)]               # [N, k]
+            ws = wh[:, sel_arr[e] if per_expert else sel_arr]         # [N, k]
+            sr = sr_arr[e] if per_expert else sr_arr
             y[p0:p1] += (sr * sw) * (rh @ ws.T)
             if want_bound:
                 bound[p0:p1] += (sr * sw) * (np.abs(rh) @ np.abs(ws).T)

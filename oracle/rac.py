@@ -110,3 +110,59 @@ def compensated(out, kdim):
     if len(out["sel"]):
         xt[:, out["sel"]] += dequantize(out["r_nib"], out["r_scale"], out["r_ts"])
     return xt
+
+
+def rac_quantize_experts(x, k, offsets):
+    """RAC with one channel selection per expert (a variant; the pages select
+    "more adaptive" residual channels as future work): for packed activation
+    rows x [rows, K] whose expert e owns rows offsets[e] .. offsets[e+1]-1.
+
+    Reading: the main NVFP4 of the whole tensor and the residual r are those
+    of rac_quantize (one tensor scale); then every expert's rows are treated
+    as a tensor of their own for Eq. (23)-(24) and the second pass: scores
+    by the same fixed-order tree over that expert's rows alone, S_e the k
+    best (ties to the lower index), and r[rows_e][:, S_e] quantized with its
+    own dynamic tensor scale.  An expert without rows gets scores 0, so
+    S_e = 0 .. k-1, and s_tR[e] = 0.
+
+    Returns nib/scale/ts, r, score [E, K], sel [E, k], r_nib [rows, k/2],
+    r_scale [rows, k/16] (row p in its expert's S_e order), r_ts [E].
+    """
+    x = np.asarray(x, dtype=np.float64)
+    rows, kdim = x.shape
+    offsets = np.asarray(offsets, dtype=np.int64)
+    if k % 16 or not 0 <= k <= kdim:
+        raise ValueError("k must be a multiple of 16 in [0, K]")
+    if offsets[0] != 0 or offsets[-1] != rows or np.any(np.diff(offsets) < 0):
+        raise ValueError("offsets must run from 0 to rows, non-decreasing")
+    e_count = len(offsets) - 1
+    nib, scale, ts = quantize(x)
+    r = residual(x, nib, scale, ts)
+    score = np.zeros((e_count, kdim))
+    sel = np.zeros((e_count, k), dtype=np.int32)
+    r_nib = np.zeros((rows, k // 2), dtype=np.uint8)
+    r_scale = np.zeros((rows, k // 16), dtype=np.uint8)
+    r_ts = np.zeros(e_count, dtype=np.float32)
+    for e in range(e_count):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        score[e] = channel_scores(r[p0:p1])
+        sel[e] = select_channels(score[e], k)
+        if p1 > p0 and k:
+            r_nib[p0:p1], r_scale[p0:p1], r_ts[e] = quantize(
+                r[p0:p1][:, sel[e]].astype(np.float64))
+    return dict(nib=nib, scale=scale, ts=ts, r=r, score=score, sel=sel,
+                r_nib=r_nib, r_scale=r_scale, r_ts=r_ts)
+
+
+def compensated_experts(out, offsets):
+    """X~ of Eq. (21) per expert (fp64): DQ(Q(x)), plus on each expert's rows
+    the dequantized second pass scattered onto its S_e."""
+    xt = dequantize(out["nib"], out["scale"], out["ts"])
+    offsets = np.asarray(offsets, dtype=np.int64)
+    for e in range(len(offsets) - 1):
+        p0, p1 = int(offsets[e]), int(offsets[e + 1])
+        if p1 > p0 and out["sel"].shape[1]:
+            xt[p0:p1][:, out["sel"][e]] += dequantize(out["r_nib"][p0:p1], out["r_scale"][p0:p1],
+                                                      out["r_ts"][e])
+    return xt
+
