@@ -315,6 +315,7 @@ def main():
     decode = decode_layer(np, torch, Q, synth, dev, w13q, w2q)
     comparator = mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx,
                                per_op["gemm_gate_up_swiglu"], fl_gu)
+    per_expert = per_expert_down(torch, Q, x, ids, E, I, H, KR, rows, w13q, w2q)
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -352,9 +353,52 @@ def main():
         "quantizer": quant,
         "comparator": comparator,
         "decode": decode,
+        "per_expert_selection": per_expert,
         "weight_qdq_ms": weight_qdq_ms,
     }
     print(json.dumps(line), flush=True)
+
+
+def per_expert_down(torch, Q, x, ids, E, I, H, KR, rows, w13q, w2q, reps=20):
+    """The variant with one channel selection per expert, at the layer's down
+    site (the packed [32768, 768] SwiGLU output, 128 experts, k = 64): RAC
+    and the down GEMM with per-expert compensation, each timed over `reps`
+    back-to-back calls beside the shared-selection calls on the same input."""
+    a = Q.quads_rac_quantize(x, KR)
+    off, rt, pos = Q.quads_moe_pack(ids, E)
+    h = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), w13q, 2 * I, rows=rows,
+                              r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"], offsets=off,
+                              row_token=rt, epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+    keep = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        for _ in range(reps):
+            fn()
+        ev[1].record()
+        torch.cuda.synchronize()
+        return ev[0].elapsed_time(ev[1]) / reps
+
+    def rac_shared():
+        keep["b"] = Q.quads_rac_quantize(h, KR)
+
+    def rac_experts():
+        keep["be"] = Q.quads_rac_quantize_experts(h, KR, off)
+
+    ms = {"rac_shared_ms": timed(rac_shared), "rac_per_expert_ms": timed(rac_experts)}
+    b, be = keep["b"], keep["be"]
+    ms["gemm_down_shared_ms"] = timed(lambda: Q.quads_moe_w4a4_gemm(
+        (b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
+        r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"], offsets=off,
+        out_dtype=Q.OUT_BF16))
+    ms["gemm_down_per_expert_ms"] = timed(lambda: Q.quads_moe_w4a4_gemm_sel_experts(
+        (be["nib"], be["scale"], be["ts"]), w2q, H, r=(be["r_nib"], be["r_scale"], be["r_ts"]),
+        sel=be["sel"], offsets=off, out_dtype=Q.OUT_BF16))
+    ms["site"] = "down projection input: 32768 packed rows x 768, 128 experts, k = 64"
+    return ms
 
 
 def quantizer_rate(np, torch, Q, synth, dev, reps=20):

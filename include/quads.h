@@ -125,6 +125,30 @@ int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
                        double* score_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * RAC with one channel selection per expert (a variant of section 3.3; the
+ * paper lists more adaptive residual-channel selection as future work), for
+ * activations already in packed expert order (the down-projection input).
+ * The main NVFP4 (nib, scale, ts) is that of quads_rac_quantize.  Expert e's
+ * rows offsets[e] .. offsets[e+1]-1 are then a tensor of their own for the
+ * scores (the same fixed-order sum over its rows alone), the selection S_e
+ * (k largest, ties to the lower index, ascending) and the second pass of
+ * r[rows_e][:, S_e] with its own dynamic tensor scale.  An expert without
+ * rows gets S_e = 0 .. k-1 and a residual scale of 0.
+ *   x        bf16 [M, K] in packed order, M <= 64^3, K % 16 == 0, K <= 8192;
+ *            E <= 4096
+ *   offsets  int32 [E+1], offsets[0] = 0, offsets[E] = M, non-decreasing
+ *   sel      out int32 [E, k];  r_ts out fp32 [E]
+ *   r_nib, r_scale  out [M, k/2], [M, k/16]: row p in its expert's S_e order
+ *   score_out  NULL or out fp64 [E, K]
+ */
+size_t quads_rac_quantize_experts_ws(int64_t M, int64_t K, int32_t k, int32_t E);
+int quads_rac_quantize_experts(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                               const int32_t* offsets, int32_t E,
+                               uint8_t* nib, uint8_t* scale, float* ts,
+                               int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                               double* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
  * Shared NVFP4 weight QDQ, Q_W of Eq. (7) / QDQ_W of Eq. (12): each expert
  * matrix W_e [N, K] (rows = output features, blocks along K) is quantized
  * with its own dynamic tensor scale.
@@ -200,6 +224,24 @@ int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t* a_scale,
                                  const int32_t* offsets, int32_t E, int64_t N,
                                  int epilogue, int out_dtype, void* out,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped W4A4 GEMM with the per-expert compensation of
+ * quads_rac_quantize_experts: packed row p of expert e takes
+ *   s_tR[e] s_tW[e] sum_{i<k} r[p, i] w_e[n, sel[e, i]]
+ * as its second term.  Activations in packed order (no row_token; row p is
+ * activation row p); sel int32 [E, k], each row strictly ascending in
+ * [0, K); r_ts fp32 [E]; offsets required.  Everything else as in
+ * quads_moe_w4a4_gemm (same workspace query).
+ */
+int quads_moe_w4a4_gemm_sel_experts(const uint8_t* a_nib, const uint8_t* a_scale,
+                                    const float* a_ts, int64_t rows, int64_t K,
+                                    const uint8_t* r_nib, const uint8_t* r_scale,
+                                    const float* r_ts, const int32_t* sel, int32_t k,
+                                    const uint8_t* w_nib, const uint8_t* w_scale,
+                                    const float* w_ts, const int32_t* offsets, int32_t E,
+                                    int64_t N, int epilogue, int out_dtype, void* out,
+                                    void* ws, size_t ws_bytes, void* stream);
 
 /*
  * MoE combine: out[t, n] = sum over slots in order of topk_w[t, slot] *

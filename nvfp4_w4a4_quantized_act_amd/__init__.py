@@ -17,6 +17,7 @@ import torch
 __all__ = [
     "QuadsError", "lib", "library_path",
     "quads_nvfp4_quantize", "quads_nvfp4_quantize_rows", "quads_rac_quantize",
+    "quads_rac_quantize_experts", "quads_moe_w4a4_gemm_sel_experts",
     "quads_nvfp4_weight_qdq", "quads_moe_pack", "quads_moe_w4a4_gemm",
     "quads_moe_w4a4_gemm_rowscale", "quads_moe_combine",
     "quads_mx_quantize", "quads_moe_mx_gemm",
@@ -44,6 +45,13 @@ _SIGNATURES = {
     "quads_rac_quantize_ws": (_SZ, [_I64, _I64, _I32]),
     "quads_rac_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _SZ, _P]),
+    "quads_rac_quantize_experts_ws": (_SZ, [_I64, _I64, _I32, _I32]),
+    "quads_rac_quantize_experts": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P,
+                                                  _P, _P, _P, _P, _P, _SZ, _P]),
+    "quads_moe_w4a4_gemm_sel_experts": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _P,
+                                                       _I32, _P, _P, _P, _P, _I32, _I64,
+                                                       ctypes.c_int, ctypes.c_int, _P, _P, _SZ,
+                                                       _P]),
     "quads_nvfp4_weight_qdq_ws": (_SZ, [_I64, _I64, _I64]),
     "quads_nvfp4_weight_qdq": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ,
                                               _P]),
@@ -167,6 +175,34 @@ def quads_rac_quantize(x, k, want_score=False):
     return out
 
 
+def quads_rac_quantize_experts(x, k, offsets, want_score=False):
+    """RAC with one selection per expert on packed bf16 x [M, K] (offsets int32
+    [E+1] on the device).  Returns a dict like quads_rac_quantize, with sel
+    [E, k], r_ts [E] and score [E, K]."""
+    x = _bits16(x)
+    m, kd = x.shape
+    e = offsets.shape[0] - 1
+    dev = x.device
+    out = {
+        "nib": torch.empty((m, kd // 2), dtype=torch.uint8, device=dev),
+        "scale": torch.empty((m, kd // 16), dtype=torch.uint8, device=dev),
+        "ts": torch.empty(4, dtype=torch.float32, device=dev)[:1],
+        "sel": torch.empty((e, k), dtype=torch.int32, device=dev),
+        "r_nib": torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+        "r_scale": torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
+        "r_ts": torch.empty(e, dtype=torch.float32, device=dev),
+    }
+    if want_score:
+        out["score"] = torch.empty((e, kd), dtype=torch.float64, device=dev)
+    ws, nws = _ws(lib().quads_rac_quantize_experts_ws(m, kd, k, e), dev)
+    _check("quads_rac_quantize_experts", lib().quads_rac_quantize_experts(
+        _ptr(x), m, kd, k, _ptr(offsets), e, _ptr(out["nib"]), _ptr(out["scale"]),
+        _ptr(out["ts"]), _ptr(out["sel"]) if k else None, _ptr(out["r_nib"]) if k else None,
+        _ptr(out["r_scale"]) if k else None, _ptr(out["r_ts"]), _ptr(out.get("score")),
+        _ptr(ws), nws, _stream(dev)))
+    return out
+
+
 def quads_nvfp4_weight_qdq(w, want_dq=False):
     """Weight QDQ of bf16 w [E, N, K] -> (nib, scale, ts [E], dq bf16 bits or None)."""
     w = _bits16(w)
@@ -245,6 +281,31 @@ def quads_moe_w4a4_gemm_rowscale(a, w, n, rows=None, offsets=None, row_token=Non
     ws, nws = _ws(lib().quads_moe_w4a4_gemm_ws(rows, kd, 0, e, n), dev)
     _check("quads_moe_w4a4_gemm_rowscale", lib().quads_moe_w4a4_gemm_rowscale(
         _ptr(a_nib), _ptr(a_scale), _ptr(a_ts), _ptr(row_token), rows, kd, _ptr(w_nib),
+        _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e, n, epilogue, out_dtype, _ptr(out),
+        _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def quads_moe_w4a4_gemm_sel_experts(a, w, n, r, sel, offsets, epilogue=EPI_NONE,
+                                    out_dtype=OUT_F32, out=None):
+    """Grouped W4A4 GEMM with per-expert compensation: a = (nib, scale, ts) in
+    packed order, r = (nib, scale, ts [E]), sel [E, k] (quads_rac_quantize_experts)."""
+    a_nib, a_scale, a_ts = a
+    w_nib, w_scale, w_ts = w
+    e = w_nib.shape[0]
+    kd = a_nib.shape[1] * 2
+    rows = a_nib.shape[0]
+    k = int(sel.shape[1])
+    dev = a_nib.device
+    ncols = n // 2 if epilogue == EPI_SWIGLU else n
+    if out is None:
+        dt = torch.float32 if out_dtype == OUT_F32 else torch.int16
+        out = torch.empty((rows, ncols), dtype=dt, device=dev)
+    ws, nws = _ws(lib().quads_moe_w4a4_gemm_ws(rows, kd, k, e, n), dev)
+    rn, rs, rt = r
+    _check("quads_moe_w4a4_gemm_sel_experts", lib().quads_moe_w4a4_gemm_sel_experts(
+        _ptr(a_nib), _ptr(a_scale), _ptr(a_ts), rows, kd, _ptr(rn) if k else None,
+        _ptr(rs) if k else None, _ptr(rt), _ptr(sel) if k else None, k, _ptr(w_nib),
         _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e, n, epilogue, out_dtype, _ptr(out),
         _ptr(ws), nws, _stream(dev)))
     return out

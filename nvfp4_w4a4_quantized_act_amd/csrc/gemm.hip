@@ -165,6 +165,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     if (!find_tile_bm(g.offsets, g.E, g.rows, blockIdx.y, kBM, s_scan, s_res, &e, &m0, &mend,
                       g.dec_rows))
         return;
+    bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
 
@@ -569,6 +570,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
     if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows)) return;
+    bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -657,7 +659,8 @@ extern "C" size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int
 // Both entry points: a_ts_rows is null (one tensor scale a_ts[0]) or the
 // per-row scales [Ta] (then a_ts == a_ts_rows and k == 0).
 static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
-                     const float* a_ts_rows, const int32_t* row_token, int64_t rows, int64_t K,
+                     const float* a_ts_rows, int sel_per_expert, const int32_t* row_token,
+                     int64_t rows, int64_t K,
                      const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
                      const int32_t* sel, int32_t k, const uint8_t* w_nib,
                      const uint8_t* w_scale, const float* w_ts, const int32_t* offsets,
@@ -683,7 +686,7 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
-               out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows};
+               out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows, sel_per_expert};
     hipStream_t st = (hipStream_t)stream;
     if (gemm_decode_fits(g)) {
         // few rows per expert: the decode kernel takes every expert with at
@@ -733,7 +736,7 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
                                    const float* w_ts, const int32_t* offsets, int32_t E,
                                    int64_t N, int epilogue, int out_dtype, void* out, void* ws,
                                    size_t ws_bytes, void* stream) {
-    return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, row_token, rows, K, r_nib, r_scale, r_ts,
+    return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 0, row_token, rows, K, r_nib, r_scale, r_ts,
                      sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out, ws,
                      ws_bytes, stream);
 }
@@ -746,7 +749,23 @@ extern "C" int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t*
                                             int epilogue, int out_dtype, void* out, void* ws,
                                             size_t ws_bytes, void* stream) {
     if (!ok_ptr(a_ts_rows)) return QUADS_EINVAL;
-    return gemm_w4a4(a_nib, a_scale, a_ts_rows, a_ts_rows, row_token, rows, K, nullptr, nullptr,
+    return gemm_w4a4(a_nib, a_scale, a_ts_rows, a_ts_rows, 0, row_token, rows, K, nullptr, nullptr,
                      nullptr, nullptr, 0, w_nib, w_scale, w_ts, offsets, E, N, epilogue,
                      out_dtype, out, ws, ws_bytes, stream);
+}
+
+extern "C" int quads_moe_w4a4_gemm_sel_experts(const uint8_t* a_nib, const uint8_t* a_scale,
+                                               const float* a_ts, int64_t rows, int64_t K,
+                                               const uint8_t* r_nib, const uint8_t* r_scale,
+                                               const float* r_ts, const int32_t* sel, int32_t k,
+                                               const uint8_t* w_nib, const uint8_t* w_scale,
+                                               const float* w_ts, const int32_t* offsets,
+                                               int32_t E, int64_t N, int epilogue,
+                                               int out_dtype, void* out, void* ws,
+                                               size_t ws_bytes, void* stream) {
+    if (!ok_ptr(offsets)) return QUADS_EINVAL;
+    if (k > 0 && !ok_ptr(r_ts)) return QUADS_EINVAL;
+    return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 1, nullptr, rows, K, r_nib, r_scale, r_ts,
+                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out, ws,
+                     ws_bytes, stream);
 }

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     }
     if (cnt <= 0 || cnt > g.dec_rows) return;        // uniform: no rows (no weight reads),
                                                       // or the tiled kernel's expert
+    bind_expert(g, e);
 
     // the wave index as a scalar, so that every branch on it is uniform
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);

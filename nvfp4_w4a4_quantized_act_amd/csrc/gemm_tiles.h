@@ -25,7 +25,21 @@ struct GemmArgs {
     // row_token), or null for the single tensor scale a_ts[0].  Only with
     // k == 0.
     const float* a_ts_rows;
+    // 1: sel is [E, k] and r_ts [E], one selection and residual scale per
+    // expert (activations in packed order); 0: one shared sel [k], r_ts [1].
+    int sel_per_expert;
 };
+
+// Once a work-group knows its expert e: point sel and r_ts at that expert's
+// selection and residual scale, so that the kernels read g.sel[i] and
+// g.r_ts[0] either way.
+__device__ __forceinline__ void bind_expert(GemmArgs& g, int e) {
+    if (g.sel_per_expert) {
+        g.sel += (int64_t)e * g.k;
+        g.r_ts += e;
+        g.sel_per_expert = 0;
+    }
+}
 
 // The activation tensor scale that multiplies a packed row's output: the
 // tensor's, or (per-row scales) 1, the row's own scale being applied in the

@@ -207,6 +207,15 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     __shared__ uint32_t s_amax[16];
     __shared__ float s_rts;
     const int tid = threadIdx.x;
+    {   // work-group b selects for expert b (one work-group: the shared selection)
+        const int64_t b = blockIdx.x;
+        score += b * nrows * (int64_t)K;
+        colmax += b * nrows * (int64_t)K;
+        sel += b * k;
+        r_ts += b;
+        if (score_out) score_out += b * (int64_t)K;
+        r_table += b * 1024;
+    }
     // the last level of the fixed-order tree: nrows (<= kSelectFold) partial
     // rows summed in order from +0
     for (int j = tid; j < K; j += 1024) {
@@ -364,6 +373,193 @@ __global__ __launch_bounds__(256) void k_rac_pass2(
     }
 }
 
+// ------------------------------------------------------ per-expert S --
+// Expert e's rows split into chunks of 64 from its first row (the tree's
+// level-0 groups); chunk_start[e] = sum over e' < e of ceil(rows_e' / 64).
+constexpr int64_t kExpertMaxRows = (int64_t)kScoreFanin * kScoreFanin * kScoreFanin;
+constexpr int kExpertMaxE = 4096;          // chunk starts kept in LDS
+
+// Level-0 partials of every chunk: work-group (x, slice) takes chunks x,
+// x + gridDim.x, ...; thread = channel; r recomputed from x and the main
+// NVFP4 exactly as pass 1 forms it, 16 rows loaded at a time, summed in row
+// order from +0.  Work-group (0, 0) also writes chunk_start.
+__global__ __launch_bounds__(256) void k_rac_expert_partials(
+    const uint16_t* __restrict__ x, int K, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ scale, const float* __restrict__ ts,
+    const int32_t* __restrict__ offsets, int E, double* __restrict__ part,
+    uint32_t* __restrict__ pmax, int32_t* __restrict__ chunk_start) {
+    __shared__ int s_cs[kExpertMaxE + 1];
+    __shared__ int s_w[4];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    // chunk starts: each thread a run of experts, then a scan over the block
+    const int per = (E + 255) / 256;
+    const int e0 = tid * per, e1 = e0 + per < E ? e0 + per : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + kTileRows - 1) / kTileRows;
+    int xs = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(xs, off, 64);
+        if (lane >= off) xs += y;
+    }
+    if (lane == 63) s_w[wid] = xs;
+    __syncthreads();
+    int run = xs - local;
+    for (int w = 0; w < wid; ++w) run += s_w[w];
+    for (int e = e0; e < e1; ++e) {
+        s_cs[e] = run;
+        run += (offsets[e + 1] - offsets[e] + kTileRows - 1) / kTileRows;
+    }
+    if (tid == 255) s_cs[E] = run;                     // thread 255 ends at the total
+    __syncthreads();
+    if (blockIdx.x == 0 && blockIdx.y == 0)
+        for (int e = tid; e <= E; e += 256) chunk_start[e] = s_cs[e];
+    const int nchunks = s_cs[E];
+    const int c = blockIdx.y * 256 + tid;
+    const float s_t = ts[0];
+    for (int ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
+        int lo = 0, hi = E;                           // s_cs[lo] <= ch < s_cs[lo + 1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_cs[mid] <= ch) lo = mid; else hi = mid;
+        }
+        const int64_t row0 = offsets[lo] + (int64_t)(ch - s_cs[lo]) * kTileRows;
+        const int64_t rend = offsets[lo + 1];
+        const int nr = (int)(rend - row0 < kTileRows ? rend - row0 : kTileRows);
+        if (c >= K) continue;
+        double acc = 0.0;
+        uint32_t m = 0;
+        for (int b = 0; b < nr; b += 16) {             // 16 rows in flight, loads first
+            uint32_t xv[16], cv[16], sv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int64_t p = row0 + (b + u < nr ? b + u : nr - 1);
+                xv[u] = x[p * K + c];
+                cv[u] = nib[p * (K / 2) + (c >> 1)];
+                sv[u] = scale[p * (K / kBlock) + (c >> 4)];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (b + u < nr) {
+                    const uint32_t code = (cv[u] >> (4 * (c & 1))) & 0xFu;
+                    float v = e2m1_value(code & 7u);
+                    if (code & 8u) v = -v;
+                    const float r = fmaf(-(v * e4m3_value(sv[u])), s_t, bf16_to_f32(xv[u]));
+                    const double rd = (double)r;
+                    acc = acc + rd * rd;                  // r^2 exact in fp64, row order
+                    const uint32_t ab = __float_as_uint(r) & 0x7FFFFFFFu;
+                    m = ab > m ? ab : m;
+                }
+            }
+        }
+        part[(int64_t)ch * K + c] = acc;
+        pmax[(int64_t)ch * K + c] = m;
+    }
+}
+
+// Scores of expert e from its chunk partials, work-group (slice, e), thread
+// = channel: the tree's upper levels streamed -- acc1 sums the chunk partials
+// of the current level-1 node in order from +0, acc2 the finished level-1
+// nodes (at most 64^2 chunks per expert).
+__global__ __launch_bounds__(256) void k_rac_expert_scores(
+    const double* __restrict__ part, const uint32_t* __restrict__ pmax,
+    const int32_t* __restrict__ chunk_start, int K, double* __restrict__ score,
+    uint32_t* __restrict__ colmax) {
+    const int e = blockIdx.y;
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= K) return;                               // no barriers below
+    const int q0 = chunk_start[e], q1 = chunk_start[e + 1];
+    double acc1 = 0.0, acc2 = 0.0;
+    int n1 = 0, n2 = 0;
+    uint32_t m = 0;
+    for (int q = q0; q < q1; q += 16) {
+        double v[16];
+        uint32_t u[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {                   // loads first, then the chain
+            const int qq = q + i < q1 ? q + i : q1 - 1;
+            v[i] = part[(int64_t)qq * K + c];
+            u[i] = pmax[(int64_t)qq * K + c];
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (q + i >= q1) break;
+            acc1 = acc1 + v[i];
+            m = u[i] > m ? u[i] : m;
+            if (++n1 == kScoreFanin) {                    // a level-1 node is done
+                acc2 = acc2 + acc1;
+                acc1 = 0.0;
+                n1 = 0;
+                ++n2;
+            }
+        }
+    }
+    // at most 64 chunks: their in-order sum (acc1, or acc2 when exactly 64
+    // were pushed up); more: the in-order sum of the level-1 nodes
+    const double sc = n2 == 0 ? acc1 : (n1 > 0 ? acc2 + acc1 : acc2);
+    score[(int64_t)e * K + c] = sc;
+    colmax[(int64_t)e * K + c] = m;
+}
+
+// Second pass with per-expert S: one thread per residual element (row, i);
+// the row's expert by binary search in offsets; as k_rac_pass2 otherwise,
+// with the expert's selection, residual scale and code table.
+__global__ __launch_bounds__(256) void k_rac_pass2_experts(
+    const uint16_t* __restrict__ x, int64_t M, int K, const int32_t* __restrict__ sel, int k,
+    const int32_t* __restrict__ offsets, int E, const uint8_t* __restrict__ nib,
+    const uint8_t* __restrict__ scale, const float* __restrict__ ts,
+    const float* __restrict__ r_ts, const uint32_t* __restrict__ r_table,
+    uint8_t* __restrict__ r_nib, uint8_t* __restrict__ r_scale) {
+    const float s_t = ts[0];
+    const int64_t n = M * k;                       // k % 16 == 0: blocks never straddle
+    for (int64_t base = (int64_t)blockIdx.x * blockDim.x; base < n;
+         base += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t t = base + threadIdx.x;
+        const bool live = t < n;                       // uniform over each 16-lane block
+        const int64_t row = live ? t / k : 0;
+        const int i = (int)(t - row * k);
+        int lo = 0, hi = E;                            // expert: offsets[e] <= row < offsets[e+1]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (offsets[mid] <= row) lo = mid; else hi = mid;
+        }
+        const int e = lo;
+        float r = 0.0f;
+        if (live) {
+            const int j = sel[(int64_t)e * k + i];
+            const uint32_t h = x[row * K + j];
+            const uint32_t code = (nib[row * (K / 2) + (j >> 1)] >> (4 * (j & 1))) & 0xFu;
+            float sv = e2m1_value(code & 7u) * e4m3_value(scale[row * (K / kBlock) + (j >> 4)]);
+            if (code & 8u) sv = -sv;
+            r = fmaf(-sv, s_t, bf16_to_f32(h));
+        }
+        const float s_tr = r_ts[e];
+        const uint32_t rb = __float_as_uint(r);
+        uint32_t am = rb & 0x7FFFFFFFu;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            const uint32_t o = __shfl_xor(am, off, 16);
+            am = o > am ? o : am;
+        }
+        const uint32_t sb = s_tr > 0.0f ? e4m3_rne_code((double)__uint_as_float(am) /
+                                                        (6.0 * (double)s_tr))
+                                        : 0u;
+        const uint32_t* tr = r_table + (int64_t)e * 1024 + 8 * sb;
+        const uint32_t thr[7] = {tr[0], tr[1], tr[2], tr[3], tr[4], tr[5], tr[6]};
+        const uint32_t c = e2m1_mag_code(rb & 0x7FFFFFFFu, thr) | ((rb >> 28) & 8u);
+        const uint32_t other = __shfl_xor(c, 1, 16);
+        if (live) {
+            if ((t & 1) == 0) r_nib[t >> 1] = (uint8_t)(c | (other << 4));
+            if ((t & 15) == 0) r_scale[t >> 4] = (uint8_t)sb;
+        }
+    }
+}
+
+__global__ void k_iota_experts(int32_t* p, int n, int k) {
+    int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) p[i] = i % k;
+}
+
 __global__ void k_iota_i32(int32_t* p, int n) {
     int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) p[i] = i;
@@ -477,3 +673,106 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
     }
     return QUADS_OK;
 }
+
+// Per-expert selection: workspace = partial maxima, scores [E, K] (fp64),
+// per-channel maxima [E, K], code tables [E, 1024], chunk starts [E + 1],
+// chunk partials [chunks, K] (fp64) and their maxima [chunks, K], with at
+// most M / 64 + E chunks.
+struct RacExpertWs {
+    uint32_t* partial;
+    double* score;
+    uint32_t* cmax;
+    uint32_t* tables;
+    int32_t* chunk_start;
+    double* part;
+    uint32_t* pmax;
+    size_t bytes;
+};
+
+static RacExpertWs rac_experts_ws_layout(char* base, int64_t M, int64_t K, int64_t E) {
+    const int64_t nch = M / kTileRows + E;
+    RacExpertWs w;
+    size_t off = 0;
+    w.partial = (uint32_t*)(base + off); off += align_up(kAmaxGroups * 4, 256);
+    w.score = (double*)(base + off); off += align_up((size_t)E * K * 8, 256);
+    w.cmax = (uint32_t*)(base + off); off += align_up((size_t)E * K * 4, 256);
+    w.tables = (uint32_t*)(base + off); off += align_up((size_t)E * 1024 * 4, 256);
+    w.chunk_start = (int32_t*)(base + off); off += align_up((size_t)(E + 1) * 4, 256);
+    w.part = (double*)(base + off); off += align_up((size_t)nch * K * 8, 256);
+    w.pmax = (uint32_t*)(base + off); off += align_up((size_t)nch * K * 4, 256);
+    w.bytes = off;
+    return w;
+}
+
+extern "C" size_t quads_rac_quantize_experts_ws(int64_t M, int64_t K, int32_t k, int32_t E) {
+    (void)k;
+    if (M < 0 || K <= 0 || E < 1) return 0;
+    return rac_experts_ws_layout(nullptr, M, K, E).bytes;
+}
+
+extern "C" int quads_rac_quantize_experts(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                          const int32_t* offsets, int32_t E, uint8_t* nib,
+                                          uint8_t* scale, float* ts, int32_t* sel,
+                                          uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                                          double* score_out, void* ws, size_t ws_bytes,
+                                          void* stream) {
+    if (M < 0 || M > kExpertMaxRows || K <= 0 || K % kBlock || K > kRacMaxK) return QUADS_ESHAPE;
+    if (k < 0 || k % kBlock || k > K || E < 1 || E > kExpertMaxE) return QUADS_ESHAPE;
+    if (!ok_ptr(ts) || !ok_ptr(r_ts) || !ok_ptr(offsets) || !ok_opt_ptr(score_out))
+        return QUADS_EINVAL;
+    if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale))) return QUADS_EINVAL;
+    if (k > 0 && !ok_ptr(sel)) return QUADS_EINVAL;
+    if (k > 0 && M > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale))) return QUADS_EINVAL;
+    if (ws_bytes < quads_rac_quantize_experts_ws(M, K, k, E) || !ok_ptr(ws))
+        return QUADS_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        launch_fill_f32(ts, 1, 0.0f, s);
+        launch_fill_f32(r_ts, E, 0.0f, s);
+        if (k > 0)
+            hipLaunchKernelGGL(k_iota_experts, dim3((unsigned)(((int64_t)E * k + 255) / 256)),
+                               dim3(256), 0, s, sel, (int)(E * k), (int)k);
+        if (score_out)
+            hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((E * K + 255) / 256)), dim3(256), 0, s,
+                               score_out, (int)(E * K), 0.0);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    const RacExpertWs w = rac_experts_ws_layout(static_cast<char*>(ws), M, K, E);
+    uint32_t* partial = w.partial;
+    const int groups = amax_groups(M * K);
+    launch_amax_partial(x, M * K, 1, partial, groups, s);
+    QUADS_CHECK_LAUNCH();
+    const int64_t c0 = (M + kTileRows - 1) / kTileRows;
+    const int64_t ctiles = (K + kP1Cols - 1) / kP1Cols;
+    int64_t gx = 2048 / ctiles;
+    gx = gx < 1 ? 1 : (gx > c0 ? c0 : gx);
+    hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)gx, (unsigned)ctiles), dim3(256), 0, s, x, M,
+                       (int)K, partial, groups, ts, nib, scale, (double*)nullptr,
+                       (uint32_t*)nullptr);
+    QUADS_CHECK_LAUNCH();
+    int64_t gp = 2048 / ctiles;                     // chunk partials: at most M / 64 + E chunks
+    const int64_t nch = M / kTileRows + E;
+    gp = gp < 1 ? 1 : (gp > nch ? nch : gp);
+    hipLaunchKernelGGL(k_rac_expert_partials, dim3((unsigned)gp, (unsigned)ctiles), dim3(256), 0,
+                       s, x, (int)K, nib, scale, ts, offsets, (int)E, w.part, w.pmax,
+                       w.chunk_start);
+    QUADS_CHECK_LAUNCH();
+    hipLaunchKernelGGL(k_rac_expert_scores, dim3((unsigned)ctiles, (unsigned)E), dim3(256), 0, s,
+                       w.part, w.pmax, w.chunk_start, (int)K, w.score, w.cmax);
+    QUADS_CHECK_LAUNCH();
+    hipLaunchKernelGGL(k_rac_select, dim3((unsigned)E), dim3(1024), 0, s, w.score, w.cmax, 1,
+                       (int)K, (int)k, sel, r_ts, score_out, w.tables);
+    QUADS_CHECK_LAUNCH();
+    if (k > 0) {
+        const int64_t nel = M * (int64_t)k;
+        int64_t grid = (nel + 255) / 256;
+        if (grid > 2048) grid = 2048;
+        hipLaunchKernelGGL(k_rac_pass2_experts, dim3((unsigned)grid), dim3(256), 0, s, x, M,
+                           (int)K, sel, (int)k, offsets, (int)E, nib, scale, ts, r_ts, w.tables,
+                           r_nib, r_scale);
+        QUADS_CHECK_LAUNCH();
+    }
+    return QUADS_OK;
+}
+

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 17
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 20
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -126,6 +126,28 @@ def test_gemm_rowscale_validation():
     assert call(offsets=None) == -1
     assert call(epi=1, odt=0) == -1
     assert call(out=MIS) == -1
+
+
+def test_experts_validation():
+    lib = Q.lib()
+    f = lib.quads_rac_quantize_experts
+    ws = lib.quads_rac_quantize_experts_ws(64, 256, 16, 4)
+    assert ws > 0
+
+    def call(m=64, kd=256, k=16, e=4, off=FAKE, wsz=ws):
+        return f(FAKE, m, kd, k, off, e, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wsz,
+                 None)
+    assert call(off=None) == -1                 # offsets required
+    assert call(k=8) == -2
+    assert call(m=64 ** 3 + 1) == -2            # rows per expert bound
+    assert call(e=0) == -2
+    assert call(wsz=ws - 1) == -3
+    g = lib.quads_moe_w4a4_gemm_sel_experts
+    gws = lib.quads_moe_w4a4_gemm_ws(64, 256, 16, 4, 64)
+    assert g(FAKE, FAKE, FAKE, 64, 256, FAKE, FAKE, FAKE, FAKE, 16, FAKE, FAKE, FAKE, None, 4, 64,
+             0, 0, FAKE, FAKE, gws, None) == -1      # offsets required
+    assert g(FAKE, FAKE, FAKE, 64, 256, FAKE, FAKE, None, FAKE, 16, FAKE, FAKE, FAKE, FAKE, 4, 64,
+             0, 0, FAKE, FAKE, gws, None) == -1      # residual scales required
 
 
 def test_combine_validation():
