@@ -40,7 +40,7 @@ __global__ __launch_bounds__(256) void k_rac_pass1(
     int groups, float* __restrict__ ts, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
     double* __restrict__ p0, uint32_t* __restrict__ cm0) {
     __shared__ __align__(16) uint32_t s_tab[kE4m3MaxCode + 2][8];
-    __shared__ float s_r[kTileRows][kP1Cols + 4];
+    __shared__ float s_r[kTileRows / 2][kP1Cols + 4];  // one half of the chunk at a time
     __shared__ float s_st;
     __shared__ uint32_t s_red[4];
     tensor_scale_prologue(partial, groups, nullptr, 0, &s_st, s_red);   // groups <= 8 * 256
@@ -66,63 +66,70 @@ __global__ __launch_bounds__(256) void k_rac_pass1(
             q0[q] = ld_stream16(p);
             q1[q] = ld_stream16(p + 1);
         }
+        // the chunk's residuals in two halves of 32 rows (LDS of one half): the
+        // per-channel sum continues over rows 0 .. 63 in order
+        double acc = 0.0;
+        uint32_t m = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int rl = (tid >> 4) + 16 * q;
-            const int64_t row = ch * kTileRows + rl;
-            float r[16];
-            if (row < M && c0 < K) {
-                const int64_t b = (row * K + c0) / kBlock;
-                const uint32_t w[8] = {q0[q].x, q0[q].y, q0[q].z, q0[q].w,
-                                       q1[q].x, q1[q].y, q1[q].z, q1[q].w};
-                uint32_t am = 0;
+        for (int half = 0; half < 2; ++half) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
-                const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
-                const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
-                const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
-                const uint4 t0 = *reinterpret_cast<const uint4*>(&s_tab[sb][0]);
-                const uint4 t1 = *reinterpret_cast<const uint4*>(&s_tab[sb][4]);
-                const uint2 packed = encode_block_bf16(w, t0, t1);
-                *reinterpret_cast<uint2*>(nib + b * 8) = packed;
-                scale[b] = (uint8_t)sb;
-                const float s_b = e4m3_value(sb);
-                float v[16];
-                decode8(packed.x, v);
-                decode8(packed.y, v + 8);
+            for (int qq = 0; qq < 2; ++qq) {
+                const int q = 2 * half + qq;
+                const int rl = (tid >> 4) + 16 * q;   // row in the chunk
+                const int64_t row = ch * kTileRows + rl;
+                float r[16];
+                if (row < M && c0 < K) {
+                    const int64_t b = (row * K + c0) / kBlock;
+                    const uint32_t w[8] = {q0[q].x, q0[q].y, q0[q].z, q0[q].w,
+                                           q1[q].x, q1[q].y, q1[q].z, q1[q].w};
+                    uint32_t am = 0;
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const float xv =
-                        __uint_as_float(e & 1 ? w[e >> 1] & 0xFFFF0000u : w[e >> 1] << 16);
-                    r[e] = fmaf(-(v[e] * s_b), s_t, xv);    // RN32(x - v s_b s_t), v s_b exact
+                    for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
+                    const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+                    const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
+                    const uint32_t sb =
+                        s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
+                    const uint4 t0 = *reinterpret_cast<const uint4*>(&s_tab[sb][0]);
+                    const uint4 t1 = *reinterpret_cast<const uint4*>(&s_tab[sb][4]);
+                    const uint2 packed = encode_block_bf16(w, t0, t1);
+                    *reinterpret_cast<uint2*>(nib + b * 8) = packed;
+                    scale[b] = (uint8_t)sb;
+                    const float s_b = e4m3_value(sb);
+                    float v[16];
+                    decode8(packed.x, v);
+                    decode8(packed.y, v + 8);
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const float xv =
+                            __uint_as_float(e & 1 ? w[e >> 1] & 0xFFFF0000u : w[e >> 1] << 16);
+                        r[e] = fmaf(-(v[e] * s_b), s_t, xv);  // RN32(x - v s_b s_t), v s_b exact
+                    }
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) r[e] = 0.0f;
                 }
-            } else {
 #pragma unroll
-                for (int e = 0; e < 16; ++e) r[e] = 0.0f;
+                for (int e = 0; e < 16; e += 4)
+                    *reinterpret_cast<float4*>(&s_r[rl - 32 * half][cb * kBlock + e]) =
+                        make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
             }
-#pragma unroll
-            for (int e = 0; e < 16; e += 4)
-                *reinterpret_cast<float4*>(&s_r[rl][cb * kBlock + e]) =
-                    make_float4(r[e], r[e + 1], r[e + 2], r[e + 3]);
-        }
-        __syncthreads();
-        if (p0 != nullptr) {                           // scores wanted
-            double acc = 0.0;
-            uint32_t m = 0;
+            __syncthreads();
+            if (p0 != nullptr) {                       // scores wanted
 #pragma unroll 16
-            for (int i = 0; i < kTileRows; ++i) {             // token order
-                const float rv = s_r[i][tid];
-                const double rd = (double)rv;
-                acc = acc + rd * rd;                          // r^2 exact in fp64
-                const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
-                m = ab > m ? ab : m;
+                for (int i = 0; i < kTileRows / 2; ++i) {     // token order
+                    const float rv = s_r[i][tid];
+                    const double rd = (double)rv;
+                    acc = acc + rd * rd;                      // r^2 exact in fp64
+                    const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
+                    m = ab > m ? ab : m;
+                }
             }
-            if (gc < K) {
-                p0[ch * K + gc] = acc;
-                cm0[ch * K + gc] = m;
-            }
+            __syncthreads();
         }
-        __syncthreads();
+        if (p0 != nullptr && gc < K) {
+            p0[ch * K + gc] = acc;
+            cm0[ch * K + gc] = m;
+        }
     }
 }
 
