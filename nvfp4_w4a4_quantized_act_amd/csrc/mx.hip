@@ -29,7 +29,7 @@ namespace mx {
 typedef int v8i __attribute__((ext_vector_type(8)));
 
 constexpr int kMxBlock = 32;
-constexpr int kFp8 = QUADS_MX_FP8, kFp4 = QUADS_MX_FP4;
+constexpr int kFp8 = QUADS_MX_FP8;
 
 // --------------------------------------------------------------- quantize --
 // One lane per 16-element half block (two 16-byte bf16 loads); the block

@@ -316,7 +316,7 @@ extern "C" int quads_nvfp4_quantize_rows(const uint16_t* x, int64_t M, int64_t K
     if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale) || !ok_ptr(ts)))
         return QUADS_EINVAL;
     if (M == 0) return QUADS_OK;
-    if (M > ((int64_t)1 << 33)) return QUADS_ESHAPE;
+    if ((M + 3) / 4 > 0x7FFFFFFF) return QUADS_ESHAPE;           // grid of M / 4 work-groups
     hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)((M + 3) / 4)), dim3(256), 0,
                        (hipStream_t)stream, x, M, (int)K, nib, scale, ts);
     QUADS_CHECK_LAUNCH();

@@ -387,19 +387,22 @@ constexpr int64_t kExpertMaxRows = (int64_t)kScoreFanin * kScoreFanin * kScoreFa
 constexpr int kExpertMaxE = 4096;          // chunk starts kept in LDS
 
 // Level-0 partials of every chunk: work-group (x, slice) takes chunks x,
-// x + gridDim.x, ...; thread = channel; r recomputed from x and the main
-// NVFP4 exactly as pass 1 forms it, 16 rows loaded at a time, summed in row
-// order from +0.  Work-group (0, 0) also writes chunk_start.
-__global__ __launch_bounds__(256) void k_rac_expert_partials(
+// x + gridDim.x, ...; thread = two neighbouring channels (one 4-byte load of
+// x, one nibble byte and one scale byte per row); r recomputed from x and the
+// main NVFP4 exactly as pass 1 forms it, 32 rows loaded at a time, summed in
+// row order from +0.  Work-group (0, 0) also writes chunk_start.
+constexpr int kPartThreads = 128;          // 256 channels per slice
+
+__global__ __launch_bounds__(kPartThreads) void k_rac_expert_partials(
     const uint16_t* __restrict__ x, int K, const uint8_t* __restrict__ nib,
     const uint8_t* __restrict__ scale, const float* __restrict__ ts,
     const int32_t* __restrict__ offsets, int E, double* __restrict__ part,
     uint32_t* __restrict__ pmax, int32_t* __restrict__ chunk_start) {
     __shared__ int s_cs[kExpertMaxE + 1];
-    __shared__ int s_w[4];
+    __shared__ int s_w[kPartThreads / 64];
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     // chunk starts: each thread a run of experts, then a scan over the block
-    const int per = (E + 255) / 256;
+    const int per = (E + kPartThreads - 1) / kPartThreads;
     const int e0 = tid * per, e1 = e0 + per < E ? e0 + per : E;
     int local = 0;
     for (int e = e0; e < e1; ++e) local += (offsets[e + 1] - offsets[e] + kTileRows - 1) / kTileRows;
@@ -417,12 +420,12 @@ __global__ __launch_bounds__(256) void k_rac_expert_partials(
         s_cs[e] = run;
         run += (offsets[e + 1] - offsets[e] + kTileRows - 1) / kTileRows;
     }
-    if (tid == 255) s_cs[E] = run;                     // thread 255 ends at the total
+    if (tid == kPartThreads - 1) s_cs[E] = run;        // the last thread ends at the total
     __syncthreads();
     if (blockIdx.x == 0 && blockIdx.y == 0)
-        for (int e = tid; e <= E; e += 256) chunk_start[e] = s_cs[e];
+        for (int e = tid; e <= E; e += kPartThreads) chunk_start[e] = s_cs[e];
     const int nchunks = s_cs[E];
-    const int c = blockIdx.y * 256 + tid;
+    const int c = blockIdx.y * 2 * kPartThreads + 2 * tid;   // channels c, c + 1 (K even)
     const float s_t = ts[0];
     for (int ch = blockIdx.x; ch < nchunks; ch += gridDim.x) {
         int lo = 0, hi = E;                           // s_cs[lo] <= ch < s_cs[lo + 1]
@@ -434,33 +437,40 @@ __global__ __launch_bounds__(256) void k_rac_expert_partials(
         const int64_t rend = offsets[lo + 1];
         const int nr = (int)(rend - row0 < kTileRows ? rend - row0 : kTileRows);
         if (c >= K) continue;
-        double acc = 0.0;
-        uint32_t m = 0;
-        for (int b = 0; b < nr; b += 16) {             // 16 rows in flight, loads first
-            uint32_t xv[16], cv[16], sv[16];
+        double acc[2] = {0.0, 0.0};
+        uint32_t m[2] = {0u, 0u};
+        for (int b = 0; b < nr; b += 32) {             // 32 rows in flight, loads first
+            uint32_t xv[32], cv[32], sv[32];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 const int64_t p = row0 + (b + u < nr ? b + u : nr - 1);
-                xv[u] = x[p * K + c];
+                xv[u] = *reinterpret_cast<const uint32_t*>(x + p * K + c);
                 cv[u] = nib[p * (K / 2) + (c >> 1)];
                 sv[u] = scale[p * (K / kBlock) + (c >> 4)];
             }
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < 32; ++u) {
                 if (b + u < nr) {
-                    const uint32_t code = (cv[u] >> (4 * (c & 1))) & 0xFu;
-                    float v = e2m1_value(code & 7u);
-                    if (code & 8u) v = -v;
-                    const float r = fmaf(-(v * e4m3_value(sv[u])), s_t, bf16_to_f32(xv[u]));
-                    const double rd = (double)r;
-                    acc = acc + rd * rd;                  // r^2 exact in fp64, row order
-                    const uint32_t ab = __float_as_uint(r) & 0x7FFFFFFFu;
-                    m = ab > m ? ab : m;
+                    const float s_b = e4m3_value(sv[u]);
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {      // channel c + h: nibble h, bf16 h
+                        const uint32_t code = (cv[u] >> (4 * h)) & 0xFu;
+                        float v = e2m1_value(code & 7u);
+                        if (code & 8u) v = -v;
+                        const float xf = __uint_as_float(h ? xv[u] & 0xFFFF0000u : xv[u] << 16);
+                        const float r = fmaf(-(v * s_b), s_t, xf);
+                        const double rd = (double)r;
+                        acc[h] = acc[h] + rd * rd;        // r^2 exact in fp64, row order
+                        const uint32_t ab = __float_as_uint(r) & 0x7FFFFFFFu;
+                        m[h] = ab > m[h] ? ab : m[h];
+                    }
                 }
             }
         }
-        part[(int64_t)ch * K + c] = acc;
-        pmax[(int64_t)ch * K + c] = m;
+        part[(int64_t)ch * K + c] = acc[0];
+        part[(int64_t)ch * K + c + 1] = acc[1];
+        pmax[(int64_t)ch * K + c] = m[0];
+        pmax[(int64_t)ch * K + c + 1] = m[1];
     }
 }
 
@@ -490,14 +500,15 @@ __global__ __launch_bounds__(256) void k_rac_expert_scores(
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            if (q + i >= q1) break;
-            acc1 = acc1 + v[i];
-            m = u[i] > m ? u[i] : m;
-            if (++n1 == kScoreFanin) {                    // a level-1 node is done
-                acc2 = acc2 + acc1;
-                acc1 = 0.0;
-                n1 = 0;
-                ++n2;
+            if (q + i < q1) {
+                acc1 = acc1 + v[i];
+                m = u[i] > m ? u[i] : m;
+                if (++n1 == kScoreFanin) {                // a level-1 node is done
+                    acc2 = acc2 + acc1;
+                    acc1 = 0.0;
+                    n1 = 0;
+                    ++n2;
+                }
             }
         }
     }
@@ -761,9 +772,9 @@ extern "C" int quads_rac_quantize_experts(const uint16_t* x, int64_t M, int64_t 
     int64_t gp = 2048 / ctiles;                     // chunk partials: at most M / 64 + E chunks
     const int64_t nch = M / kTileRows + E;
     gp = gp < 1 ? 1 : (gp > nch ? nch : gp);
-    hipLaunchKernelGGL(k_rac_expert_partials, dim3((unsigned)gp, (unsigned)ctiles), dim3(256), 0,
-                       s, x, (int)K, nib, scale, ts, offsets, (int)E, w.part, w.pmax,
-                       w.chunk_start);
+    hipLaunchKernelGGL(k_rac_expert_partials, dim3((unsigned)gp, (unsigned)ctiles),
+                       dim3(kPartThreads), 0, s, x, (int)K, nib, scale, ts, offsets, (int)E,
+                       w.part, w.pmax, w.chunk_start);
     QUADS_CHECK_LAUNCH();
     hipLaunchKernelGGL(k_rac_expert_scores, dim3((unsigned)ctiles, (unsigned)E), dim3(256), 0, s,
                        w.part, w.pmax, w.chunk_start, (int)K, w.score, w.cmax);
