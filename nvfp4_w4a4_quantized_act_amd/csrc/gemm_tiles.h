@@ -126,7 +126,7 @@ __device__ __forceinline__ int rows_of(const int32_t* offsets, int e, int skip) 
 }
 
 template <int BMT>
-__device__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
+__device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
                                int* m0_out, int* mend_out, int skip = 0) {
     constexpr int kH = BMT / 32;                  // tile heights 1 .. kH blocks
     if (offsets == nullptr) {

@@ -206,6 +206,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
                                                      double* __restrict__ score_out,
                                                      uint32_t* __restrict__ r_table) {
     __shared__ unsigned long long s_key[kRacMaxK];
+    __shared__ uint32_t s_cmax[kRacMaxK];          // per-channel max |r| over the rows
     __shared__ int s_hist[256];
     __shared__ int s_tmp[40];
     __shared__ unsigned long long s_prefix;
@@ -227,8 +228,14 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     // rows summed in order from +0
     for (int j = tid; j < K; j += 1024) {
         double v = 0.0;
-        for (int r = 0; r < nrows; ++r) v = v + score[(int64_t)r * K + j];
+        uint32_t cm = 0;
+        for (int r = 0; r < nrows; ++r) {
+            v = v + score[(int64_t)r * K + j];
+            const uint32_t c = colmax[(int64_t)r * K + j];
+            cm = c > cm ? c : cm;
+        }
         s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
+        s_cmax[j] = cm;
         if (score_out) score_out[j] = v;
     }
     if (tid == 0) { s_prefix = 0ull; s_need = k; s_done = k == 0; }
@@ -308,10 +315,7 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
             const unsigned long long key = s_key[j] & mask;
             if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) {
                 sel[o++] = j;
-                for (int r = 0; r < nrows; ++r) {
-                    const uint32_t c = colmax[(int64_t)r * K + j];
-                    am = c > am ? c : am;
-                }
+                am = s_cmax[j] > am ? s_cmax[j] : am;
             }
         }
     }
