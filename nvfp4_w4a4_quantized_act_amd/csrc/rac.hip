@@ -198,46 +198,19 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* s_tmp, int* tota
     return res;
 }
 
-__global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ score,
-                                                     const uint32_t* __restrict__ colmax,
-                                                     int nrows, int K,
-                                                     int k, int32_t* __restrict__ sel,
-                                                     float* __restrict__ r_ts,
-                                                     double* __restrict__ score_out,
-                                                     uint32_t* __restrict__ r_table) {
-    __shared__ unsigned long long s_key[kRacMaxK];
-    __shared__ uint32_t s_cmax[kRacMaxK];          // per-channel max |r| over the rows
+// Radix select of the k largest of K keys held in LDS (fp64 scores as bit
+// patterns; ties to the lower index), by a 1024-thread work-group: S into
+// sel (ascending), and the tensor scale of the gathered residual, from the
+// selected channels' maxima s_cmax, into *s_rts (LDS).
+__device__ void select_keys(const unsigned long long* s_key, const uint32_t* s_cmax, int K, int k,
+                            int32_t* __restrict__ sel, float* s_rts) {
     __shared__ int s_hist[256];
     __shared__ int s_tmp[40];
     __shared__ unsigned long long s_prefix;
     __shared__ int s_need;
     __shared__ int s_done;
     __shared__ uint32_t s_amax[16];
-    __shared__ float s_rts;
     const int tid = threadIdx.x;
-    {   // work-group b selects for expert b (one work-group: the shared selection)
-        const int64_t b = blockIdx.x;
-        score += b * nrows * (int64_t)K;
-        colmax += b * nrows * (int64_t)K;
-        sel += b * k;
-        r_ts += b;
-        if (score_out) score_out += b * (int64_t)K;
-        r_table += b * 1024;
-    }
-    // the last level of the fixed-order tree: nrows (<= kSelectFold) partial
-    // rows summed in order from +0
-    for (int j = tid; j < K; j += 1024) {
-        double v = 0.0;
-        uint32_t cm = 0;
-        for (int r = 0; r < nrows; ++r) {
-            v = v + score[(int64_t)r * K + j];
-            const uint32_t c = colmax[(int64_t)r * K + j];
-            cm = c > cm ? c : cm;
-        }
-        s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
-        s_cmax[j] = cm;
-        if (score_out) score_out[j] = v;
-    }
     if (tid == 0) { s_prefix = 0ull; s_need = k; s_done = k == 0; }
     __syncthreads();
     // MSB-first radix select of the k-th largest key, 8 bits per pass.  It
@@ -325,11 +298,253 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
     if (tid == 0) {
         uint32_t m = 0;
         for (int i = 0; i < 16; ++i) m = s_amax[i] > m ? s_amax[i] : m;
-        s_rts = tensor_scale_from_amax(__uint_as_float(m));
-        r_ts[0] = s_rts;
+        *s_rts = tensor_scale_from_amax(__uint_as_float(m));
     }
     __syncthreads();
+}
+
+__global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ score,
+                                                     const uint32_t* __restrict__ colmax,
+                                                     int nrows, int K,
+                                                     int k, int32_t* __restrict__ sel,
+                                                     float* __restrict__ r_ts,
+                                                     double* __restrict__ score_out,
+                                                     uint32_t* __restrict__ r_table) {
+    __shared__ unsigned long long s_key[kRacMaxK];
+    __shared__ uint32_t s_cmax[kRacMaxK];          // per-channel max |r| over the rows
+    __shared__ float s_rts;
+    const int tid = threadIdx.x;
+    {   // work-group b selects for expert b (one work-group: the shared selection)
+        const int64_t b = blockIdx.x;
+        score += b * nrows * (int64_t)K;
+        colmax += b * nrows * (int64_t)K;
+        sel += b * k;
+        r_ts += b;
+        if (score_out) score_out += b * (int64_t)K;
+        r_table += b * 1024;
+    }
+    // the last level of the fixed-order tree: nrows (<= kSelectFold) partial
+    // rows summed in order from +0
+    for (int j = tid; j < K; j += 1024) {
+        double v = 0.0;
+        uint32_t cm = 0;
+        for (int r = 0; r < nrows; ++r) {
+            v = v + score[(int64_t)r * K + j];
+            const uint32_t c = colmax[(int64_t)r * K + j];
+            cm = c > cm ? c : cm;
+        }
+        s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
+        s_cmax[j] = cm;
+        if (score_out) score_out[j] = v;
+    }
+    select_keys(s_key, s_cmax, K, k, sel, &s_rts);
+    if (tid == 0) r_ts[0] = s_rts;
     build_threshold_table(s_rts, reinterpret_cast<uint32_t(*)[8]>(r_table), false);
+}
+
+// ------------------------------------------------------------------ small --
+// Tiny activations (at most 64 rows, one level-0 group, and at most 16384
+// elements, e.g. a decode step of a few tokens): the whole RAC in one
+// 1024-thread work-group and one launch, with the same arithmetic as the
+// launches above.  Measured against the five launches: 11.2 / 13.5 us
+// against 17.0 / 18.2 us at 16 x 128 and 32 x 256 (k = 64), but 23.9 against
+// 20.5 us at 64 x 512 and 55.7 against 23.7 us at 64 x 2048, where one CU's
+// share of the work outweighs the launches it saves.
+//  1. max |x| -> s_t, and the code table of x in LDS;
+//  2. rows in groups of RG = 1024 / (K/16) (thread = one 16-block of one row
+//     of the group, loads of four groups in flight): NVFP4 codes and scale
+//     bytes, r = RN32(x - v s_b s_t) into LDS, then thread = channel adds the
+//     group's r^2 to its in-order fp64 sum (and max |r|), so every channel's
+//     score is the sum over rows 0 .. M-1 in order from +0;
+//  3. the radix selection (select_keys), the residual's tensor scale and its
+//     code table in LDS;
+//  4. the second pass as in k_rac_pass2.
+constexpr int kSmallMaxK = 2048;
+constexpr int64_t kSmallMaxElems = 16384;
+constexpr int kSmallPre = 4;                      // row groups loaded together
+
+__global__ __launch_bounds__(1024) void k_rac_small(
+    const uint16_t* __restrict__ x, int M, int K, int k, bool want_scores,
+    uint8_t* __restrict__ nib, uint8_t* __restrict__ scale, float* __restrict__ ts,
+    int32_t* __restrict__ sel, uint8_t* __restrict__ r_nib, uint8_t* __restrict__ r_scale,
+    float* __restrict__ r_ts, double* __restrict__ score_out) {
+    __shared__ __align__(16) uint32_t s_tab[kE4m3MaxCode + 2][8];
+    __shared__ __align__(16) float s_r[16 * 1024];    // one group's residuals, [RG][K]
+    __shared__ unsigned long long s_key[kSmallMaxK];
+    __shared__ uint32_t s_cmax[kSmallMaxK];
+    __shared__ uint32_t s_w[16];
+    __shared__ float s_st, s_rts;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+
+    // 1. tensor scale: 8 bf16 per load, 8 loads in flight per thread
+    const int64_t n8 = (int64_t)M * K / 8;
+    const uint4* x8 = reinterpret_cast<const uint4*>(x);
+    uint32_t mx = 0;
+    for (int64_t b = 0; b < n8; b += 8 * 1024) {
+        uint4 q[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int64_t i = b + u * 1024 + tid;
+            q[u] = i < n8 ? x8[i] : make_uint4(0, 0, 0, 0);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            mx = pk_max_u16(mx, q[u].x & 0x7FFF7FFFu);
+            mx = pk_max_u16(mx, q[u].y & 0x7FFF7FFFu);
+            mx = pk_max_u16(mx, q[u].z & 0x7FFF7FFFu);
+            mx = pk_max_u16(mx, q[u].w & 0x7FFF7FFFu);
+        }
+    }
+    {
+        const uint32_t lo = mx & 0xFFFFu, hi = mx >> 16;
+        const uint32_t m = wave_max_u32(lo > hi ? lo : hi);
+        if (lane == 0) s_w[wid] = m;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        uint32_t m = 0;
+        for (int w = 0; w < 16; ++w) m = s_w[w] > m ? s_w[w] : m;
+        s_st = tensor_scale_from_amax(bf16_to_f32(m));
+        ts[0] = s_st;
+    }
+    __syncthreads();
+    const float s_t = s_st;
+    const double six_st = 6.0 * (double)s_t;
+    build_threshold_table(s_t, s_tab, true);
+    __syncthreads();
+
+    // 2. codes, residuals and the in-order channel sums
+    const int kb = K / kBlock;                        // blocks per row
+    const int rg = 1024 / kb;                         // rows per group (>= 8)
+    const int ngroups = (M + rg - 1) / rg;
+    const int bcol = tid % kb, rr = tid / kb;         // this thread's block in a group
+    double acc[2] = {0.0, 0.0};
+    uint32_t cm[2] = {0u, 0u};
+    for (int g0 = 0; g0 < ngroups; g0 += kSmallPre) {
+        uint4 q0[kSmallPre], q1[kSmallPre];
+#pragma unroll
+        for (int u = 0; u < kSmallPre; ++u) {          // loads of four groups first
+            const int row = (g0 + u) * rg + rr;
+            const bool ok = rr < rg && row < M;
+            const uint4* p = reinterpret_cast<const uint4*>(x + (ok ? (int64_t)row * K + bcol * kBlock : 0));
+            q0[u] = p[0];
+            q1[u] = p[1];
+        }
+#pragma unroll
+        for (int u = 0; u < kSmallPre; ++u) {
+            const int g = g0 + u;
+            if (g >= ngroups) break;                  // uniform
+            const int row = g * rg + rr;
+            if (rr < rg && row < M) {
+                const int64_t b = (int64_t)row * kb + bcol;
+                const uint32_t w[8] = {q0[u].x, q0[u].y, q0[u].z, q0[u].w,
+                                       q1[u].x, q1[u].y, q1[u].z, q1[u].w};
+                uint32_t am = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) am = pk_max_u16(am, w[i] & 0x7FFF7FFFu);
+                const uint32_t lo = am & 0xFFFFu, hi = am >> 16;
+                const float amax_b = bf16_to_f32(lo > hi ? lo : hi);
+                const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)amax_b / six_st) : 0u;
+                const uint4 t0 = *reinterpret_cast<const uint4*>(&s_tab[sb][0]);
+                const uint4 t1 = *reinterpret_cast<const uint4*>(&s_tab[sb][4]);
+                const uint2 packed = encode_block_bf16(w, t0, t1);
+                *reinterpret_cast<uint2*>(nib + b * 8) = packed;
+                scale[b] = (uint8_t)sb;
+                const float s_b = e4m3_value(sb);
+                float v[16];
+                decode8(packed.x, v);
+                decode8(packed.y, v + 8);
+#pragma unroll
+                for (int e = 0; e < 16; e += 4) {
+                    float r4[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) {
+                        const int ee = e + t;
+                        const float xv =
+                            __uint_as_float(ee & 1 ? w[ee >> 1] & 0xFFFF0000u : w[ee >> 1] << 16);
+                        r4[t] = fmaf(-(v[ee] * s_b), s_t, xv);   // RN32(x - v s_b s_t)
+                    }
+                    *reinterpret_cast<float4*>(&s_r[rr * K + bcol * kBlock + e]) =
+                        make_float4(r4[0], r4[1], r4[2], r4[3]);
+                }
+            }
+            __syncthreads();
+            if (want_scores) {
+#pragma unroll
+                for (int ci = 0; ci < 2; ++ci) {
+                    const int c = tid + 1024 * ci;
+                    if (c < K) {
+                        const int nr = M - g * rg < rg ? M - g * rg : rg;
+                        for (int i = 0; i < nr; ++i) {        // row order
+                            const float rv = s_r[i * K + c];
+                            const double rd = (double)rv;
+                            acc[ci] = acc[ci] + rd * rd;      // r^2 exact in fp64
+                            const uint32_t ab = __float_as_uint(rv) & 0x7FFFFFFFu;
+                            cm[ci] = ab > cm[ci] ? ab : cm[ci];
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
+    }
+    if (!want_scores) {                               // neither S nor the scores
+        if (tid == 0) r_ts[0] = 0.0f;
+        return;
+    }
+#pragma unroll
+    for (int ci = 0; ci < 2; ++ci) {
+        const int c = tid + 1024 * ci;
+        if (c < K) {
+            s_key[c] = (unsigned long long)__double_as_longlong(acc[ci]);   // >= +0: bits order
+            s_cmax[c] = cm[ci];
+            if (score_out) score_out[c] = acc[ci];
+        }
+    }
+    __syncthreads();
+
+    // 3. selection, the residual's tensor scale and code table
+    select_keys(s_key, s_cmax, K, k, sel, &s_rts);
+    const float s_tr = s_rts;
+    if (tid == 0) r_ts[0] = s_tr;
+    build_threshold_table(s_tr, s_tab, false);
+    __syncthreads();                                  // sel, codes and scales written above
+
+    // 4. second pass: one thread per element of r[:, S], 16-lane blocks
+    const int64_t n = (int64_t)M * k;                 // k % 16 == 0: blocks never straddle
+    const double six_str = 6.0 * (double)s_tr;
+    for (int64_t t = tid; t - tid < n; t += 1024) {
+        const bool live = t < n;                      // uniform over each 16-lane block
+        float r = 0.0f;
+        if (live) {
+            const int64_t row = t / k;
+            const int i = (int)(t - row * k);
+            const int j = sel[i];
+            const uint32_t h = x[row * K + j];
+            const uint32_t code = (nib[row * (K / 2) + (j >> 1)] >> (4 * (j & 1))) & 0xFu;
+            float sv = e2m1_value(code & 7u) * e4m3_value(scale[row * kb + (j >> 4)]);
+            if (code & 8u) sv = -sv;
+            r = fmaf(-sv, s_t, bf16_to_f32(h));
+        }
+        const uint32_t rb = __float_as_uint(r);
+        uint32_t am = rb & 0x7FFFFFFFu;
+#pragma unroll
+        for (int off = 8; off > 0; off >>= 1) {
+            const uint32_t o = __shfl_xor(am, off, 16);
+            am = o > am ? o : am;
+        }
+        const uint32_t sb =
+            s_tr > 0.0f ? e4m3_rne_code((double)__uint_as_float(am) / six_str) : 0u;
+        const uint4 t0 = *reinterpret_cast<const uint4*>(&s_tab[sb][0]);
+        const uint4 t1 = *reinterpret_cast<const uint4*>(&s_tab[sb][4]);
+        const uint32_t thr[7] = {t0.x, t0.y, t0.z, t0.w, t1.x, t1.y, t1.z};
+        const uint32_t c = e2m1_mag_code(rb & 0x7FFFFFFFu, thr) | ((rb >> 28) & 8u);
+        const uint32_t other = __shfl_xor(c, 1, 16);
+        if (live) {
+            if ((t & 1) == 0) r_nib[t >> 1] = (uint8_t)(c | (other << 4));
+            if ((t & 15) == 0) r_scale[t >> 4] = (uint8_t)sb;
+        }
+    }
 }
 
 // ----------------------------------------------------------------- pass 2 --
@@ -645,6 +860,13 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
         if (score_out)
             hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
                                score_out, (int)K, 0.0);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    if (M <= kTileRows && K <= kSmallMaxK && M * K <= kSmallMaxElems) {   // one launch
+        hipLaunchKernelGGL(k_rac_small, dim3(1), dim3(1024), 0, s, x, (int)M, (int)K, (int)k,
+                           k > 0 || score_out != nullptr, nib, scale, ts, sel, r_nib, r_scale,
+                           r_ts, score_out);
         QUADS_CHECK_LAUNCH();
         return QUADS_OK;
     }

@@ -70,8 +70,12 @@ def test_rac_moe_down_site_shape(Q):
 
 
 @pytest.mark.parametrize("m,kd,k", [(1, 16, 16), (37, 48, 16), (65, 272, 32), (300, 1040, 256),
-                                    (64, 256, 0), (5, 64, 64)])
+                                    (64, 256, 0), (5, 64, 64), (64, 2048, 64), (63, 1040, 32),
+                                    (17, 2048, 0), (8, 2048, 32), (64, 256, 256), (4, 2064, 16)])
 def test_rac_ragged(Q, m, kd, k):
+    """Ragged shapes on both paths: one work-group for at most 64 rows, K <=
+    2048 and at most 16384 elements (8 x 2048, 64 x 256), the launches
+    otherwise (65 rows; 64 x 2048, the decode step's gate/up input; K = 2064)."""
     rng = np.random.default_rng(m + kd + k)
     x = (rng.standard_normal((m, kd)) * np.exp2(rng.integers(-2, 3, (1, kd)))).astype(np.float32)
     _check(Q, synth.f32_to_bf16_bits(x), k)
