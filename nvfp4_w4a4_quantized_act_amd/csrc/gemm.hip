@@ -690,11 +690,12 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     hipStream_t st = (hipStream_t)stream;
     if (gemm_decode_fits(g)) {
         // few rows per expert: the decode kernel takes every expert with at
-        // most kDecodeMaxRows rows; when some expert may have more (rows >
-        // kDecodeMaxRows), the tiled kernel below takes those
-        g.dec_rows = kDecodeMaxRows;
+        // most kDecodeMaxRows rows, or all of them at most kDecodeAllRows
+        // rows in all; when some expert may have more than it takes, the
+        // tiled kernel below takes those
+        g.dec_rows = rows <= kDecodeAllRows ? (int)rows : kDecodeMaxRows;
         const int rc = launch_gemm_decode(g, st);
-        if (rc != QUADS_OK || rows <= kDecodeMaxRows) return rc;
+        if (rc != QUADS_OK || rows <= g.dec_rows) return rc;
     }
     if (K % v2::BK == 0 && k % v2::BK == 0) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)

@@ -10,8 +10,11 @@
 // epilogue pairs them in registers) and streams it from HBM once per 32 token
 // rows of the expert (later passes find it in L2); a work-group of an expert
 // without rows leaves at once, so only active experts' weights are read.  An
-// expert with more than kDecodeMaxRows rows is left to the tiled kernel, which
-// the caller launches after this one (gemm.hip).
+// expert with more than g.dec_rows rows (kDecodeMaxRows, or all rows when
+// there are at most kDecodeAllRows) is left to the tiled kernel, which the
+// caller launches after this one (gemm.hip); an expert above kDecodeMaxRows
+// rows that this kernel takes is split over work-groups of at most
+// kDecodeMaxRows rows each.
 //
 // Streaming.  A lane (row r = lane % 32, half h = lane / 32) of a wave holds,
 // per 128-deep chunk of K, codes 64h .. 64h + 63 of one weight row in each of
@@ -117,12 +120,21 @@ __device__ __forceinline__ void chunk_mma(const Piece& w0, const Piece& w1, cons
     }
 }
 
-// Grid: 8 ceil(E / 8) x slabs work-groups over the experts this kernel
-// takes (0 < rows <= dec_rows), ranked in index order: block b runs on XCD
-// b % 8 and takes slab (b / 8) % slabs of the active expert of rank
-// 8 ((b / 8) / slabs) + b % 8, so all slabs of an expert share one XCD's L2
-// (where its activation rows stay) and the blocks past the active experts,
-// which only look up their expert and leave, come last in dispatch order.
+// Work units: each expert this kernel takes (0 < rows <= dec_rows) splits
+// into units of at most kDecodeMaxRows rows (one unit, unless dec_rows is
+// raised above kDecodeMaxRows), so that an expert of many rows is spread over
+// work-groups rather than run in many passes by one.  At most
+// E + rows / kDecodeMaxRows units.
+static __host__ __device__ inline int decode_units_max(const GemmArgs& g) {
+    return g.E + (g.dec_rows > kDecodeMaxRows ? (int)(g.rows / kDecodeMaxRows) : 0);
+}
+
+// Grid: 8 ceil(units / 8) x slabs work-groups over the units, ranked in
+// expert and row order: block b runs on XCD b % 8 and takes slab
+// (b / 8) % slabs of the unit of rank 8 ((b / 8) / slabs) + b % 8, so all
+// slabs of a unit share one XCD's L2 (where its activation rows stay) and
+// the blocks past the last unit, which only look up their unit and leave,
+// come last in dispatch order.
 // (Ordering by expert index instead interleaved those idle blocks with the
 // working ones: at the decode step, 16 active experts of 128 took 45 us
 // against 17 us for the same 16 experts alone.)
@@ -141,20 +153,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     __shared__ int s_sel[kWaves][kCapMax];
 
     const int lane = threadIdx.x & 63;
-    const int nslab = (int)(gridDim.x / (8u * (((unsigned)g.E + 7u) / 8u)));
+    const int nslab = (int)(gridDim.x / (8u * (((unsigned)decode_units_max(g) + 7u) / 8u)));
     const int local = (int)(blockIdx.x >> 3);
     const int rank = 8 * (local / nslab) + (int)(blockIdx.x & 7u);
     const int slab = local % nslab;
     int e = 0, p0 = 0, cnt = (int)g.rows;
     if (g.offsets) {
-        // the active expert of this rank: lane l counts experts l*per ..
-        // l*per + per - 1, a wave scan finds the lane, the lane finds the expert
+        // the unit of this rank: lane l counts the units of experts l*per ..
+        // l*per + per - 1, a wave scan finds the lane, the lane finds the
+        // expert and the unit's place in it
         const int per = (g.E + 63) / 64;
         const int e0 = lane * per, e1 = e0 + per < g.E ? e0 + per : g.E;
         int na = 0;
         for (int x = e0; x < e1; ++x) {
             const int n = g.offsets[x + 1] - g.offsets[x];
-            na += n > 0 && n <= g.dec_rows;
+            na += n > 0 && n <= g.dec_rows ? (n + kDecodeMaxRows - 1) / kDecodeMaxRows : 0;
         }
         int inc = na;
 #pragma unroll
@@ -163,17 +176,21 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             if (lane >= off) inc += y;
         }
         if (rank >= __builtin_amdgcn_readlane(inc, 63)) return;   // uniform: past the last
-        int found = -1;
+        int found = -1, part = 0;
         if (rank >= inc - na && rank < inc) {                       // exactly one lane
             int rr = rank - (inc - na);
             for (int x = e0; x < e1; ++x) {
                 const int n = g.offsets[x + 1] - g.offsets[x];
-                if (n > 0 && n <= g.dec_rows && rr-- == 0) { found = x; break; }
+                const int u = n > 0 && n <= g.dec_rows ? (n + kDecodeMaxRows - 1) / kDecodeMaxRows
+                                                       : 0;
+                if (rr < u) { found = x; part = rr; break; }
+                rr -= u;
             }
         }
-        e = __builtin_amdgcn_readlane(found, __ffsll(__ballot(found >= 0)) - 1);
-        p0 = g.offsets[e];
-        cnt = g.offsets[e + 1] - p0;
+        const int src = __ffsll(__ballot(found >= 0)) - 1;
+        e = __builtin_amdgcn_readlane(found, src);
+        p0 = g.offsets[e] + kDecodeMaxRows * __builtin_amdgcn_readlane(part, src);
+        cnt = min(g.offsets[e + 1] - p0, kDecodeMaxRows);
     } else if (rank > 0 || cnt <= 0 || cnt > g.dec_rows) {
         return;                                       // one expert, all rows
     }
@@ -426,13 +443,14 @@ bool gemm_decode_fits(const GemmArgs& g) {
     const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
     return g.K % dec::kChunk == 0 && g.k <= dec::kCapMax &&
            g.rows <= (int64_t)kDecodeRowsPerExpert * g.E &&
-           slabs * 8 * ((g.E + 7) / 8) < ((int64_t)1 << 31) &&
+           slabs * 8 * ((g.E + kDecodeAllRows / kDecodeMaxRows + 7) / 8) < ((int64_t)1 << 31) &&
            (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
 }
 
 int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
     const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
-    const dim3 grid((unsigned)(slabs * 8 * ((g.E + 7) / 8))), block(dec::kThreads);
+    const dim3 grid((unsigned)(slabs * 8 * ((dec::decode_units_max(g) + 7) / 8))),
+        block(dec::kThreads);
     const int nch = g.K / dec::kChunk;
     const bool ring3 = nch % 4 != 0 && nch % 3 == 0;
     const bool sw = g.epilogue == QUADS_EPI_SWIGLU;

@@ -316,9 +316,16 @@ __device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool*
 // Grouped GEMM for experts with few rows (gemm_decode.hip): used when K is a
 // multiple of 128, k <= 64 and there are at most kDecodeRowsPerExpert packed
 // rows per expert on average; it takes the experts with at most
-// kDecodeMaxRows rows, the tiled kernel the others.
+// kDecodeMaxRows rows, the tiled kernel the others.  With at most
+// kDecodeAllRows packed rows in all (a decode step of up to 64 tokens at
+// top-8, where distinct routes give an expert at most 64 rows) it takes every
+// expert, so that the tiled kernel is not launched only to find no expert
+// above kDecodeMaxRows rows; an expert that still holds more (routes that
+// repeat an expert within a token, or top-1 routing) is then split into
+// work-groups of at most kDecodeMaxRows rows.
 constexpr int kDecodeRowsPerExpert = 32;
 constexpr int kDecodeMaxRows = 128;
+constexpr int kDecodeAllRows = 512;
 bool gemm_decode_fits(const GemmArgs& g);
 int launch_gemm_decode(const GemmArgs& g, hipStream_t st);
 

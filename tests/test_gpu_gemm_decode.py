@@ -3,7 +3,8 @@
 and k <= 64 select the weight-streaming kernel (one work-group of two waves
 per expert and 128-row weight slab, K streamed in 128-deep chunks through a
 three-deep register ring, the compensation columns taken from the stream)
-for every expert with at most 128 rows; the tiled kernel takes the others.
+for every expert with at most 128 rows, the tiled kernel the others; with at
+most 512 packed rows in all the decode kernel takes every expert.
 Same bar as the tiled kernels: |y_gpu - y_oracle| <= 1e-5 * sum_i |a_i w_i|
 per element.
 
@@ -104,13 +105,19 @@ def test_decode_grouped(Q, t, e, h, n, k):
     _assert_close(y, exp, bound)
 
 
-@pytest.mark.parametrize("k", [64, 48])
-def test_decode_with_a_large_expert(Q, k):
-    """Decode regime with one expert above 128 rows: the tiled kernel takes
-    that expert (k = 48: the 128 x 128 tiling), the decode kernel the rest."""
-    out, wq, off, rt = _case(77 + k, 150, 16, 3, 256, 160, k, heavy=(0,))
+@pytest.mark.parametrize("t,e,topk,k", [(200, 24, 3, 64), (200, 24, 3, 48), (150, 16, 3, 64),
+                                         (500, 16, 1, 64)])
+def test_decode_with_a_large_expert(Q, t, e, topk, k):
+    """Decode regime with one expert above 128 rows.  Above 512 packed rows
+    (t = 200, top-3) the tiled kernel takes that expert (k = 48: the 128 x 128
+    tiling) and the decode kernel the rest; at 450 and 500 packed rows the
+    decode kernel takes it too, split into work-groups of at most 128 rows
+    (two, and four with a last one of fewer rows)."""
+    out, wq, off, rt = _case(77 + k + t, t, e, topk, 256, 160, k, heavy=(0,))
     cnt = np.diff(off)
     assert cnt.max() > 128 and ((cnt > 0) & (cnt <= 128)).sum() > 8
+    assert topk == 3 or cnt.max() > 384
+    assert (int(off[-1]) > 512) == (t == 200)
     y = _gpu(Q, out, wq, 160, k, offsets=off, row_token=rt)
     exp, bound = _oracle(out, wq, k, off, rt)
     _assert_close(y, exp, bound)
