@@ -1,7 +1,8 @@
 """Pins for oracle/moe.py (CPU only): packing against a brute-force bucket
 sort, the GEMM against an exact rational triple loop and against the dense
 product of the compensated activation (Eq. (6) applied to X~ of Eq. (21)),
-SwiGLU against scipy's logistic function, combine against a loop."""
+SwiGLU against scipy's logistic function, combine against the brute-force
+bucket rows (one-hot routing weights) and an exact rational sum."""
 
 from fractions import Fraction
 
@@ -100,6 +101,57 @@ def test_swiglu_against_scipy_and_torch_rounding():
     got = F.bf16_to_f64(h)
     ulp = np.exp2(np.floor(np.log2(np.abs(ref))) - 7)
     assert np.all(np.abs(got - ref) <= ulp / 2 * (1 + 1e-9))
+
+
+def _bucket_row_of(ids, e):
+    """Brute force: the packed row of every (token, slot) pair, filling experts
+    in ascending order and, within an expert, pairs in (token, slot) order."""
+    t, topk = ids.shape
+    row, p = {}, 0
+    for ex in range(e):
+        for tt in range(t):
+            for s in range(topk):
+                if ids[tt, s] == ex:
+                    row[(tt, s)] = p
+                    p += 1
+    return row
+
+
+def test_combine_one_hot_picks_the_bucket_row():
+    """With routing weight 1 on one slot and 0 on the others, token t's output
+    is exactly the expert output row that the brute-force bucket sort gives
+    (t, slot): pins the pos convention (index t * top_k + slot) of combine."""
+    rng = np.random.default_rng(15)
+    for t, e, topk, n in [(9, 5, 3, 6), (17, 16, 8, 4), (1, 1, 1, 3)]:
+        ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+        bucket = _bucket_row_of(ids, e)
+        pos = np.array([bucket[(tt, s)] for tt in range(t) for s in range(topk)], np.int32)
+        y2 = rng.standard_normal((t * topk, n))
+        for s in range(topk):
+            w = np.zeros((t, topk), np.float32)
+            w[:, s] = 1.0
+            out = M.combine(y2, pos, w, t, topk)
+            for tt in range(t):
+                assert np.array_equal(out[tt], y2[bucket[(tt, s)]])
+
+
+def test_combine_exact_rational():
+    """Dyadic expert outputs (multiples of 1/8 below 64) and routing weights
+    (multiples of 1/16 below 1): every partial sum is exact in fp64, so the
+    output equals the exact rational weighted sum over the token's slots."""
+    rng = np.random.default_rng(16)
+    t, e, topk, n = 7, 6, 4, 5
+    ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
+    bucket = _bucket_row_of(ids, e)
+    pos = np.array([bucket[(tt, s)] for tt in range(t) for s in range(topk)], np.int32)
+    y_int = rng.integers(-511, 512, size=(t * topk, n))
+    w_int = rng.integers(0, 16, size=(t, topk))
+    out = M.combine(y_int / 8.0, pos, (w_int / 16.0).astype(np.float32), t, topk)
+    for tt in range(t):
+        for c in range(n):
+            ref = sum(Fraction(int(w_int[tt, s]), 16) * Fraction(int(y_int[bucket[(tt, s)], c]), 8)
+                      for s in range(topk))
+            assert Fraction(float(out[tt, c])) == ref
 
 
 def test_combine_loop():
