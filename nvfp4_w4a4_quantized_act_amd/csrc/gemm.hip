@@ -185,13 +185,25 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     const uint8_t* w_nib_row = g.w_nib + wbase * (g.K / 2);
     const uint8_t* w_sc_row = g.w_scale + wbase * (g.K / kBlock);
 
-    f32x16 acc[2][2], accc[2][2];
+    // acc / accc: the MFMA chains of the main product and the compensation,
+    // restarted every kAccChain channels into the fp32 totals tot / totc
+    f32x16 acc[2][2], accc[2][2], tot[2][2], totc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) { acc[i][j][v] = 0.f; accc[i][j][v] = 0.f; }
+            for (int v = 0; v < 16; ++v) {
+                acc[i][j][v] = 0.f; accc[i][j][v] = 0.f; tot[i][j][v] = 0.f; totc[i][j][v] = 0.f;
+            }
+    auto flush = [](f32x16 (&a)[2][2], f32x16 (&t)[2][2]) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) { t[i][j][v] += a[i][j][v]; a[i][j][v] = 0.f; }
+    };
 
     for (int k0 = 0; k0 < g.K; k0 += kBK) {
         f16x8 va[4], vb[4];
@@ -202,6 +214,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
         store_lds32(sB + lr * kLd + 32 * lh, vb);
         __syncthreads();
         mma_stage(sA, sB, wm, wn, lane, acc);
+        if ((k0 + kBK) % kAccChain == 0 || k0 + kBK >= g.K) flush(acc, tot);
     }
 
     if (g.k > 0) {
@@ -234,6 +247,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
             store_lds32(sB + lr * kLd + 32 * lh, vb);
             __syncthreads();
             mma_stage(sA, sB, wm, wn, lane, accc);
+            if ((i0 + kBK) % kAccChain == 0 || i0 + kBK >= g.k) flush(accc, totc);
         }
     }
 
@@ -252,8 +266,8 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
             float y[2];
 #pragma unroll
             for (int nj = 0; nj < 2; ++nj) {
-                y[nj] = acc[mi][nj][v] * ca_row;
-                if (g.k > 0) y[nj] = fmaf(accc[mi][nj][v], cr, y[nj]);
+                y[nj] = tot[mi][nj][v] * ca_row;
+                if (g.k > 0) y[nj] = fmaf(totc[mi][nj][v], cr, y[nj]);
             }
             if (swiglu) {
                 const int feat = f0 + wn * 32 + (lane & 31);
@@ -697,7 +711,12 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
         const int rc = launch_gemm_decode(g, st);
         if (rc != QUADS_OK || rows <= g.dec_rows) return rc;
     }
-    if (K % v2::BK == 0 && k % v2::BK == 0) {
+    // one accumulator chain is short enough for the error bound: the
+    // 256 x 256-tile kernel; longer chains: the kernels that restart their
+    // accumulators every kAccChain channels
+    const bool one_chain = K + k <= kSingleChainMax;
+    if (!one_chain && gemm_v3_fits(g)) return launch_gemm_v3(g, st);
+    if (one_chain && K % v2::BK == 0 && k % v2::BK == 0) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
                                                           : (N + v2::BN - 1) / v2::BN;
         // M-tiles: at most rows / BM + one partial tile per expert that has

@@ -30,6 +30,10 @@
 // k0 + 64 + 8j + u: both operands take the same channels in the same slots,
 // so the MFMAs sum exactly the products of Eq. (6).
 //
+// Accumulation.  The MFMA accumulators restart from zero every kAccChain
+// channels and are added into fp32 totals (gfx950's f16 MFMA rounds once per
+// group of 8 products, so a chain of 1024 channels is 128 roundings).
+//
 // Compensation.  The weight columns W[n, sel[i]] are taken from the chunks as
 // they stream by (sel ascending: chunk c holds the selected channels in
 // [128c, 128c + 128), a uniform range), converted to fp16 and parked in LDS,
@@ -138,10 +142,12 @@ static __host__ __device__ inline int decode_units_max(const GemmArgs& g) {
 // (Ordering by expert index instead interleaved those idle blocks with the
 // working ones: at the decode step, 16 active experts of 128 took 45 us
 // against 17 us for the same 16 experts alone.)
-// kRing (3 or 4): chunks in flight per wave, chosen so that the chunk count
+// kSplit: accumulators restarted every two ring turns into fp32 totals
+// (chains longer than kSingleChainMax channels).
+// kRing (2, 3 or 4): chunks in flight per wave, chosen so that the chunk count
 // is a multiple of it where it can be (the loads past the last chunk are
 // wasted work).
-template <int kEpi, int kRing>
+template <int kEpi, int kRing, bool kSplit>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     // compensation weight columns, per wave and row block: [row][channel]
@@ -241,11 +247,13 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     for (int c0 = 0; c0 < cnt; c0 += kRows) {
         const bool rv = c0 + r < cnt;
         const int p = p0 + c0 + r;
-        f32x16 acc[2];
+        // acc: the MFMA chain, restarted every kAccChain channels into the
+        // fp32 totals tot (the error bound of split accumulation)
+        f32x16 acc[2], tot[2];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
-            for (int v = 0; v < 16; ++v) acc[q][v] = 0.0f;
+            for (int v = 0; v < 16; ++v) { acc[q][v] = 0.0f; tot[q][v] = 0.0f; }
 
         // The ring: chunk c lives in slot c % kRing (named slots, no array,
         // so everything stays in registers); loads past the last chunk repeat
@@ -272,8 +280,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         lda(aa, 0);
         ldw(w0b, w1b, 1);
         lda(ab, 1);
-        ldw(w0c, w1c, 2);
-        lda(ac, 2);
+        if (kRing >= 3) {
+            ldw(w0c, w1c, 2);
+            lda(ac, 2);
+        }
         if (kRing == 4) {
             ldw(w0d, w1d, 3);
             lda(ad, 3);
@@ -338,12 +348,22 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             ldw(w0, w1, c + kRing);
             lda(a, c + kRing);
         };
+        auto flush = [&]() {
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) { tot[q][v] += acc[q][v]; acc[q][v] = 0.0f; }
+        };
         for (int cb = 0; cb < nch; cb += kRing) {
             step(w0a, w1a, aa, cb);
             step(w0b, w1b, ab, cb + 1);
-            step(w0c, w1c, ac, cb + 2);
+            if (kRing >= 3) step(w0c, w1c, ac, cb + 2);
             if (kRing == 4) step(w0d, w1d, ad, cb + 3);
+            // with split accumulation a chain is two ring turns (4 chunks,
+            // 512 channels); otherwise one chain covers every chunk
+            if (kSplit && ((cb / kRing) & 1)) flush();
         }
+        if (kSplit) flush();
 
         // compensation: captured columns against this pass's residual rows,
         // in the same accumulators once the main product, scaled, has moved
@@ -354,7 +374,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-                ym[q][v] = acc[q][v] * ca_row;
+                ym[q][v] = (kSplit ? tot[q][v] : acc[q][v]) * ca_row;
                 acc[q][v] = 0.0f;
             }
 #pragma unroll
@@ -454,14 +474,25 @@ int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
     const int nch = g.K / dec::kChunk;
     const bool ring3 = nch % 4 != 0 && nch % 3 == 0;
     const bool sw = g.epilogue == QUADS_EPI_SWIGLU;
-    if (sw && ring3)
-        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU, 3>), grid, block, 0, st, g);
-    else if (sw)
-        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_SWIGLU, 4>), grid, block, 0, st, g);
-    else if (ring3)
-        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_NONE, 3>), grid, block, 0, st, g);
-    else
-        hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<QUADS_EPI_NONE, 4>), grid, block, 0, st, g);
+    // a chain longer than kSingleChainMax channels needs split accumulation;
+    // its totals take registers, so that variant keeps two chunks in flight
+    // per wave (two waves per SIMD instead of one: the same loads in flight)
+    const bool split = g.K + g.k > kSingleChainMax;
+#define QUADS_DEC(EPI, RING, SPLIT) \
+    hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<EPI, RING, SPLIT>), grid, block, 0, st, g)
+    if (split) {
+        if (sw) QUADS_DEC(QUADS_EPI_SWIGLU, 2, true);
+        else QUADS_DEC(QUADS_EPI_NONE, 2, true);
+    } else if (sw && ring3) {
+        QUADS_DEC(QUADS_EPI_SWIGLU, 3, false);
+    } else if (sw) {
+        QUADS_DEC(QUADS_EPI_SWIGLU, 4, false);
+    } else if (ring3) {
+        QUADS_DEC(QUADS_EPI_NONE, 3, false);
+    } else {
+        QUADS_DEC(QUADS_EPI_NONE, 4, false);
+    }
+#undef QUADS_DEC
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

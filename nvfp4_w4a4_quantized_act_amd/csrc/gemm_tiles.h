@@ -324,6 +324,21 @@ __device__ __forceinline__ int w_row_v2(int r, int f0, int N, bool swiglu, bool*
 // repeat an expert within a token, or top-1 routing) is then split into
 // work-groups of at most kDecodeMaxRows rows.
 constexpr int kDecodeRowsPerExpert = 32;
+// Channels after which every GEMM kernel restarts its MFMA accumulators and
+// adds them into separate fp32 totals: gfx950's f16 MFMA rounds once per group
+// of 8 products, so a chain of at most 1024 channels is 128 roundings.
+constexpr int kAccChain = 1024;
+// A single accumulator chain of at most this many channels (main product and
+// compensation together) stays within 1e-5 sum|a w|: at most 144 group
+// roundings plus the in-group truncation and the scaling roundings, (144 + 14
+// + 4) 2^-24 < 9.7e-6.  The 256 x 256-tile kernel (one chain) serves those
+// shapes; longer ones go to the kernels with split accumulation.
+constexpr int kSingleChainMax = 1152;
+// Tiled kernel for many rows per expert (gemm_v3.hip): K a multiple of 128,
+// at most kCapMaxV3 compensation channels.
+constexpr int kCapMaxV3 = 256;
+bool gemm_v3_fits(const GemmArgs& g);
+int launch_gemm_v3(const GemmArgs& g, hipStream_t st);
 constexpr int kDecodeMaxRows = 128;
 constexpr int kDecodeAllRows = 512;
 bool gemm_decode_fits(const GemmArgs& g);

@@ -1,0 +1,491 @@
+// Grouped W4A4 GEMM with the RAC compensation term (arXiv 2607.15810, Eq. (6)
+// applied to the compensated activation of Eq. (21)), tiled for many rows per
+// expert and contractions longer than one accumulator chain may be.  Both
+// operands arrive as NVFP4 codes; every v * s_b is an fp16 number (at most 6
+// significant bits, magnitude in [2^-10, 2688]), so the MFMAs (16x16x32 f16,
+// fp32 accumulation) see the exact dequantized values and every product is
+// exact.
+//
+// Accumulation bound.  gfx950's f16 MFMA adds its products in groups of 8
+// (each aligned to the group's largest product, the bits below its last bit
+// dropped) and rounds each group sum once, to nearest even, into the
+// accumulator.  A chain of G groups therefore errs by up to
+// (G + 14) 2^-24 sum|a w| -- over 1e-5 sum|a w| once K exceeds about 1200
+// channels, whatever the MFMA shape.  Here the accumulators restart from
+// zero every 1024 channels (128 groups) and their sums are added into fp32
+// totals; the compensation has a chain of its own.  For K + k channels the
+// error stays below (128 + 14 + (K + k) / 1024 + 4) 2^-24 sum|a w|: under
+// 9.1e-6 sum|a w| up to K + k = 4352, whatever the data.
+//
+// Tile and waves.  The totals double the accumulator registers, which sets
+// the tile: a work-group of 8 waves (two per SIMD) computes 256 packed rows x
+// 128 weight rows (SwiGLU: 64 gate + the 64 matching up rows).  Wave w owns
+// rows 32 w .. 32 w + 31 (two 16-row fragments) against all 128 weight rows
+// (eight fragments): 16 MFMAs per 32-channel step, weights as the first
+// operand so a lane's four accumulators are four consecutive output features
+// of one row; 64 accumulator and 64 total registers per wave.
+//
+// Where the dequantization happens.  An MFMA leaves about 37% of its SIMD's
+// cycles to vector instructions (from either wave); beyond that each
+// conversion costs the MFMA pipe its cycles.  So every code is converted once
+// per work-group:
+//  * activation rows belong to one wave, so their codes go straight from
+//    memory to that wave's registers and are converted there (hardware
+//    fp4 -> fp16 convert, then a packed multiply by the E4M3 block scale);
+//  * weight rows are shared by the eight waves, so each thread converts its
+//    32 codes of the 128 x 128-channel chunk into an fp16 LDS buffer (two
+//    buffers: one read while the next is written).  The buffer holds each
+//    MFMA operand as one 1 KB block in lane order, so every fragment read is
+//    1 KB contiguous (a ds_read_b128 is conflict-free only when each 16-lane
+//    group reads 256 contiguous bytes), and wave w converts rows 16 w ..
+//    16 w + 15, filling one block per store.
+// The codes of chunk c + 1 (activations) and c + 2 (weights) are requested at
+// the top of chunk c, pinned there so the scheduler does not sink them
+// towards their use.  The two waves of a SIMD convert their weight share at
+// opposite ends of the chunk, so one's conversions overlap the other's MFMAs.
+//
+// Channel order.  Within a 128-channel chunk, lane group q (lanes 16 q ..
+// 16 q + 15) of step s holds channels 32 q + 8 s .. 32 q + 8 s + 7 for both
+// operands, so a lane's 32 activation codes of a chunk are one 16-byte load
+// and every MFMA contracts the products of Eq. (6) in matching pairs.
+//
+// Compensation.  The weight columns of the selected channels, W[:, S], are
+// copied (as fp16) out of each staged weight chunk into an LDS buffer as the
+// chunks go by; after the main chunks, R x W[:, S] runs in the accumulators
+// (restarted from zero) and the epilogue forms
+//   Y = totals * s_tA s_tW[e] + acc * s_tR s_tW[e].
+#include "common.h"
+#include "gemm_tiles.h"
+
+namespace quads {
+namespace v3 {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int BM = 256;              // packed rows per tile
+constexpr int BN = 128;              // weight rows per tile
+constexpr int BK = 128;              // channels per chunk
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kFlush = 8;            // chunks per accumulation segment (1024 channels)
+constexpr int kCapLd = kCapMaxV3 + 8;  // halfs per captured row (16-byte pad)
+
+// Activation codes of one chunk for the lane's two row fragments: channels
+// 32 q .. 32 q + 31 (16 bytes) and the scale bytes of blocks 2 q, 2 q + 1.
+struct ARaw {
+    uint4 c[2];
+    uint32_t s[2];
+};
+// Weight codes of one chunk for one thread: channels 32 h .. 32 h + 31 of
+// one weight row (16 bytes) and the scale bytes of blocks 2 h, 2 h + 1.
+struct WRaw {
+    uint4 c;
+    uint32_t s;
+};
+
+__device__ __forceinline__ uint32_t word4(const uint4& v, int j) {
+    return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
+}
+
+// 8 codes (one dword) times an fp16 block scale -> 8 exact fp16 values.
+__device__ __forceinline__ f16x8 cvt8(uint32_t w, _Float16 s) {
+    const f16x2 s2 = {s, s};
+    const f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+    const f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+    const f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+    const f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+    return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Weight chunk layout in LDS: the MFMA operand of weight fragment n (rows
+// 16 n .. 16 n + 15) at step s is one 1 KB block, lane l's 16 bytes at
+// l * 16 (row 16 n + l % 16, channels 32 (l / 16) + 8 s .. + 7), so every
+// fragment read is 1 KB contiguous (each 16-lane group reads 256 contiguous
+// bytes: no bank conflict).  Block (n, s) sits at (4 n + s) KB.
+__device__ __forceinline__ int wblock_off(int row, int ch) {      // bytes, ch % 8 == 0
+    const int n = row >> 4, r = row & 15, q = ch >> 5, s = (ch >> 3) & 3;
+    return ((4 * n + s) * 64 + 16 * q + r) * 16;
+}
+
+struct Ctx {
+    // activation rows: per fragment, byte offsets of the lane's codes and
+    // scales of chunk 0
+    const uint8_t* a_nib;
+    const uint8_t* a_sc;
+    int64_t a_off[2], s_off[2];
+    // weight row of this thread: codes and scales of chunk 0
+    const uint8_t* w_nib;
+    const uint8_t* w_sc;
+    int nk;                   // chunks
+};
+
+template <int MACT>
+__device__ __forceinline__ void load_a(const Ctx& x, int c, ARaw& r) {
+    const int cc = c < x.nk ? c : x.nk - 1;            // past the end: a redundant load
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        if (f < MACT) {
+            r.c[f] = *reinterpret_cast<const uint4*>(x.a_nib + x.a_off[f] + 64 * cc);
+            r.s[f] = *reinterpret_cast<const uint16_t*>(x.a_sc + x.s_off[f] + 8 * cc);
+        }
+    }
+}
+
+__device__ __forceinline__ void load_w(const Ctx& x, int c, WRaw& r) {
+    const int cc = c < x.nk ? c : x.nk - 1;
+    r.c = *reinterpret_cast<const uint4*>(x.w_nib + 64 * cc);
+    r.s = *reinterpret_cast<const uint16_t*>(x.w_sc + 8 * cc);
+}
+
+// Convert this thread's weight codes of a chunk (row wr, channels 32 h ..
+// 32 h + 31) into the LDS chunk buffer at byte address `wb`: piece j is
+// channels 32 h + 8 j .. + 7, block (wr / 16, j), lane 16 h + wr % 16.  The 16
+// threads of rows 16 i .. 16 i + 15 store 256 contiguous bytes.
+__device__ __forceinline__ void store_w(const WRaw& r, char* wb, int wr, int h) {
+    const f16x2 s01 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.s, 1.0f, false);
+    char* base = wb + wblock_off(wr, 32 * h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        *reinterpret_cast<f16x8*>(base + j * 1024) = cvt8(word4(r.c, j), s01[j >> 1]);
+}
+
+// Weight fragments of step s of the chunk in buffer `wb` (this lane's bytes).
+__device__ __forceinline__ void read_wf(const char* wb_lane, int s, f16x8 wf[8]) {
+#pragma unroll
+    for (int n = 0; n < 8; ++n)
+        wf[n] = *reinterpret_cast<const f16x8*>(wb_lane + (4 * n + s) * 1024);
+}
+
+// MFMAs of one 32-channel step into accumulator set `acc`: activation
+// fragments converted from the lane's codes (word s of each fragment's 16
+// bytes, the block scale of block 2 q + s / 2).
+template <int MACT>
+__device__ __forceinline__ void mma_step(const f16x8 wf[8], const ARaw& ra, int s,
+                                         f32x4 acc[2][8]) {
+#pragma unroll
+    for (int f = 0; f < MACT; ++f) {
+        const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(ra.s[f], 1.0f, false);
+        const f16x8 af = cvt8(word4(ra.c[f], s), s < 2 ? sc[0] : sc[1]);
+#pragma unroll
+        for (int n = 0; n < 8; ++n)
+            acc[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[n], af, acc[f][n], 0, 0, 0);
+    }
+}
+
+template <int MACT>
+__device__ __forceinline__ void add_set(f32x4 dst[2][8], const f32x4 src[2][8]) {
+#pragma unroll
+    for (int f = 0; f < MACT; ++f)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) dst[f][n] = dst[f][n] + src[f][n];
+}
+
+template <int MACT>
+__device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int n = 0; n < 8; ++n) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
+}
+
+template <int kEpi, int MACT, bool LATE>
+__device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
+                                         const int* s_sel, const Ctx& x, int wr, int wh,
+                                         int kc, int wave, int lane, const int64_t src[2],
+                                         int m0, int mend, int f0, int e) {
+    // The MFMA accumulators X restart from zero every kFlush chunks (1024
+    // channels); their sums are added into the fp32 totals T.
+    f32x4 X[2][8], T[2][8];
+    zero_set<MACT>(X);
+    zero_set<MACT>(T);
+    const int nk = x.nk;
+    const char* wb_lane = wbuf + lane * 16;
+    // capture bookkeeping (uniform): selected channels ci .. ce - 1 lie in
+    // the chunks seen so far
+    int ci = 0;
+    const int cap_row = threadIdx.x & (BN - 1), cap_par = threadIdx.x >> 7;   // capture roles
+    auto capture = [&](const char* wb, int c) {
+        if (kc == 0) return;
+        int ce = ci;
+        while (ce < kc && s_sel[ce] < BK * (c + 1)) ++ce;
+        for (int i = ci + cap_par; i < ce; i += kThreads / BN) {
+            int ch = s_sel[i] - BK * c;
+            ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);     // bounds only: sel ascending
+            cap[cap_row * kCapLd + i] = *reinterpret_cast<const _Float16*>(
+                wb + wblock_off(cap_row, ch & ~7) + 2 * (ch & 7));
+        }
+        ci = ce;
+    };
+
+    ARaw a0, a1;
+    WRaw w0, w1;
+    // prologue: chunk 0's codes and chunk 1's weight codes requested, chunk
+    // 0's weights converted
+    load_w(x, 0, w0);
+    load_a<MACT>(x, 0, a0);
+    load_w(x, 1, w1);
+    store_w(w0, wbuf, wr, wh);
+    __syncthreads();
+
+    // chunk c: activation codes of c + 1 and weight codes of c + 2 requested
+    // (chunk c - 1's activation slot and chunk c's weight slot, converted in
+    // chunk c - 1, are free); chunk c + 1's weights converted into the other
+    // buffer after step 0; weight fragments read one step ahead of the MFMAs
+    auto chunk = [&](int c, ARaw& ac, ARaw& an, WRaw& wn, WRaw& wn2) {
+        if (c >= nk) return;
+        load_a<MACT>(x, c + 1, an);
+        load_w(x, c + 2, wn2);
+        // keep the requests here, a whole chunk ahead of their use (left to
+        // itself the scheduler sinks them towards their use and the chunk
+        // then waits on their latency)
+        __builtin_amdgcn_sched_barrier(0);
+        const char* wb = wb_lane + (c & 1) * (BN * BK * 2);
+        // the two waves of a SIMD (w and w + 4) convert their weight share at
+        // opposite ends of the chunk, so one's conversions overlap the other's
+        // MFMAs
+        char* wnext = wbuf + ((c + 1) & 1) * (BN * BK * 2);
+        if (LATE && c + 1 < nk) store_w(wn, wnext, wr, wh);
+        f16x8 wf[8];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (MACT > 0) read_wf(wb, st, wf);
+            mma_step<MACT>(wf, ac, st, X);
+        }
+        if (!LATE && c + 1 < nk) store_w(wn, wnext, wr, wh);
+        capture(wbuf + (c & 1) * (BN * BK * 2), c);
+        if ((c + 1) % kFlush == 0 || c + 1 == nk) {
+            add_set<MACT>(T, X);
+            zero_set<MACT>(X);
+        }
+        __syncthreads();
+    };
+    for (int c = 0; c < nk; c += 2) {
+        chunk(c, a0, a1, w1, w0);
+        chunk(c + 1, a1, a0, w0, w1);
+    }
+
+    // compensation: R x W[:, S] into X (zero), from the captured columns
+    const float s_tr = g.k > 0 ? g.r_ts[0] : 0.0f;
+    const bool comp = kc > 0 && s_tr > 0.0f;
+    if (comp && MACT > 0) {
+        const int r = lane & 15, q = lane >> 4;
+        const int nsteps = (kc + 31) / 32;
+        for (int s = 0; s < nsteps; ++s) {
+            f16x8 wf[8];
+#pragma unroll
+            for (int n = 0; n < 8; ++n)
+                wf[n] = *reinterpret_cast<const f16x8*>(cap + (16 * n + r) * kCapLd + 32 * s + 8 * q);
+            const int ch = 32 * s + 8 * q;            // first channel of the lane's 8
+#pragma unroll
+            for (int f = 0; f < MACT; ++f) {
+                uint32_t code = 0u, sb = 0u;
+                if (ch < kc) {
+                    code = *reinterpret_cast<const uint32_t*>(g.r_nib + src[f] * (g.k / 2) + ch / 2);
+                    sb = g.r_scale[src[f] * (g.k / kBlock) + ch / kBlock];
+                }
+                const f16x8 rf = cvt8(code, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false)[0]);
+#pragma unroll
+                for (int n = 0; n < 8; ++n)
+                    X[f][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[n], rf, X[f][n], 0, 0, 0);
+            }
+        }
+    }
+
+    // epilogue: y = T s_tA s_tW + X s_tR s_tW
+    if (MACT == 0) return;
+    const float s_tw = g.w_ts[e];
+    const float ca0 = tensor_scale_a(g) * s_tw;
+    const float cr = comp ? s_tr * s_tw : 0.0f;
+    const int r = lane & 15, q = lane >> 4;
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int prow0 = m0 + 32 * wave + r;
+    if (swiglu) {
+        const int nh = g.N / 2;
+        bool need = false;
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            if (pass == 1 && __ballot(need) == 0ull) break;
+#pragma unroll
+            for (int f = 0; f < MACT; ++f) {
+                const int prow = prow0 + 16 * f;
+                if (prow >= mend) continue;
+                const float ca = g.a_ts_rows ? g.a_ts_rows[src[f]] * s_tw : ca0;
+#pragma unroll
+                for (int n = 0; n < 4; ++n) {
+                    float hv[4];
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const float gt = fmaf(X[f][n][v], cr, T[f][n][v] * ca);
+                        const float up = fmaf(X[f][n + 4][v], cr, T[f][n + 4][v] * ca);
+                        if (pass == 0) {
+                            hv[v] = silu_mul_short(gt, up);
+                            need = need || silu_a(gt) > kSiluShortMaxA;
+                        } else {
+                            hv[v] = silu_mul_full(gt, up);
+                        }
+                    }
+                    const int feat = f0 + 16 * n + 4 * q;
+                    const uint32_t p01 = v2::pk_bf16(hv[0], hv[1]), p23 = v2::pk_bf16(hv[2], hv[3]);
+                    uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
+                    if (feat + 3 < nh && (nh & 3) == 0) {
+                        *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                    } else {
+                        const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+#pragma unroll
+                        for (int u = 0; u < 4; ++u)
+                            if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                    }
+                }
+            }
+        }
+        return;
+    }
+#pragma unroll
+    for (int f = 0; f < MACT; ++f) {
+        const int prow = prow0 + 16 * f;
+        if (prow >= mend) continue;
+        const float ca = g.a_ts_rows ? g.a_ts_rows[src[f]] * s_tw : ca0;
+#pragma unroll
+        for (int n = 0; n < 8; ++n) {
+            float y[4];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) y[v] = fmaf(X[f][n][v], cr, T[f][n][v] * ca);
+            const int nf = f0 + 16 * n + 4 * q;
+            const int64_t o = (int64_t)prow * g.N + nf;
+            const bool vec = nf + 3 < g.N && (g.N & 3) == 0;
+            if (g.out_bf16) {
+                uint16_t* ob = (uint16_t*)g.out + o;
+                const uint32_t p01 = v2::pk_bf16(y[0], y[1]), p23 = v2::pk_bf16(y[2], y[3]);
+                if (vec) {
+                    *reinterpret_cast<uint2*>(ob) = make_uint2(p01, p23);
+                } else {
+                    const uint32_t b4[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (nf + u < g.N) ob[u] = (uint16_t)b4[u];
+                }
+            } else {
+                float* of = (float*)g.out + o;
+                if (vec) {
+                    *reinterpret_cast<float4*>(of) = make_float4(y[0], y[1], y[2], y[3]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 4; ++u)
+                        if (nf + u < g.N) of[u] = y[u];
+                }
+            }
+        }
+    }
+}
+
+template <int kEpi>
+__global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n, int grp) {
+    __shared__ __align__(16) char wbuf[2 * BN * BK * 2];
+    __shared__ __align__(16) _Float16 cap[BN * kCapLd];
+    __shared__ int s_sel[kCapMaxV3];
+    // XCD-aware numbering: hardware id h runs on XCD h % 8; tiles are dealt in
+    // groups of `grp` consecutive tiles (M-tile major: one M tile's N tiles
+    // share its activation rows) per XCD
+    const int h = blockIdx.x;
+    const int slot = h / v2::kXcds;
+    const int tile = (slot / grp) * (v2::kXcds * grp) + (h % v2::kXcds) * grp + slot % grp;
+    const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
+    int e, m0, mend;
+    if (!v2::find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows))
+        return;
+    bind_expert(g, e);
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int f0 = tile_n * (swiglu ? BN / 2 : BN);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // this thread's weight row and quarter (chunk loads and conversion):
+    // wave w takes rows 16 w .. 16 w + 15 (lane l: row 16 w + l % 16, channels
+    // 32 (l / 16) ..), so its loads read whole 64-byte row pieces and its fp16
+    // stores fill one 1 KB block in lane order
+    const int wr = 16 * (tid >> 6) + (tid & 15), wh = (tid >> 4) & 3;   // channels 32 wh ..
+    int wrow;
+    bool wvalid;
+    if (swiglu) {
+        const int feat = f0 + (wr & 63);
+        wvalid = feat < g.N / 2;
+        wrow = (wr >> 6) * (g.N / 2) + feat;
+    } else {
+        wrow = f0 + wr;
+        wvalid = wrow < g.N;
+    }
+    const int64_t wfull = (int64_t)e * g.N + (wvalid ? wrow : 0);
+    Ctx x;
+    x.nk = g.K / BK;
+    x.w_nib = g.w_nib + wfull * (g.K / 2) + 16 * wh;
+    x.w_sc = g.w_scale + wfull * (g.K / kBlock) + 2 * wh;
+    // the lane's activation rows (a row past the tile reads row 0; its
+    // results are never stored)
+    const int r = lane & 15, q = lane >> 4;
+    int64_t src[2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f) {
+        const int p = m0 + 32 * wave + 16 * f + r;
+        src[f] = p < mend ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
+        x.a_off[f] = src[f] * (g.K / 2) + 16 * q;
+        x.s_off[f] = src[f] * (g.K / kBlock) + 2 * q;
+    }
+    x.a_nib = g.a_nib;
+    x.a_sc = g.a_scale;
+
+    // compensation: selected channels to LDS, padding columns of the capture
+    // buffer zeroed (a step reads 32 columns)
+    const int kc = g.k;
+    if (kc > 0) {
+        for (int i = tid; i < kc; i += kThreads) s_sel[i] = g.sel[i];
+        const int kpad = (kc + 31) & ~31;
+        for (int i = tid; i < BN * (kpad - kc); i += kThreads)
+            cap[(i / (kpad - kc)) * kCapLd + kc + i % (kpad - kc)] = (_Float16)0.0f;
+    }
+    __syncthreads();
+
+    int mact = (mend - (m0 + 32 * wave) + 15) / 16;
+    mact = __builtin_amdgcn_readfirstlane(mact < 0 ? 0 : (mact > 2 ? 2 : mact));
+    switch (mact + (wave >= 4 ? 4 : 0)) {
+#define QUADS_V3_TILE(M, L)                                                                     \
+    case M + (L ? 4 : 0):                                                                       \
+        run_tile<kEpi, M, L>(g, wbuf, cap, s_sel, x, wr, wh, kc, wave, lane, src, m0, mend, f0, e); \
+        break;
+        QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)
+        QUADS_V3_TILE(1, true) QUADS_V3_TILE(0, true)
+        default: QUADS_V3_TILE(0, false)
+#undef QUADS_V3_TILE
+    }
+}
+
+}  // namespace v3
+
+bool gemm_v3_fits(const GemmArgs& g) {
+    return g.K % v3::BK == 0 && g.k <= kCapMaxV3 && (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+}
+
+int launch_gemm_v3(const GemmArgs& g, hipStream_t st) {
+    const bool sw = g.epilogue == QUADS_EPI_SWIGLU;
+    const int64_t nt_n = sw ? (g.N / 2 + v3::BN / 2 - 1) / (v3::BN / 2) : (g.N + v3::BN - 1) / v3::BN;
+    // M-tiles: at most rows / BM + one partial tile per expert that has tiles
+    // (with a decode share, only experts above g.dec_rows rows)
+    const int64_t big = g.dec_rows > 0 ? g.rows / (g.dec_rows + 1) : g.E;
+    const int64_t nt_m = (g.rows + v3::BM - 1) / v3::BM + (g.offsets ? (big < g.E ? big : g.E) : 0);
+    const int64_t grp = 2 * nt_n;
+    const int64_t span = grp * v2::kXcds;
+    const int64_t blocks = (nt_m * nt_n + span - 1) / span * span;
+    if (blocks >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
+    const dim3 grid((unsigned)blocks);
+    if (sw)
+        hipLaunchKernelGGL(v3::k_gemm_w4a4_v3<QUADS_EPI_SWIGLU>, grid, dim3(v3::kThreads), 0, st, g,
+                           (int)nt_n, (int)grp);
+    else
+        hipLaunchKernelGGL(v3::k_gemm_w4a4_v3<QUADS_EPI_NONE>, grid, dim3(v3::kThreads), 0, st, g,
+                           (int)nt_n, (int)grp);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+}  // namespace quads
