@@ -18,23 +18,36 @@ forward pass; it is timed on its own and reported as `weight_qdq_ms`.
 
 Inputs are seeded synthetic tensors (synth.py) already resident in HBM when
 the timed region starts.  `value` is the step's algorithmic GEMM work,
-2 * rows * N * (K + k) summed over both GEMMs, divided by the step time.
-`roofline` is for the dominant kernel, the gate/up GEMM: its algorithmic
-flops per launch over its mean launch time (a pair of HIP events on the
-launch stream around it in every timed step; an event record leaves the GPU
-idle for a few microseconds, so the other per-op times in `ops` come from
-extra steps after the timed region), against the dense fp16 MFMA peak (the GEMM's operands are exact fp16);
-`traffic` is its HBM-side bytes per launch from the FETCH_SIZE / WRITE_SIZE
-counter summary under profiles/ (null when that summary was taken on other
-GEMM sources).  `cpu_baseline` times the NumPy oracle on a bounded sample of
-the same layer.  `comparator` times the same gate/up GEMM as an MX
-block-scaled GEMM with FP8 and with FP4 elements (quads_moe_mx_gemm), the
-FP8 W8A8 baseline the paper's speed claim is measured against, next to the
-W4A4+RAC GEMM.  `decode` runs the same layer at the decode step (64 tokens,
-Zipf routing, most experts with 0-2 rows), where the GEMMs are bound by the
-active experts' weight bytes.
+2 * rows * N * (K + k) summed over both GEMMs, divided by the step time of
+back-to-back steps.  `roofline` is for the dominant kernel, the gate/up GEMM:
+its algorithmic flops per launch over its mean launch time (a pair of HIP
+events on the launch stream around it in every timed step; an event record
+leaves the GPU idle for a few microseconds, so the other per-op times in
+`ops` come from extra steps after the timed region), against the dense fp16
+MFMA peak (the GEMM's operands are exact fp16); `traffic` is its HBM-side
+bytes per launch from the FETCH_SIZE / WRITE_SIZE counter summary under
+profiles/ (null when that summary was taken on other GEMM sources).
 
-    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline]
+Cold figures (`cold`): before each timed call or step a 512 MiB buffer is
+written, which evicts the 256 MB last-level cache and the L2s, and an event
+pair brackets the call (median and min over the reps).  The quantizer's cold
+rate instead cycles through copies of its input spaced at least 512 MiB
+apart, back to back, so no event gap enters its 20-50 us calls.
+
+Other workloads: `config2` (dense 4096 x 4096 x 4096 linear, k = 128),
+`config5` (64 experts, hidden 4096, intermediate 1536, 16384 tokens: the
+gate/up RAC and GEMM at k = 0, 64, 256 and 2048 = 50% of the channels, and
+the quantizer on the down-site input, the 131072 x 1536 SwiGLU output),
+`rac_overhead` (the step with plain NVFP4 at both sites, k = 0, beside the
+RAC step), `decode` (the same layer at the decode step: 64 tokens, Zipf
+routing), `comparator` (the gate/up GEMM as MXFP8 and MXFP4),
+`per_expert_selection`, and `cpu_baseline` (the NumPy oracle on a bounded
+sample of the layer).
+
+    python bench.py [--steps K] [--warmup W] [--no-cpu-baseline] [--layer-only]
+    python bench.py --traffic-from FETCH_DIR WRITE_DIR --copy-probe-mib N
+    python bench.py --trace-from TRACE_DIR
+    python bench.py --pmc-from DIR [DIR ...]
 """
 
 import argparse
@@ -48,9 +61,12 @@ PEAK_HBM_GBS = 8000.0            # MI355X HBM3E
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_gemm_gate_up_traffic.md")
+TRACE_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_kernel_trace.md")
+PMC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_counters.md")
 GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_quantized_act_amd", "csrc", f)
-                for f in ("gemm.hip", "gemm_tiles.h", "common.h")]
-GEMM_KERNEL_KEY = "k_gemm_w4a4_v2<1>"     # the gate/up (SwiGLU) GEMM kernel
+                for f in ("gemm.hip", "gemm_v3.hip", "gemm_tiles.h", "common.h")]
+GEMM_KERNEL_KEY = "k_gemm_w4a4_v3<1>"     # the gate/up (SwiGLU) GEMM kernel
+FLUSH_BYTES = 512 << 20
 
 
 def _parse():
@@ -62,9 +78,17 @@ def _parse():
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a device copy of this size (for counter calibration)")
+    ap.add_argument("--layer-only", action="store_true",
+                    help="only the prefill layer's steps (for counter runs)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE) of "
                          "`bench.py --copy-probe-mib N` into the traffic summary under profiles/")
+    ap.add_argument("--trace-from", metavar="TRACE_DIR",
+                    help="no GPU: turn a rocprofv3 --kernel-trace run of bench.py into the "
+                         "per-kernel, per-launch-shape summary under profiles/")
+    ap.add_argument("--pmc-from", nargs="+", metavar="DIR",
+                    help="no GPU: turn rocprofv3 --pmc runs of `bench.py --layer-only` into "
+                         "the counter summary under profiles/")
     return ap.parse_args()
 
 
@@ -133,10 +157,10 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
         "```",
         f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc FETCH_SIZE "
         f"--output-format csv -d $REPO/gpurun_out/pmc_fetch -o f -- python -u $REPO/bench.py "
-        f"--steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"--steps 2 --warmup 1 --no-cpu-baseline --layer-only --copy-probe-mib {copy_mib}",
         f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 120 rocprofv3 --pmc WRITE_SIZE "
         f"--output-format csv -d $REPO/gpurun_out/pmc_write -o w -- python -u $REPO/bench.py "
-        f"--steps 2 --warmup 1 --no-cpu-baseline --copy-probe-mib {copy_mib}",
+        f"--steps 2 --warmup 1 --no-cpu-baseline --layer-only --copy-probe-mib {copy_mib}",
         f"python bench.py --traffic-from gpurun_out/pmc_fetch gpurun_out/pmc_write "
         f"--copy-probe-mib {copy_mib}",
         "```",
@@ -161,6 +185,165 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
     print("\n".join(lines))
 
 
+def _short_name(name):
+    """Kernel name without the return type, the library namespace and the
+    argument list: `v3::k_gemm_w4a4_v3<1>`."""
+    name = name.strip()
+    if name.startswith("void "):
+        name = name[5:]
+    depth = 0
+    for i, ch in enumerate(name):
+        if ch == "<":
+            depth += 1
+        elif ch == ">":
+            depth -= 1
+        elif ch == "(" and depth == 0:
+            name = name[:i]
+            break
+    return name.replace("quads::", "")
+
+
+def trace_summary(trace_dir):
+    """Per kernel and launch shape (work-groups in x and y, threads per
+    work-group): calls and start-to-end durations from a rocprofv3
+    --kernel-trace run of the default benchmark."""
+    import csv
+    import glob
+    groups = {}
+    for f in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                wx, wy = int(r["Workgroup_Size_X"]), int(r["Workgroup_Size_Y"])
+                wz = int(r["Workgroup_Size_Z"])
+                key = (_short_name(r["Kernel_Name"]), int(r["Grid_Size_X"]) // wx,
+                       int(r["Grid_Size_Y"]) // wy, wx * wy * wz)
+                dt = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                groups.setdefault(key, []).append(dt)
+    if not groups:
+        raise SystemExit(f"no kernel_trace.csv under {trace_dir}")
+    total = sum(sum(v) for v in groups.values())
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    lines = [
+        "# Kernel trace: MoE FFN layer, 128 experts, T=4096, hidden 2048, intermediate 768, "
+        "top-8, RAC k=64, with the benchmark's other workloads",
+        "",
+        "Commands (repository root, one MI355X; `$REPO` is the repository root), then this "
+        "summary on any host:",
+        "",
+        "```",
+        "cd /tmp && export TMPDIR=/tmp && timeout -k 10 900 rocprofv3 --kernel-trace --stats "
+        "--output-format csv -d $REPO/gpurun_out/prof_trace -o bench -- python -u "
+        "$REPO/bench.py --steps 10 --warmup 3 --no-cpu-baseline",
+        "python bench.py --trace-from gpurun_out/prof_trace",
+        "```",
+        "",
+        "Durations are the trace's start-to-end times in microseconds, grouped by kernel and "
+        "launch shape (work-groups in x and y, threads per work-group), so that launches of one "
+        "kernel on different workloads show apart.  The prefill layer's gate/up GEMM is "
+        "`v3::k_gemm_w4a4_v3<1>` at (1536, 1) x 512 (128 experts, 256-row by 64-feature "
+        "tiles); config 5's gate/up GEMMs are the same kernel at larger grids, config 2's the "
+        "`<0>` instance.",
+        "",
+        "| kernel | work-groups (x, y) x threads | calls | total (us) | average (us) | min (us) | "
+        "max (us) | % |",
+        "|---|---|---|---|---|---|---|---|",
+    ]
+    for (name, gx, gy, th), v in rows[:60]:
+        lines.append(f"| `{name}` | ({gx}, {gy}) x {th} | {len(v)} | {sum(v):.1f} | "
+                     f"{sum(v) / len(v):.2f} | {min(v):.2f} | {max(v):.2f} | "
+                     f"{100 * sum(v) / total:.1f} |")
+    if len(rows) > 60:
+        lines.append(f"| ({len(rows) - 60} more groups) | | | "
+                     f"{sum(sum(v) for _, v in rows[60:]):.1f} | | | | |")
+    lines += ["", f"gemm_source_sha256: {_gemm_source_hash()}", ""]
+    with open(TRACE_FILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
+PMC_PASSES = (
+    "SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_F16 SQ_INSTS_VALU "
+    "SQ_INSTS_MFMA SQ_VALU_MFMA_COEXEC_CYCLES SQ_WAVE_CYCLES SQ_WAIT_INST_ANY GRBM_GUI_ACTIVE",
+    "SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_LDS_BANK_CONFLICT SQ_INSTS_VMEM_RD SQ_INSTS_VMEM_WR "
+    "SQ_ACTIVE_INST_VALU SQ_WAIT_ANY SQ_INST_LEVEL_VMEM GRBM_GUI_ACTIVE",
+)
+
+
+def pmc_summary(dirs):
+    """Per-dispatch counter means for the layer's kernels from rocprofv3 --pmc
+    runs of `bench.py --layer-only`, with the derived MFMA-busy fraction and
+    LDS conflict rate."""
+    import csv
+    import glob
+    per = {}
+    for d in dirs:
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    key = (_short_name(r["Kernel_Name"]), int(r["Grid_Size"]))
+                    disp = (f, r["Dispatch_Id"])
+                    c = per.setdefault(key, {}).setdefault(r["Counter_Name"], {})
+                    c[disp] = c.get(disp, 0.0) + float(r["Counter_Value"])
+    if not per:
+        raise SystemExit("no counter_collection.csv found")
+    n_xcd, n_simd = 8, 1024
+    lines = [
+        "# Hardware counters: MoE FFN layer (128 experts, T=4096, hidden 2048, intermediate 768, "
+        "top-8, RAC k=64) and the quantizer on a [16384, 4096] input",
+        "",
+        "Commands (repository root, one MI355X; `$REPO` is the repository root), one run per "
+        "counter pass, then this summary on any host:",
+        "",
+        "```",
+    ]
+    for i, ctrs in enumerate(PMC_PASSES):
+        lines.append(f"cd /tmp && export TMPDIR=/tmp && timeout -s KILL 180 rocprofv3 --pmc "
+                     f"{ctrs} --output-format csv -d $REPO/gpurun_out/pmc_{'ab'[i]} -o p -- "
+                     f"python -u $REPO/bench.py --steps 2 --warmup 1 --no-cpu-baseline "
+                     f"--layer-only")
+    lines += [
+        "python bench.py --pmc-from gpurun_out/pmc_a gpurun_out/pmc_b",
+        "```",
+        "",
+        "Values are means per dispatch over the runs' dispatches of each kernel and grid size "
+        "(threads).  `GRBM_GUI_ACTIVE` counts GPU-busy cycles summed over the 8 XCDs; "
+        "`SQ_VALU_MFMA_BUSY_CYCLES` counts busy cycles of the MFMA unit summed over the 1024 "
+        "SIMDs.  Derived: MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 x 1024); "
+        "f16 MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_F16 x 512; LDS conflict = "
+        "SQ_LDS_BANK_CONFLICT / SQ_ACTIVE_INST_LDS (cycles stalled on bank conflicts per cycle "
+        "of issued LDS instructions); VALU per MFMA = SQ_INSTS_VALU / SQ_INSTS_MFMA.",
+        "",
+        "| kernel | grid (threads) | dispatches | MFMA busy | f16 MFMA GFLOP | VALU / MFMA | "
+        "LDS conflict | VMEM rd | VMEM wr |",
+        "|---|---|---|---|---|---|---|---|---|",
+    ]
+
+    def mean(c, name):
+        v = c.get(name)
+        return sum(v.values()) / len(v) if v else float("nan")
+
+    order = sorted(per.items(), key=lambda kv: -mean(kv[1], "GRBM_GUI_ACTIVE"))
+    for (name, grid), c in order:
+        gui = mean(c, "GRBM_GUI_ACTIVE")
+        busy = mean(c, "SQ_VALU_MFMA_BUSY_CYCLES") / (gui / n_xcd * n_simd)
+        mops = mean(c, "SQ_INSTS_VALU_MFMA_MOPS_F16") * 512 / 1e9
+        mfma = mean(c, "SQ_INSTS_MFMA")
+        valu_per = mean(c, "SQ_INSTS_VALU") / mfma if mfma else float("nan")
+        lds_c = mean(c, "SQ_LDS_BANK_CONFLICT") / max(mean(c, "SQ_ACTIVE_INST_LDS"), 1.0)
+        nd = max(len(v) for v in c.values())
+        lines.append(f"| `{name}` | {grid} | {nd} | {busy:.3f} | {mops:.1f} | "
+                     f"{valu_per:.2f} | {lds_c:.3f} | {mean(c, 'SQ_INSTS_VMEM_RD'):.3g} | "
+                     f"{mean(c, 'SQ_INSTS_VMEM_WR'):.3g} |")
+    lines += ["", "Raw means per dispatch:", ""]
+    for (name, grid), c in order:
+        lines.append(f"- `{name}` grid {grid}: " + ", ".join(
+            f"{k} {mean(c, k):.4g}" for k in sorted(c)))
+    lines += ["", f"gemm_source_sha256: {_gemm_source_hash()}", ""]
+    with open(PMC_FILE, "w") as fh:
+        fh.write("\n".join(lines))
+    print("\n".join(lines))
+
+
 def measured_traffic():
     """Traffic bytes per launch from the committed counter summary, or None when
     it is missing or was taken on a different GEMM source."""
@@ -180,6 +363,12 @@ def main():
     args = _parse()
     if args.traffic_from:
         traffic_summary(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 512)
+        return
+    if args.trace_from:
+        trace_summary(args.trace_from)
+        return
+    if args.pmc_from:
+        pmc_summary(args.pmc_from)
         return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
@@ -238,6 +427,7 @@ def main():
     # per-op breakdown comes from extra steps after the timed region.
     nev = 7
     timers, gemm_timers = [], []
+    last = {}
 
     def step(mode):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)] if mode else None
@@ -263,6 +453,7 @@ def main():
         mark(5)
         out = Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
         mark(6)
+        last.update(a=a, off=off, rt=rt)
         if mode == "all":
             timers.append(evs)
         elif mode == "gemm":
@@ -311,11 +502,52 @@ def main():
     for k in ("rac_gate_up", "rac_down"):
         ops[k]["hbm_frac"] = ops[k]["GB/s"] / PEAK_HBM_GBS
 
-    quant = quantizer_rate(np, torch, Q, synth, dev)
-    decode = decode_layer(np, torch, Q, synth, dev, w13q, w2q)
-    comparator = mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx,
-                               per_op["gemm_gate_up_swiglu"], fl_gu)
-    per_expert = per_expert_down(torch, Q, x, ids, E, I, H, KR, rows, w13q, w2q)
+    _progress("timed steps done")
+    # cold: a 512 MiB write before each step (and before each lone GEMM call)
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    la = last["a"]
+
+    def gate_up_alone():
+        return Q.quads_moe_w4a4_gemm((la["nib"], la["scale"], la["ts"]), w13q, 2 * I, rows=rows,
+                                     r=(la["r_nib"], la["r_scale"], la["r_ts"]), sel=la["sel"],
+                                     offsets=last["off"], row_token=last["rt"],
+                                     epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+    cold_step = _cold_us(torch, lambda: step(None), flush, 20)
+    cold_gemm = _cold_us(torch, gate_up_alone, flush, 20)
+    warm_gemm_us = _back_to_back_us(torch, gate_up_alone, 20)
+    cold = {
+        "protocol": "512 MiB buffer written before each call, event pair around the call",
+        "layer_step_ms": {"median": cold_step["median_us"] / 1e3,
+                          "min": cold_step["min_us"] / 1e3, "reps": 20},
+        "layer_value_TFLOP/s": (fl_gu + fl_dn) / (cold_step["median_us"] * 1e-6) / 1e12,
+        "gemm_gate_up_swiglu": {
+            "median_us": cold_gemm["median_us"], "min_us": cold_gemm["min_us"],
+            "TFLOP/s": fl_gu / (cold_gemm["median_us"] * 1e-6) / 1e12,
+            "frac": fl_gu / (cold_gemm["median_us"] * 1e-6) / 1e12 / PEAK_FP16_TFLOPS,
+            "warm_back_to_back_us": warm_gemm_us},
+    }
+    _progress("cold figures done")
+    overhead = rac_overhead(torch, Q, x, ids, tw, w13q, w2q, E, I, H, KR, rows, step)
+
+    d5 = synth.make(5, with_weights=False)
+    x5 = torch.from_numpy(d5["x"].view(np.int16)).to(dev)
+    quant = {"gate_up_input_16384x4096": quantizer_rate(np, torch, Q, x5)}
+    cfg2 = cfg5 = None
+    if not args.layer_only:
+        cfg2 = config2(np, torch, Q, synth, dev, flush)
+        _progress("config 2 done")
+        cfg5, h5 = config5(np, torch, Q, d5, x5, dev)
+        _progress("config 5 done")
+        quant["down_input_131072x1536"] = quantizer_rate(np, torch, Q, h5)
+        del h5
+    del x5
+    decode = comparator = per_expert = None
+    if not args.layer_only:
+        decode = decode_layer(np, torch, Q, synth, dev, w13q, w2q)
+        comparator = mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx,
+                                   per_op["gemm_gate_up_swiglu"], fl_gu)
+        per_expert = per_expert_down(torch, Q, x, ids, E, I, H, KR, rows, w13q, w2q)
+        _progress("decode, comparator and per-expert selection done")
 
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
@@ -345,12 +577,16 @@ def main():
                    "tokens": T, "experts": E, "hidden": H, "intermediate": I, "top_k": TOPK,
                    "rac_k": KR, "packed_rows": rows, "gemm_operands": "nvfp4 -> exact fp16",
                    "accumulate": "fp32", "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": "v2::k_gemm_w4a4_v2<1> (gate/up GEMM, SwiGLU epilogue)",
+        "roofline": {"bound": "mfma", "kernel": "v3::k_gemm_w4a4_v3<1> (gate/up GEMM, SwiGLU epilogue)",
                      "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,
         "ops": ops,
+        "cold": cold,
+        "rac_overhead": overhead,
         "quantizer": quant,
+        "config2": cfg2,
+        "config5": cfg5,
         "comparator": comparator,
         "decode": decode,
         "per_expert_selection": per_expert,
@@ -401,20 +637,88 @@ def per_expert_down(torch, Q, x, ids, E, I, H, KR, rows, w13q, w2q, reps=20):
     return ms
 
 
-def quantizer_rate(np, torch, Q, synth, dev, reps=20):
-    """quads_nvfp4_quantize on the large-prefill gate/up input (16384 x 4096
-    bf16, Student-t body with outlier channels): algorithmic bytes (2 read +
-    0.5625 written per element) per call, with the dynamic tensor scale (a max
-    pass, then the quantize pass) and with a given tensor scale (one pass).
-    Calls go straight to the C ABI with buffers allocated once, so the rate is
-    the device's; a device-to-device copy of the same input is timed alongside
-    as context (it moves 4 bytes per element)."""
+def _progress(msg):
+    print(f"bench: {msg}", file=sys.stderr, flush=True)
+
+
+def _back_to_back_us(torch, fn, reps):
+    """Mean time per call of `reps` calls issued back to back (one event pair)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / reps
+
+
+def _cold_us(torch, fn, flush, reps):
+    """Each call right after `flush` (512 MiB) is written, an event pair around
+    the call: median and min over `reps`, in microseconds."""
+    fn()
+    torch.cuda.synchronize()
+    ts = []
+    for i in range(reps):
+        flush.fill_(float(i))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3)
+    ts.sort()
+    return {"median_us": ts[len(ts) // 2], "min_us": ts[0]}
+
+
+def rac_overhead(torch, Q, x, ids, tw, w13q, w2q, E, I, H, KR, rows, step, reps=20):
+    """The layer with plain NVFP4 W4A4 at both GEMM inputs (k = 0: the
+    quantizer, no residual pass and no compensation) beside the RAC layer
+    (k = 64), both timed as `reps` back-to-back steps with no events inside."""
+    def plain():
+        a = Q.quads_nvfp4_quantize(x)
+        off, rt, pos = Q.quads_moe_pack(ids, E)
+        h = Q.quads_moe_w4a4_gemm(a, w13q, 2 * I, rows=rows, offsets=off, row_token=rt,
+                                  epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+        b = Q.quads_nvfp4_quantize(h)
+        y2 = Q.quads_moe_w4a4_gemm(b, w2q, H, rows=rows, offsets=off, out_dtype=Q.OUT_BF16)
+        return Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / reps
+
+    ms_plain = timed(plain)
+    ms_rac = timed(lambda: step(None))
+    return {"layer_k0_ms": ms_plain, "layer_k64_ms": ms_rac, "ratio": ms_rac / ms_plain,
+            "note": "k = 0 is plain NVFP4 W4A4 (quads_nvfp4_quantize, GEMMs without "
+                    "compensation); k = 64 is the benchmark step; each timed as back-to-back "
+                    "layers"}
+
+
+def quantizer_rate(np, torch, Q, x, reps=20):
+    """quads_nvfp4_quantize on bf16 x [M, K]: algorithmic bytes (2 read + 0.5625
+    written per element) per call, with the dynamic tensor scale (a max pass,
+    then the quantize pass) and with a given tensor scale (one pass).  Warm:
+    `reps` calls on the same input.  Cold: the calls cycle through copies of
+    the input spaced at least 512 MiB apart (each call's input was last read
+    before 512 MiB of other inputs), back to back.  Calls go straight to the C
+    ABI with buffers allocated once; a device-to-device copy of the input is
+    timed the same two ways as context (4 bytes per element)."""
     import ctypes
     lib = Q.lib()
-    d = synth.make(5, with_weights=False)
-    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    dev = x.device
     m, k = x.shape
     nbytes = 2.5625 * m * k
+    ncopy = -(-FLUSH_BYTES // (2 * m * k)) + 1
+    xs = [x] + [x.clone() for _ in range(ncopy - 1)]
     nib = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
     sc = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
     ts = torch.empty(4, dtype=torch.float32, device=dev)
@@ -426,34 +730,123 @@ def quantizer_rate(np, torch, Q, synth, dev, reps=20):
     def P(t):
         return ctypes.c_void_p(t.data_ptr())
 
-    def timed(fn):
-        fn()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(reps):
-            fn()
-        e1.record()
-        torch.cuda.synchronize()
-        return e0.elapsed_time(e1) * 1e3 / reps
-
-    def call(ts_in):
-        st = lib.quads_nvfp4_quantize(P(x), m, k, ts_in, P(nib), P(sc), P(ts), P(ws), nws, stream)
+    def call(xi, ts_in):
+        st = lib.quads_nvfp4_quantize(P(xi), m, k, ts_in, P(nib), P(sc), P(ts), P(ws), nws,
+                                      stream)
         if st != 0:
             raise RuntimeError(f"quads_nvfp4_quantize failed with status {st}")
 
-    call(None)
+    call(x, None)
     ts_given.copy_(ts)
-    out = {"shape": [m, k], "algorithmic_bytes": nbytes}
+    out = {"shape": [m, k], "algorithmic_bytes": nbytes, "cold_copies": ncopy}
+
+    def rate(us, b=nbytes):
+        gbs = b / (us * 1e-6) / 1e9
+        return {"us": us, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+
     for name, ts_in in (("dynamic_scale", None), ("given_scale", P(ts_given))):
-        us = timed(lambda: call(ts_in))
-        gbs = nbytes / (us * 1e-6) / 1e9
-        out[name] = {"us": us, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+        out[name] = rate(_back_to_back_us(torch, lambda: call(x, ts_in), reps))
+        it = iter(range(10 ** 9))
+        out[name + "_cold"] = rate(_back_to_back_us(
+            torch, lambda: call(xs[next(it) % ncopy], ts_in), ncopy * max(2, reps // ncopy)))
     y = torch.empty_like(x)
-    us = timed(lambda: y.copy_(x))
-    out["device_copy"] = {"us": us, "GB/s": 4.0 * m * k / (us * 1e-6) / 1e9,
-                          "hbm_frac": 4.0 * m * k / (us * 1e-6) / 1e9 / PEAK_HBM_GBS}
+    out["device_copy"] = rate(_back_to_back_us(torch, lambda: y.copy_(x), reps), 4.0 * m * k)
+    it = iter(range(10 ** 9))
+    out["device_copy_cold"] = rate(_back_to_back_us(
+        torch, lambda: y.copy_(xs[next(it) % ncopy]), ncopy * max(2, reps // ncopy)), 4.0 * m * k)
+    del xs
     return out
+
+
+def config2(np, torch, Q, synth, dev, flush, reps=20):
+    """The dense rollout-shaped linear: x [4096, 4096] bf16 (Student-t(3) body,
+    41 outlier channels x20), W [4096, 4096] N(0, 0.02) through the weight
+    QDQ, RAC k = 128, one W4A4 GEMM with compensation, bf16 output."""
+    d = synth.make(2)
+    x = torch.from_numpy(d["x"].view(np.int16)).to(dev)
+    w = torch.from_numpy(d["w"].view(np.int16)).to(dev)
+    m, kd = x.shape
+    n = w.shape[1]
+    kr = d["rac_k"]
+    wq = Q.quads_nvfp4_weight_qdq(w)[:3]
+    keep = {}
+
+    def rac():
+        keep["a"] = Q.quads_rac_quantize(x, kr)
+
+    rac_us = _back_to_back_us(torch, rac, reps)
+    a = keep["a"]
+
+    def gemm():
+        return Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), wq, n,
+                                     r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"],
+                                     out_dtype=Q.OUT_BF16)
+    us = _back_to_back_us(torch, gemm, reps)
+    cold = _cold_us(torch, gemm, flush, reps)
+    fl = 2.0 * m * n * (kd + kr)
+    qb = 2.5625 * m * kd + 0.5625 * m * kr
+    return {"workload": "dense_linear_m4096_k4096_n4096_rac128",
+            "rac_us": rac_us, "rac_GB/s": qb / (rac_us * 1e-6) / 1e9,
+            "gemm_us": us, "gemm_TFLOP/s": fl / (us * 1e-6) / 1e12,
+            "gemm_frac": fl / (us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS,
+            "gemm_cold_median_us": cold["median_us"],
+            "gemm_cold_TFLOP/s": fl / (cold["median_us"] * 1e-6) / 1e12}
+
+
+def config5(np, torch, Q, d5, x, dev, reps=5):
+    """The large-prefill layer's gate/up site: 16384 tokens (Student-t(2.5)
+    body, 82 outlier channels x32), 64 experts, uniform top-8 routing (131072
+    packed rows), hidden 4096, intermediate 1536.  Weights: N(0, 0.02) drawn
+    on the device from a seeded generator, through the weight QDQ.  For
+    k = 0 (plain NVFP4), 64, 256 and 2048 (half the channels): the input
+    quantization (quads_nvfp4_quantize for k = 0, else quads_rac_quantize)
+    and the gate/up GEMM with the SwiGLU bf16 epilogue, each timed back to
+    back.  Returns the figures and the k = 64 SwiGLU output (the down site's
+    input, [131072, 1536] bf16)."""
+    E, H, I = 64, 4096, 1536
+    ids = torch.from_numpy(d5["topk_ids"]).to(dev)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(20260505)
+    w = (torch.randn((E, 2 * I, H), generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+    w13q = Q.quads_nvfp4_weight_qdq(w)[:3]
+    del w
+    off, rt, _ = Q.quads_moe_pack(ids, E)
+    rows = int(rt.shape[0])
+    out = {"workload": "moe_gate_up_e64_h4096_i1536_top8_t16384_uniform", "packed_rows": rows,
+           "k": {}}
+    h64 = None
+    for k in (0, 64, 256, 2048):
+        keep = {}
+
+        def quant():
+            keep["a"] = Q.quads_rac_quantize(x, k) if k else Q.quads_nvfp4_quantize(x)
+        q_us = _back_to_back_us(torch, quant, reps)
+        a = keep["a"]
+        if k:
+            av, rv, sel = (a["nib"], a["scale"], a["ts"]), (a["r_nib"], a["r_scale"], a["r_ts"]), \
+                a["sel"]
+        else:
+            av, rv, sel = a, None, None
+
+        def gemm():
+            keep["h"] = Q.quads_moe_w4a4_gemm(av, w13q, 2 * I, rows=rows, r=rv, sel=sel,
+                                              offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
+                                              out_dtype=Q.OUT_BF16)
+        us = _back_to_back_us(torch, gemm, reps)
+        fl = 2.0 * rows * 2 * I * (H + k)
+        qb = 2.5625 * x.shape[0] * H + 0.5625 * x.shape[0] * k
+        out["k"][str(k)] = {"quantize_us": q_us, "quantize_GB/s": qb / (q_us * 1e-6) / 1e9,
+                            "gemm_us": us, "gemm_TFLOP/s": fl / (us * 1e-6) / 1e12,
+                            "gemm_frac": fl / (us * 1e-6) / 1e12 / PEAK_FP16_TFLOPS}
+        if k == 64:
+            h64 = keep["h"]
+        del keep
+    base = out["k"]["0"]
+    for k, v in out["k"].items():
+        v["time_vs_k0"] = (v["quantize_us"] + v["gemm_us"]) / (base["quantize_us"] +
+                                                               base["gemm_us"])
+    del w13q
+    return out, h64
 
 
 def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
