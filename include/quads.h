@@ -13,14 +13,16 @@
  *    pointer must be 16-byte aligned.
  *  - Calls are asynchronous on `stream` (a hipStream_t; NULL = the null
  *    stream).  No call synchronizes with the host, allocates memory or keeps
- *    a pointer after it returns.  Scalars produced on the device (tensor
+ *    a pointer after it returns (quads_rac_quantize_noalloc keeps its own
+ *    static scratch).  Scalars produced on the device (tensor
  *    scales, selected channels, expert offsets) stay on the device.
  *  - Scratch memory is caller-owned: `ws` must hold at least the bytes the
  *    matching *_ws() query returns for the same sizes (NULL is allowed when
  *    that is 0).  Calls that share a workspace must be ordered on one stream.
  *  - Argument checks run on the host before any launch.  A failed check
  *    returns QUADS_EINVAL (null or misaligned pointer, bad enum),
- *    QUADS_ESHAPE (a size rule below) or QUADS_EWORKSPACE; nothing is
+ *    QUADS_ESHAPE (a size rule below), QUADS_EWORKSPACE or QUADS_ESCRATCH
+ *    (input too large for a no-allocation call's static scratch); nothing is
  *    launched then.  A failed launch returns QUADS_EHIP; quads_status_string
  *    then describes the HIP error of the calling thread.
  *  - Inputs must be finite.  Size-0 tensors (M, T or rows = 0) are a no-op
@@ -54,7 +56,8 @@ typedef enum {
     QUADS_EINVAL = -1,
     QUADS_ESHAPE = -2,
     QUADS_EWORKSPACE = -3,
-    QUADS_EHIP = -4
+    QUADS_EHIP = -4,
+    QUADS_ESCRATCH = -5
 } quads_status;
 
 typedef enum { QUADS_OUT_F32 = 0, QUADS_OUT_BF16 = 1 } quads_out_dtype;
@@ -123,6 +126,26 @@ int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
                        uint8_t* nib, uint8_t* scale, float* ts,
                        int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
                        double* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * quads_rac_quantize without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, outputs and results are
+ * those of quads_rac_quantize; the workspace is a static device array of
+ * QUADS_RAC_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs
+ * on until the process ends.  Sizes whose quads_rac_quantize_ws exceeds it
+ * return QUADS_ESCRATCH before any launch (the other argument checks come
+ * first).  The call runs on the calling thread's current device; `stream`
+ * must belong to it.  All calls on one GPU share that GPU's array: calls
+ * that may overlap in time on one GPU (different streams, or threads without
+ * ordering) race and give undefined results.  The first call on a device
+ * looks up the array's address there (no allocation).
+ */
+#define QUADS_RAC_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int quads_rac_quantize_noalloc(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                               uint8_t* nib, uint8_t* scale, float* ts,
+                               int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                               double* score_out, void* stream);
 
 /*
  * RAC with one channel selection per expert (a variant of section 3.3; the

@@ -45,6 +45,8 @@ _SIGNATURES = {
     "quads_rac_quantize_ws": (_SZ, [_I64, _I64, _I32]),
     "quads_rac_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _SZ, _P]),
+    "quads_rac_quantize_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P,
+                                                  _P, _P, _P]),
     "quads_rac_quantize_experts_ws": (_SZ, [_I64, _I64, _I32, _I32]),
     "quads_rac_quantize_experts": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _I32, _P, _P, _P, _P,
                                                   _P, _P, _P, _P, _P, _SZ, _P]),
@@ -172,6 +174,36 @@ def quads_rac_quantize(x, k, want_score=False):
         _ptr(out["sel"]) if k else None, _ptr(out["r_nib"]) if k and m else None,
         _ptr(out["r_scale"]) if k and m else None, _ptr(out["r_ts"]), _ptr(out.get("score")),
         _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+RAC_NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def quads_rac_quantize_noalloc(x, k, want_score=False, out=None):
+    """quads_rac_quantize through the entry point that allocates no device
+    memory (the library's static per-GPU scratch).  `out` may hold the output
+    tensors (a dict as returned); else they are allocated here, by torch."""
+    x = _bits16(x)
+    m, kd = x.shape
+    dev = x.device
+    if out is None:
+        out = dict(
+            nib=torch.empty((m, kd // 2), dtype=torch.uint8, device=dev),
+            scale=torch.empty((m, kd // 16), dtype=torch.uint8, device=dev),
+            ts=torch.empty(4, dtype=torch.float32, device=dev)[:1],
+            sel=torch.empty(max(k, 4), dtype=torch.int32, device=dev)[:k],
+            r_nib=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+            r_scale=torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
+            r_ts=torch.empty(4, dtype=torch.float32, device=dev)[:1],
+        )
+        if want_score:
+            out["score"] = torch.empty(kd, dtype=torch.float64, device=dev)
+    _check("quads_rac_quantize_noalloc", lib().quads_rac_quantize_noalloc(
+        _ptr(x), m, kd, k, _ptr(out["nib"]), _ptr(out["scale"]), _ptr(out["ts"]),
+        _ptr(out["sel"]) if k else None, _ptr(out["r_nib"]) if k and m else None,
+        _ptr(out["r_scale"]) if k and m else None, _ptr(out["r_ts"]), _ptr(out.get("score")),
+        _stream(dev)))
     return out
 
 

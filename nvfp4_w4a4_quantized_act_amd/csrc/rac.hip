@@ -20,6 +20,8 @@
 //  pass 2  one thread per element of r[:, S] (recomputed from x, the codes
 //          and the block scales of pass 1), NVFP4-quantized in 16-blocks along
 //          the compacted index (the second term of Eq. (21)).
+#include <mutex>
+
 #include "common.h"
 
 namespace quads {
@@ -841,18 +843,24 @@ extern "C" size_t quads_rac_quantize_ws(int64_t M, int64_t K, int32_t k) {
     return rac_ws_layout(nullptr, M, K).bytes;
 }
 
-extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
-                                  uint8_t* nib, uint8_t* scale, float* ts, int32_t* sel,
-                                  uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
-                                  double* score_out, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks of quads_rac_quantize other than the workspace.
+static int rac_check_args(const uint16_t* x, int64_t M, int64_t K, int32_t k, uint8_t* nib,
+                          uint8_t* scale, float* ts, int32_t* sel, uint8_t* r_nib,
+                          uint8_t* r_scale, float* r_ts, double* score_out) {
     if (M < 0 || K <= 0 || K % kBlock || K > kRacMaxK) return QUADS_ESHAPE;
     if (k < 0 || k % kBlock || k > K) return QUADS_ESHAPE;
     if (!ok_ptr(ts) || !ok_ptr(r_ts) || !ok_opt_ptr(score_out)) return QUADS_EINVAL;
     if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale))) return QUADS_EINVAL;
     if (k > 0 && !ok_ptr(sel)) return QUADS_EINVAL;
     if (k > 0 && M > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale))) return QUADS_EINVAL;
-    if (ws_bytes < quads_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
-    hipStream_t s = (hipStream_t)stream;
+    return QUADS_OK;
+}
+
+// The launches of quads_rac_quantize once the arguments are checked; `ws`
+// holds at least quads_rac_quantize_ws(M, K, k) bytes of device memory.
+static int rac_run(const uint16_t* x, int64_t M, int64_t K, int32_t k, uint8_t* nib,
+                   uint8_t* scale, float* ts, int32_t* sel, uint8_t* r_nib, uint8_t* r_scale,
+                   float* r_ts, double* score_out, void* ws, hipStream_t s) {
     if (M == 0) {
         launch_fill_f32(ts, 1, 0.0f, s);
         launch_fill_f32(r_ts, 1, 0.0f, s);
@@ -916,6 +924,60 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
         QUADS_CHECK_LAUNCH();
     }
     return QUADS_OK;
+}
+
+extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                  uint8_t* nib, uint8_t* scale, float* ts, int32_t* sel,
+                                  uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                                  double* score_out, void* ws, size_t ws_bytes, void* stream) {
+    const int st = rac_check_args(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts,
+                                  score_out);
+    if (st != QUADS_OK) return st;
+    if (ws_bytes < quads_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    return rac_run(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out, ws,
+                   (hipStream_t)stream);
+}
+
+// Workspace of quads_rac_quantize_noalloc.  In host code `scratch` names a
+// host-side shadow, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that address is passed on.
+static __device__ __align__(256) char scratch[QUADS_RAC_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's copy of `scratch`.
+int scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return set_hip_error(e);
+    if (dev < 0 || dev >= kMaxDevices) return QUADS_EINVAL;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return set_hip_error(e);
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return QUADS_OK;
+}
+}  // namespace
+
+extern "C" int quads_rac_quantize_noalloc(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                          uint8_t* nib, uint8_t* scale, float* ts,
+                                          int32_t* sel, uint8_t* r_nib, uint8_t* r_scale,
+                                          float* r_ts, double* score_out, void* stream) {
+    int st = rac_check_args(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out);
+    if (st != QUADS_OK) return st;
+    if (quads_rac_quantize_ws(M, K, k) > QUADS_RAC_NOALLOC_SCRATCH_BYTES) return QUADS_ESCRATCH;
+    void* ws = nullptr;
+    st = scratch_address(&ws);
+    if (st != QUADS_OK) return st;
+    return rac_run(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out, ws,
+                   (hipStream_t)stream);
 }
 
 // Per-expert selection: workspace = partial maxima, scores [E, K] (fp64),

@@ -21,6 +21,9 @@ extern "C" const char* quads_status_string(int status) {
         case QUADS_ESHAPE: return "invalid shape (see the size rules in quads.h)";
         case QUADS_EWORKSPACE: return "workspace too small (query the matching *_ws function)";
         case QUADS_EHIP: return quads::g_last_hip[0] ? quads::g_last_hip : "HIP error";
+        case QUADS_ESCRATCH:
+            return "input too large for the static scratch of a no-allocation call "
+                   "(quads_rac_quantize_ws exceeds QUADS_RAC_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 20
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 21
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -71,6 +71,36 @@ def test_rac_validation():
     assert args(64, 256, 32, ws - 1) == -3
     assert f(FAKE, 64, 256, 32, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None, FAKE, ws,
              None) == -1                        # sel missing with k > 0
+
+
+def test_rac_noalloc_validation():
+    """The no-allocation RAC: the argument checks of quads_rac_quantize, then
+    QUADS_ESCRATCH for sizes whose workspace exceeds the static scratch; all
+    before any device call."""
+    lib = Q.lib()
+    f = lib.quads_rac_quantize_noalloc
+    cap = Q.RAC_NOALLOC_SCRATCH_BYTES
+    call = lambda m, k_dim, k: f(FAKE, m, k_dim, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 None, None)
+    assert call(64, 256, 8) == -2              # k % 16
+    assert call(64, 250, 16) == -2             # K % 16
+    assert f(FAKE, 64, 256, 32, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, None,
+             None) == -1                        # sel missing with k > 0
+    # the largest M (multiple of 64) that fits at K = 4096, and the next
+    k_dim = 4096
+    m = 64
+    while lib.quads_rac_quantize_ws(2 * m, k_dim, 64) <= cap:
+        m *= 2
+    while lib.quads_rac_quantize_ws(m + 64, k_dim, 64) <= cap:
+        m += 64
+    assert lib.quads_rac_quantize_ws(m, k_dim, 64) <= cap
+    assert call(m + 64, k_dim, 64) == -5
+    assert call(4 * m, k_dim, 64) == -5
+    assert "scratch" in lib.quads_status_string(-5).decode()
+    # the scratch covers every RAC site of the five workloads
+    for mm, kk, k in ((32, 256, 16), (4096, 4096, 128), (4096, 2048, 64), (32768, 768, 64),
+                      (16384, 4096, 256), (131072, 1536, 64)):
+        assert lib.quads_rac_quantize_ws(mm, kk, k) <= cap, (mm, kk)
 
 
 def test_weight_qdq_validation():
