@@ -188,7 +188,7 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
 def _short_name(name):
     """Kernel name without the return type, the library namespace and the
     argument list: `v3::k_gemm_w4a4_v3<1>`."""
-    name = name.strip()
+    name = name.strip().replace("(anonymous namespace)::", "")
     if name.startswith("void "):
         name = name[5:]
     depth = 0
@@ -239,10 +239,11 @@ def trace_summary(trace_dir):
         "",
         "Durations are the trace's start-to-end times in microseconds, grouped by kernel and "
         "launch shape (work-groups in x and y, threads per work-group), so that launches of one "
-        "kernel on different workloads show apart.  The prefill layer's gate/up GEMM is "
-        "`v3::k_gemm_w4a4_v3<1>` at (1536, 1) x 512 (128 experts, 256-row by 64-feature "
-        "tiles); config 5's gate/up GEMMs are the same kernel at larger grids, config 2's the "
-        "`<0>` instance.",
+        "kernel on different workloads show apart.  The gate/up GEMM is "
+        "`v3::k_gemm_w4a4_v3<1>`: the prefill layer's launches are its smallest grid, config "
+        "5's (k = 0, 64, 256) the largest; config 5 at k = 2048 runs `k_gemm_w4a4<1>`.  The "
+        "down GEMM (768 + 64 channels, one accumulator chain) is `v2::k_gemm_w4a4_v2<0>`; "
+        "config 2's GEMM is `v3::k_gemm_w4a4_v3<0>`.",
         "",
         "| kernel | work-groups (x, y) x threads | calls | total (us) | average (us) | min (us) | "
         "max (us) | % |",
