@@ -71,6 +71,7 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kFlush = 8;            // chunks per accumulation segment (1024 channels)
 constexpr int kCapLd = kCapMaxV3 + 8;  // halfs per captured row (16-byte pad)
+constexpr int kMaxChunksV3 = 64;       // K <= 8192
 
 // Activation codes of one chunk for the lane's two row fragments: channels
 // 32 q .. 32 q + 31 (16 bytes) and the scale bytes of blocks 2 q, 2 q + 1.
@@ -192,7 +193,8 @@ __device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
 
 template <int kEpi, int MACT, bool LATE>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
-                                         const int* s_sel, const Ctx& x, int wr, int wh,
+                                         const int* s_sel, const int* s_cs, const Ctx& x,
+                                         int wr, int wh,
                                          int kc, int wave, int lane, const int64_t src[2],
                                          int m0, int mend, int f0, int e) {
     // The MFMA accumulators X restart from zero every kFlush chunks (1024
@@ -201,22 +203,28 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     zero_set<MACT>(X);
     zero_set<MACT>(T);
     const int nk = x.nk;
+    // the epilogue's scales, requested now rather than after the loop
+    const float s_tr = kc > 0 ? g.r_ts[0] : 0.0f;
+    const float s_tw = g.w_ts[e];
+    const float ca0 = tensor_scale_a(g) * s_tw;
+    // residual codes and scale bytes of the compensation's first two steps,
+    // requested in the last chunk (their latency hides behind its MFMAs)
+    uint32_t rcode[2][2] = {{0u, 0u}, {0u, 0u}}, rsb[2][2] = {{0u, 0u}, {0u, 0u}};
+    const int rq = lane >> 4;
     const char* wb_lane = wbuf + lane * 16;
-    // capture bookkeeping (uniform): selected channels ci .. ce - 1 lie in
-    // the chunks seen so far
-    int ci = 0;
+    // capture: the selected channels s_cs[c] .. s_cs[c + 1] - 1 lie in chunk c
     const int cap_row = threadIdx.x & (BN - 1), cap_par = threadIdx.x >> 7;   // capture roles
     auto capture = [&](const char* wb, int c) {
         if (kc == 0) return;
-        int ce = ci;
-        while (ce < kc && s_sel[ce] < BK * (c + 1)) ++ce;
+        int ci = s_cs[c], ce = s_cs[c + 1];
+        ci = ci < 0 ? 0 : (ci > kc ? kc : ci);                 // bounds only: sel ascending
+        ce = ce < ci ? ci : (ce > kc ? kc : ce);
         for (int i = ci + cap_par; i < ce; i += kThreads / BN) {
             int ch = s_sel[i] - BK * c;
-            ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);     // bounds only: sel ascending
+            ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);
             cap[cap_row * kCapLd + i] = *reinterpret_cast<const _Float16*>(
                 wb + wblock_off(cap_row, ch & ~7) + 2 * (ch & 7));
         }
-        ci = ce;
     };
 
     ARaw a0, a1;
@@ -237,6 +245,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
         if (c >= nk) return;
         load_a<MACT>(x, c + 1, an);
         load_w(x, c + 2, wn2);
+        if (c == nk - 1 && kc > 0) {
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+                const int ch = 32 * s2 + 8 * rq;
+                if (ch < kc) {
+#pragma unroll
+                    for (int f = 0; f < MACT; ++f) {
+                        rcode[f][s2] = *reinterpret_cast<const uint32_t*>(
+                            g.r_nib + src[f] * (g.k / 2) + ch / 2);
+                        rsb[f][s2] = g.r_scale[src[f] * (g.k / kBlock) + ch / kBlock];
+                    }
+                }
+            }
+        }
         // keep the requests here, a whole chunk ahead of their use (left to
         // itself the scheduler sinks them towards their use and the chunk
         // then waits on their latency)
@@ -248,11 +270,15 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
         char* wnext = wbuf + ((c + 1) & 1) * (BN * BK * 2);
         if (LATE && c + 1 < nk) store_w(wn, wnext, wr, wh);
         f16x8 wf[8];
+        // the MFMA section at raised wave priority, so that the SIMD's other
+        // wave (in its conversions) does not take issue slots from it
+        __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             if (MACT > 0) read_wf(wb, st, wf);
             mma_step<MACT>(wf, ac, st, X);
         }
+        __builtin_amdgcn_s_setprio(0);
         if (!LATE && c + 1 < nk) store_w(wn, wnext, wr, wh);
         capture(wbuf + (c & 1) * (BN * BK * 2), c);
         if ((c + 1) % kFlush == 0 || c + 1 == nk) {
@@ -267,7 +293,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     }
 
     // compensation: R x W[:, S] into X (zero), from the captured columns
-    const float s_tr = g.k > 0 ? g.r_ts[0] : 0.0f;
     const bool comp = kc > 0 && s_tr > 0.0f;
     if (comp && MACT > 0) {
         const int r = lane & 15, q = lane >> 4;
@@ -281,7 +306,10 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
 #pragma unroll
             for (int f = 0; f < MACT; ++f) {
                 uint32_t code = 0u, sb = 0u;
-                if (ch < kc) {
+                if (s < 2) {
+                    code = s == 0 ? rcode[f][0] : rcode[f][1];
+                    sb = s == 0 ? rsb[f][0] : rsb[f][1];
+                } else if (ch < kc) {
                     code = *reinterpret_cast<const uint32_t*>(g.r_nib + src[f] * (g.k / 2) + ch / 2);
                     sb = g.r_scale[src[f] * (g.k / kBlock) + ch / kBlock];
                 }
@@ -295,8 +323,6 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
 
     // epilogue: y = T s_tA s_tW + X s_tR s_tW
     if (MACT == 0) return;
-    const float s_tw = g.w_ts[e];
-    const float ca0 = tensor_scale_a(g) * s_tw;
     const float cr = comp ? s_tr * s_tw : 0.0f;
     const int r = lane & 15, q = lane >> 4;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
@@ -385,6 +411,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     __shared__ __align__(16) char wbuf[2 * BN * BK * 2];
     __shared__ __align__(16) _Float16 cap[BN * kCapLd];
     __shared__ int s_sel[kCapMaxV3];
+    __shared__ int s_cs[kMaxChunksV3 + 1];
     // XCD-aware numbering: hardware id h runs on XCD h % 8; tiles are dealt in
     // groups of `grp` consecutive tiles (M-tile major: one M tile's N tiles
     // share its activation rows) per XCD
@@ -440,6 +467,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     const int kc = g.k;
     if (kc > 0) {
         for (int i = tid; i < kc; i += kThreads) s_sel[i] = g.sel[i];
+        // s_cs[c] = the first selected index whose channel is in chunk c or
+        // later (sel ascending: thread i writes the chunks from just past
+        // sel[i - 1]'s chunk to sel[i]'s)
+        for (int i = tid; i <= kc; i += kThreads) {
+            int lo = i == 0 ? 0 : g.sel[i - 1] / BK + 1;
+            int hi = i == kc ? x.nk : g.sel[i] / BK;
+            lo = lo < 0 ? 0 : lo;
+            hi = hi > x.nk ? x.nk : hi;
+            for (int c = lo; c <= hi; ++c) s_cs[c] = i;
+        }
         const int kpad = (kc + 31) & ~31;
         for (int i = tid; i < BN * (kpad - kc); i += kThreads)
             cap[(i / (kpad - kc)) * kCapLd + kc + i % (kpad - kc)] = (_Float16)0.0f;
@@ -451,7 +488,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     switch (mact + (wave >= 4 ? 4 : 0)) {
 #define QUADS_V3_TILE(M, L)                                                                     \
     case M + (L ? 4 : 0):                                                                       \
-        run_tile<kEpi, M, L>(g, wbuf, cap, s_sel, x, wr, wh, kc, wave, lane, src, m0, mend, f0, e); \
+        run_tile<kEpi, M, L>(g, wbuf, cap, s_sel, s_cs, x, wr, wh, kc, wave, lane, src, m0,    \
+                             mend, f0, e);                                                      \
         break;
         QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)
         QUADS_V3_TILE(1, true) QUADS_V3_TILE(0, true)
@@ -463,7 +501,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
 }  // namespace v3
 
 bool gemm_v3_fits(const GemmArgs& g) {
-    return g.K % v3::BK == 0 && g.k <= kCapMaxV3 && (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+    return g.K % v3::BK == 0 && g.K <= v3::BK * v3::kMaxChunksV3 && g.k <= kCapMaxV3 &&
+           (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
 }
 
 int launch_gemm_v3(const GemmArgs& g, hipStream_t st) {
