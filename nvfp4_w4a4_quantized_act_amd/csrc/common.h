@@ -57,6 +57,61 @@ __device__ __forceinline__ uint32_t e4m3_rne_code(double q) {
     return c > (uint32_t)kE4m3MaxCode ? (uint32_t)kE4m3MaxCode : c;
 }
 
+// Block-scale codes without the fp64 division.  thr2[c] (c = 0 .. 126) packs
+// thr(c) | thr(c + 1) << 16, where thr(c) is the smallest bf16 magnitude
+// (bits) whose code RNE_E4M3(a / (6 s_t)) is c or more (thr(0) = 0; thr(127)
+// = 0xFFFF, above every finite magnitude).  The E4M3 midpoint between codes
+// c - 1 and c, times 6 s_t, is exact in fp64 (at most 7 + 24 significant
+// bits); at a tie the even code wins.  Built by threads 0 .. 126 of a block.
+__device__ __forceinline__ uint32_t scale_threshold(uint32_t c, double six_st) {
+    if (c == 0) return 0u;
+    if (c > (uint32_t)kE4m3MaxCode) return 0xFFFFu;
+    const double t = 0.5 * ((double)e4m3_value(c - 1) + (double)e4m3_value(c)) * six_st;
+    const float f = (float)t;
+    uint32_t fb = __float_as_uint(f);
+    if ((double)f < t) fb += 1u;                          // smallest fp32 >= t
+    uint32_t b = (fb + 0xFFFFu) >> 16;                    // smallest bf16 >= that
+    if ((c & 1u) && (double)__uint_as_float(b << 16) == t) b += 1u;   // tie: even code
+    return b > 0x7F80u ? 0xFFFFu : b;
+}
+
+__device__ __forceinline__ void build_scale_thresholds(float s_t, uint32_t* thr2) {
+    const uint32_t c = threadIdx.x;
+    if (c <= (uint32_t)kE4m3MaxCode) {
+        const double six_st = 6.0 * (double)s_t;
+        thr2[c] = scale_threshold(c, six_st) | (scale_threshold(c + 1u, six_st) << 16);
+    }
+}
+
+// Block-scale code of a block with bf16 maximum magnitude `am` (bits), for a
+// tensor scale s_t >= 2^-100 (inv6st = RN32(1 / (6 s_t))): the code of the
+// fp32 quotient estimate (relative error under 2^-22, against a 1/16 relative
+// spacing of the E4M3 midpoints, so at most one code off), then one compare
+// with each threshold around it.
+__device__ __forceinline__ uint32_t scale_code_thr(uint32_t am, float inv6st,
+                                                   const uint32_t* thr2) {
+    const float q = __uint_as_float(am << 16) * inv6st;
+    uint32_t c;
+    if (!(q < 448.0f)) {
+        c = kE4m3MaxCode;
+    } else if (q < 0x1p-6f) {
+        c = (uint32_t)__builtin_rintf(q * 512.0f);              // subnormal codes 0 .. 8
+    } else {
+        const uint32_t b = __float_as_uint(q);
+        c = ((b + 0x7FFFFu + ((b >> 20) & 1u)) >> 20) - (120u << 3);   // rebias 127 -> 7
+        c = c > (uint32_t)kE4m3MaxCode ? (uint32_t)kE4m3MaxCode : c;
+    }
+    const uint32_t pr = thr2[c];
+    c += am >= (pr >> 16) ? 1u : 0u;
+    c -= am < (pr & 0xFFFFu) ? 1u : 0u;
+    return c;
+}
+
+// Value of the neighbouring lane (lane ^ 1), by a DPP quad permutation.
+__device__ __forceinline__ uint32_t lane_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+
 // Tensor scale s_t = RN32(A / 2688) for A = max|x| >= 0.  fp64 division then
 // one fp32 rounding equals the exact RN32 for every bf16 and fp32 A here.
 __device__ __forceinline__ float tensor_scale_from_amax(float amax) {

@@ -66,22 +66,25 @@ __global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restri
                           true);
 }
 
-constexpr int kQuantUnroll = 4;                 // half-block loads in flight per lane
+constexpr int kQuantUnroll = 4;                 // half-blocks per batch per lane (two batches in flight)
 
 // Half-block h (8 elements) of a segment, the other half on the neighbouring
 // lane (h ^ 1): block maximum by one shuffle, then codes (4 bytes), the
 // block's scale byte (even lane) and the optional bf16 QDQ (16 bytes).
 template <bool kDq>
 __device__ __forceinline__ void quantize_half(const uint4 q, int64_t h, float s_t, double six_st,
+                                              float inv6st, bool fast_sc, const uint32_t* thr2,
                                               const uint4* s_tab, uint8_t* ns, uint8_t* ss,
                                               uint16_t* ds) {
     const uint32_t w[4] = {q.x, q.y, q.z, q.w};
     uint32_t am = pk_max_u16(pk_max_u16(w[0] & 0x7FFF7FFFu, w[1] & 0x7FFF7FFFu),
                              pk_max_u16(w[2] & 0x7FFF7FFFu, w[3] & 0x7FFF7FFFu));
     am = (am & 0xFFFFu) > (am >> 16) ? (am & 0xFFFFu) : (am >> 16);
-    const uint32_t o = __shfl_xor(am, 1, 64);
+    const uint32_t o = lane_xor1(am);
     am = o > am ? o : am;
-    const uint32_t sb = s_t > 0.0f ? e4m3_rne_code((double)bf16_to_f32(am) / six_st) : 0u;
+    const uint32_t sb = !(s_t > 0.0f) ? 0u
+                        : fast_sc     ? scale_code_thr(am, inv6st, thr2)
+                                      : e4m3_rne_code((double)bf16_to_f32(am) / six_st);
     const uint4 t1 = s_tab[2 * sb + 1];                       // word 7: fast-path multiplier
     uint32_t codes = 0u;
     if (t1.w != kSlowPath) {
@@ -118,23 +121,50 @@ __device__ __forceinline__ void quantize_half(const uint4 q, int64_t h, float s_
     }
 }
 
-// kFold: one segment with a dynamic tensor scale; every work-group folds the
-// partial maxima (`table` is then the partial-max array, `ts` the output
-// scale, written by work-group 0) and builds the code table itself, so no
-// finalize launch runs in between.  Otherwise the table and the scale come
-// from k_scale_finalize.
+// kFold: one segment; every work-group takes the tensor scale (the caller's
+// `ts_in`, or the fold of the partial maxima in `table`) and builds the code
+// table itself, so no finalize launch runs before it; work-group 0 writes the
+// scale to `ts`.  Otherwise the table and the scale come from
+// k_scale_finalize (the per-expert weight tensors).
+//
+// Lane i of a wave reads 16 contiguous bytes (a wave: 1 KB); the two lanes of
+// a block are neighbours.  A thread takes kQuantUnroll half-blocks per batch
+// (`stride` apart) and keeps two batches in registers: the first is
+// requested before the table set-up, and each next one before the current
+// one is encoded, so a work-group's loads never wait on its own set-up or
+// encoding.  A lane and its neighbour are both in range or both out (the
+// half-block count is even).
+template <bool kDq>
+__device__ __forceinline__ void quant_load_batch(uint4 (&q)[kQuantUnroll], const uint16_t* xs,
+                                                 int64_t h0, int64_t stride, int64_t nhalf) {
+#pragma unroll
+    for (int u = 0; u < kQuantUnroll; ++u) {
+        const int64_t h = h0 + u * stride;
+        q[u] = ld_stream16(xs + (h < nhalf ? h : 0) * 8);
+    }
+}
+
 template <bool kDq, bool kFold = false>
 __global__ __launch_bounds__(256) void k_quantize_bf16(
     const uint16_t* __restrict__ x, int64_t seg_elems, float* __restrict__ ts,
     const uint32_t* __restrict__ table, uint8_t* __restrict__ nib, uint8_t* __restrict__ scale,
-    uint16_t* __restrict__ dq, int groups = 0) {
+    uint16_t* __restrict__ dq, int groups = 0, const float* __restrict__ ts_in = nullptr) {
     __shared__ uint4 s_tab[2 * (kE4m3MaxCode + 1)];
+    __shared__ uint32_t s_thr2[kE4m3MaxCode + 1];
     const int seg = blockIdx.y;
+    const int64_t nhalf = seg_elems / 8;                      // even: whole blocks
+    const uint16_t* xs = x + (int64_t)seg * seg_elems;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    const int64_t step = kQuantUnroll * stride;
+    int64_t h0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    uint4 qa[kQuantUnroll], qb[kQuantUnroll];
+    quant_load_batch<kDq>(qa, xs, h0, stride, nhalf);
+
     float s_t;
     if (kFold) {
         __shared__ float s_st;
         __shared__ uint32_t s_red[4];
-        tensor_scale_prologue(table, groups, nullptr, 0, &s_st, s_red);   // groups <= 8 * 256
+        tensor_scale_prologue(table, groups, ts_in, 0, &s_st, s_red);     // groups <= 8 * 256
         __syncthreads();
         s_t = s_st;
         build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(s_tab), true);
@@ -144,31 +174,36 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
         for (int i = threadIdx.x; i < 2 * (kE4m3MaxCode + 1); i += blockDim.x) s_tab[i] = tg[i];
         s_t = ts[seg];
     }
+    // block-scale thresholds (exact codes from an fp32 quotient estimate) for
+    // s_t >= 2^-100; below that the fp64 division
+    const bool fast_sc = s_t >= 0x1p-100f;
+    const float inv6st = fast_sc ? (float)(1.0 / (6.0 * (double)s_t)) : 0.0f;
+    if (fast_sc) build_scale_thresholds(s_t, s_thr2);
     __syncthreads();
 
-    const int64_t nhalf = seg_elems / 8;                      // even: whole blocks
-    const uint16_t* xs = x + (int64_t)seg * seg_elems;
     uint8_t* ns = nib + (int64_t)seg * (seg_elems / 2);
     uint8_t* ss = scale + (int64_t)seg * (seg_elems / kBlock);
     uint16_t* ds = kDq ? dq + (int64_t)seg * seg_elems : nullptr;
     const double six_st = 6.0 * (double)s_t;                  // exact
-    // lane i of a wave reads 16 contiguous bytes (a wave: 1 KB); the two
-    // lanes of a block are neighbours; four reads in flight per lane.  A
-    // lane and its neighbour are both in range or both out (nhalf is even).
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (int64_t h0 = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; h0 < nhalf;
-         h0 += kQuantUnroll * stride) {
-        uint4 q[kQuantUnroll];
+    auto encode = [&](const uint4 (&q)[kQuantUnroll], int64_t hb) {
 #pragma unroll
         for (int u = 0; u < kQuantUnroll; ++u) {
-            const int64_t h = h0 + u * stride;
-            q[u] = ld_stream16(xs + (h < nhalf ? h : h0) * 8);
+            const int64_t h = hb + u * stride;
+            if (h < nhalf)
+                quantize_half<kDq>(q[u], h, s_t, six_st, inv6st, fast_sc, s_thr2, s_tab, ns, ss,
+                                   ds);
         }
-#pragma unroll
-        for (int u = 0; u < kQuantUnroll; ++u) {
-            const int64_t h = h0 + u * stride;
-            if (h < nhalf) quantize_half<kDq>(q[u], h, s_t, six_st, s_tab, ns, ss, ds);
-        }
+    };
+    while (h0 < nhalf) {
+        int64_t hn = h0 + step;
+        if (hn < nhalf) quant_load_batch<kDq>(qb, xs, hn, stride, nhalf);
+        encode(qa, h0);
+        h0 = hn;
+        if (h0 >= nhalf) break;
+        hn = h0 + step;
+        if (hn < nhalf) quant_load_batch<kDq>(qa, xs, hn, stride, nhalf);
+        encode(qb, h0);
+        h0 = hn;
     }
 }
 
@@ -249,6 +284,24 @@ void launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
                            (int)n, v);
 }
 
+// Work-groups of 256 threads of `kernel` the current device holds at once
+// (the occupancy query, once per kernel and device; 2048 if it fails).
+template <typename F>
+int resident_groups(F kernel) {
+    static int cached[16] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 16) return 2048;
+    if (cached[dev] == 0) {
+        int per_cu = 0, cus = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, 0) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            per_cu < 1 || cus < 1)
+            return 2048;
+        cached[dev] = per_cu * cus;
+    }
+    return cached[dev];
+}
+
 int quant_grid(int64_t nblk) {
     int64_t g = (2 * nblk + 256 * kQuantUnroll - 1) / (256 * kQuantUnroll);  // half-blocks
     if (g > 8192) g = 8192;
@@ -285,27 +338,25 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     }
     const int64_t n = M * K;
     uint32_t* partial = static_cast<uint32_t*>(ws);
-    uint32_t* table = partial + align_up(kAmaxGroups * 4, 256) / 4;
-    int groups = 1;
     if (!ts_in) {
         // dynamic scale: the partial maxima, then the quantize pass folds
         // them itself, with at most one work-group per resident slot (2048 =
         // 8 per CU) so that the per-work-group table build is paid once
-        groups = amax_groups(n);
+        const int groups = amax_groups(n);
         hipLaunchKernelGGL(k_amax_partial, dim3(groups, 1), dim3(256), 0, s, x, n, partial,
                            (uint32_t*)nullptr, 0);
         QUADS_CHECK_LAUNCH();
-        const int qg = quant_grid(n / kBlock);
-        hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < 2048 ? qg : 2048, 1),
+        const int qg = quant_grid(n / kBlock), qr = resident_groups(k_quantize_bf16<false, true>);
+        hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < qr ? qg : qr, 1),
                            dim3(256), 0, s, x, n, ts_out, partial, nib, scale, (uint16_t*)nullptr,
                            groups);
         QUADS_CHECK_LAUNCH();
         return QUADS_OK;
     }
-    launch_scale_finalize(partial, groups, ts_in, 1, ts_out, table, s);
-    QUADS_CHECK_LAUNCH();
-    hipLaunchKernelGGL(k_quantize_bf16<false>, dim3(quant_grid(n / kBlock), 1), dim3(256), 0, s, x, n,
-                       ts_out, table, nib, scale, (uint16_t*)nullptr);
+    // the caller's scale: one launch, every work-group building the table
+    const int qg = quant_grid(n / kBlock), qr = resident_groups(k_quantize_bf16<false, true>);
+    hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < qr ? qg : qr, 1), dim3(256), 0, s,
+                       x, n, ts_out, partial, nib, scale, (uint16_t*)nullptr, 0, ts_in);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

@@ -102,6 +102,29 @@ def test_quantize_static_scale(Q):
     _check(Q, d["x"], ts=np.float32(1.0))
 
 
+def _all_magnitudes():
+    """Every finite bf16 magnitude, each block of 16 holding one of them at
+    its maximum (both signs), so every block maximum occurs."""
+    mags = np.arange(0x0000, 0x7F80, dtype=np.uint16)         # 0 .. largest finite
+    rows = len(mags) // 16 * 16
+    blk = np.zeros((len(mags), 16), np.uint16)
+    blk[:, 0] = mags
+    blk[:, 1] = mags | 0x8000
+    blk[:, 2:] = (mags[:, None] >> 1) + np.arange(14, dtype=np.uint16)[None, :] % 3
+    return blk[:rows].reshape(-1, 256)
+
+
+@pytest.mark.parametrize("ts", [2.0 ** -126, 2.0 ** -101, 2.0 ** -100, 3.1e-27, 1.0 / 2688,
+                                0.0371, 1.0, 447.0, 6.0e9, 2.0 ** 100, 1.3e35])
+def test_quantize_scale_codes_every_magnitude(Q, ts):
+    """Caller-given tensor scales across the fp32 range, on blocks whose
+    maxima run through every finite bf16 magnitude: block-scale codes and
+    element codes bit-exact (the block-scale code comes from an fp32 quotient
+    corrected against exact thresholds for s_t >= 2^-100, from the fp64
+    quotient below)."""
+    _check(Q, _all_magnitudes(), ts=np.float32(ts))
+
+
 def test_quantize_empty(Q):
     x = torch.zeros((0, 64), dtype=torch.int16, device="cuda:0")
     nib, sc, t = Q.quads_nvfp4_quantize(x)
