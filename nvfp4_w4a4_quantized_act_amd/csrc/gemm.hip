@@ -664,10 +664,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
 
 using namespace quads;
 
+// Workspace: only the tiled kernel's gathered compensation uses one (W[:, S]
+// as fp16, E * N * k * 2 bytes, for long contractions with k above 256).
 extern "C" size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int32_t E,
                                          int64_t N) {
-    (void)rows; (void)K; (void)k; (void)E; (void)N;
-    return 0;
+    (void)rows;
+    return gemm_v3_gather_ws(K, k, E, N);
 }
 
 // Both entry points: a_ts_rows is null (one tensor scale a_ts[0]) or the
@@ -696,7 +698,8 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
         return QUADS_EINVAL;
     if (k > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale) || !ok_ptr(r_ts) || !ok_ptr(sel)))
         return QUADS_EINVAL;
-    if (ws_bytes < quads_moe_w4a4_gemm_ws(rows, K, k, E, N)) return QUADS_EWORKSPACE;
+    const size_t need = quads_moe_w4a4_gemm_ws(rows, K, k, E, N);
+    if (ws_bytes < need || (need > 0 && !ok_ptr(ws))) return QUADS_EWORKSPACE;
     if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
@@ -716,6 +719,9 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     // accumulators every kAccChain channels
     const bool one_chain = K + k <= kSingleChainMax;
     if (!one_chain && gemm_v3_fits(g)) return launch_gemm_v3(g, st);
+    if (!one_chain && gemm_v3_gather_fits(g) && ws_bytes >= gemm_v3_gather_ws(K, k, E, N) &&
+        ws != nullptr)
+        return launch_gemm_v3_gather(g, ws, st);
     if (one_chain && K % v2::BK == 0 && k % v2::BK == 0) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
                                                           : (N + v2::BN - 1) / v2::BN;

@@ -28,6 +28,9 @@ struct GemmArgs {
     // 1: sel is [E, k] and r_ts [E], one selection and residual scale per
     // expert (activations in packed order); 0: one shared sel [k], r_ts [1].
     int sel_per_expert;
+    // The tiled kernel's gathered compensation (k above kCapMaxV3): W[:, S]
+    // as exact fp16 values [E, N, k] in the caller's workspace, else null.
+    const _Float16* w_sel;
 };
 
 // Once a work-group knows its expert e: point sel and r_ts at that expert's
@@ -339,6 +342,11 @@ constexpr int kSingleChainMax = 1152;
 constexpr int kCapMaxV3 = 256;
 bool gemm_v3_fits(const GemmArgs& g);
 int launch_gemm_v3(const GemmArgs& g, hipStream_t st);
+// Long chains with k above kCapMaxV3 (k % 128 == 0, one shared selection):
+// the tiled kernel with W[:, S] gathered into `ws` (gemm_v3_gather_ws bytes).
+size_t gemm_v3_gather_ws(int64_t K, int64_t k, int64_t E, int64_t N);
+bool gemm_v3_gather_fits(const GemmArgs& g);
+int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st);
 constexpr int kDecodeMaxRows = 128;
 constexpr int kDecodeAllRows = 512;
 bool gemm_decode_fits(const GemmArgs& g);

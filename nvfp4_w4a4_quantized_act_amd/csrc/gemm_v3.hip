@@ -86,6 +86,12 @@ struct WRaw {
     uint32_t s;
 };
 
+// fp16 weight columns of one gathered-compensation chunk for one thread:
+// 32 channels of one weight row (64 bytes).
+struct WsRaw {
+    uint4 a, b, c, d;
+};
+
 __device__ __forceinline__ uint32_t word4(const uint4& v, int j) {
     return j == 0 ? v.x : (j == 1 ? v.y : (j == 2 ? v.z : v.w));
 }
@@ -191,10 +197,10 @@ __device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
         for (int n = 0; n < 8; ++n) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
-template <int kEpi, int MACT, bool LATE>
+template <int kEpi, int MACT, bool LATE, bool kGather>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
                                          const int* s_sel, const int* s_cs, const Ctx& x,
-                                         int wr, int wh,
+                                         int wr, int wh, int64_t wfull,
                                          int kc, int wave, int lane, const int64_t src[2],
                                          int m0, int mend, int f0, int e) {
     // The MFMA accumulators X restart from zero every kFlush chunks (1024
@@ -204,7 +210,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     zero_set<MACT>(T);
     const int nk = x.nk;
     // the epilogue's scales, requested now rather than after the loop
-    const float s_tr = kc > 0 ? g.r_ts[0] : 0.0f;
+    const float s_tr = g.k > 0 ? g.r_ts[0] : 0.0f;
     const float s_tw = g.w_ts[e];
     const float ca0 = tensor_scale_a(g) * s_tw;
     // residual codes and scale bytes of the compensation's first two steps,
@@ -292,9 +298,78 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
         chunk(c + 1, a1, a0, w0, w1);
     }
 
+    const bool comp = (kGather ? g.k : kc) > 0 && s_tr > 0.0f;
+    if (kGather && comp) {
+        // Gathered compensation: R x W[:, S] as further 128-channel chunks,
+        // the residual codes through the activation path and W[:, S] (exact
+        // fp16, gathered into the workspace) copied into the LDS tile.  X
+        // restarts every kFlush chunks; a finished segment joins the totals
+        // as X rho (rho = s_tR / s_tA, at most 1), the last one stays in X
+        // for the epilogue's s_tR s_tW.
+        Ctx xr = x;
+        xr.nk = g.k / BK;
+        xr.a_nib = g.r_nib;
+        xr.a_sc = g.r_scale;
+        const int rq = lane >> 4;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            xr.a_off[f] = src[f] * (g.k / 2) + 16 * rq;
+            xr.s_off[f] = src[f] * (g.k / kBlock) + 2 * rq;
+        }
+        const _Float16* wsrow = g.w_sel + wfull * g.k + 32 * wh;
+        const float rho = s_tr / tensor_scale_a(g);
+        const int nkc = xr.nk;
+        auto load_ws = [&](int cc) {
+            const int c2 = cc < nkc ? cc : nkc - 1;
+            const uint4* p = reinterpret_cast<const uint4*>(wsrow + BK * c2);
+            return WsRaw{p[0], p[1], p[2], p[3]};
+        };
+        auto store_ws = [&](const WsRaw& v, char* wb) {
+            char* base = wb + wblock_off(wr, 32 * wh);
+            *reinterpret_cast<uint4*>(base) = v.a;
+            *reinterpret_cast<uint4*>(base + 1024) = v.b;
+            *reinterpret_cast<uint4*>(base + 2048) = v.c;
+            *reinterpret_cast<uint4*>(base + 3072) = v.d;
+        };
+        ARaw r0, r1;
+        load_a<MACT>(xr, 0, r0);
+        WsRaw wv = load_ws(0);
+        store_ws(wv, wbuf);
+        __syncthreads();
+        auto cchunk = [&](int cc, ARaw& rc, ARaw& rn) {
+            if (cc >= nkc) return;
+            load_a<MACT>(xr, cc + 1, rn);
+            wv = load_ws(cc + 1);
+            __builtin_amdgcn_sched_barrier(0);
+            const char* wb = wb_lane + (cc & 1) * (BN * BK * 2);
+            f16x8 wf[8];
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                if (MACT > 0) read_wf(wb, st, wf);
+                mma_step<MACT>(wf, rc, st, X);
+            }
+            __builtin_amdgcn_s_setprio(0);
+            if (cc + 1 < nkc) store_ws(wv, wbuf + ((cc + 1) & 1) * (BN * BK * 2));
+            if ((cc + 1) % kFlush == 0 && cc + 1 < nkc) {
+#pragma unroll
+                for (int f = 0; f < MACT; ++f)
+#pragma unroll
+                    for (int n = 0; n < 8; ++n)
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) T[f][n][v] = fmaf(X[f][n][v], rho, T[f][n][v]);
+                zero_set<MACT>(X);
+            }
+            __syncthreads();
+        };
+        for (int cc = 0; cc < nkc; cc += 2) {
+            cchunk(cc, r0, r1);
+            cchunk(cc + 1, r1, r0);
+        }
+    }
+
     // compensation: R x W[:, S] into X (zero), from the captured columns
-    const bool comp = kc > 0 && s_tr > 0.0f;
-    if (comp && MACT > 0) {
+    if (!kGather && comp && MACT > 0) {
         const int r = lane & 15, q = lane >> 4;
         const int nsteps = (kc + 31) / 32;
         for (int s = 0; s < nsteps; ++s) {
@@ -406,7 +481,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     }
 }
 
-template <int kEpi>
+template <int kEpi, bool kGather>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n, int grp) {
     __shared__ __align__(16) char wbuf[2 * BN * BK * 2];
     __shared__ __align__(16) _Float16 cap[BN * kCapLd];
@@ -464,7 +539,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
 
     // compensation: selected channels to LDS, padding columns of the capture
     // buffer zeroed (a step reads 32 columns)
-    const int kc = g.k;
+    const int kc = kGather ? 0 : g.k;                     // channels to capture
     if (kc > 0) {
         for (int i = tid; i < kc; i += kThreads) s_sel[i] = g.sel[i];
         // s_cs[c] = the first selected index whose channel is in chunk c or
@@ -488,8 +563,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     switch (mact + (wave >= 4 ? 4 : 0)) {
 #define QUADS_V3_TILE(M, L)                                                                     \
     case M + (L ? 4 : 0):                                                                       \
-        run_tile<kEpi, M, L>(g, wbuf, cap, s_sel, s_cs, x, wr, wh, kc, wave, lane, src, m0,    \
-                             mend, f0, e);                                                      \
+        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, s_sel, s_cs, x, wr, wh, wfull, kc, wave,   \
+                                      lane, src, m0, mend, f0, e);                              \
         break;
         QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)
         QUADS_V3_TILE(1, true) QUADS_V3_TILE(0, true)
@@ -505,26 +580,84 @@ bool gemm_v3_fits(const GemmArgs& g) {
            (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
 }
 
-int launch_gemm_v3(const GemmArgs& g, hipStream_t st) {
+namespace v3 {
+
+// W[:, S] of every weight row as exact fp16 values (v * s_b: at most 6
+// significant bits, magnitude in [2^-10, 2688]), [E * N, k] row-major: a
+// thread writes 8 consecutive selected channels of one row.
+__global__ __launch_bounds__(256) void k_gather_wsel(const uint8_t* __restrict__ w_nib,
+                                                     const uint8_t* __restrict__ w_scale,
+                                                     const int32_t* __restrict__ sel, int K, int k,
+                                                     int64_t nrows, _Float16* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = k / 8;
+    if (t >= nrows * per_row) return;
+    const int64_t row = t / per_row;
+    const int j0 = (int)(t - row * per_row) * 8;
+    const uint8_t* nrow = w_nib + row * (K / 2);
+    const uint8_t* srow = w_scale + row * (K / kBlock);
+    _Float16 v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int c = sel[j0 + i];
+        c = c < 0 ? 0 : (c >= K ? K - 1 : c);                // bounds only: sel < K
+        const uint32_t code = (nrow[c >> 1] >> (4 * (c & 1))) & 15u;
+        const _Float16 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0)[0];
+        const _Float16 sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(srow[c / kBlock], 1.0f,
+                                                                     false)[0];
+        v[i] = e * sb;
+    }
+    *reinterpret_cast<f16x8*>(out + row * k + j0) = (f16x8){v[0], v[1], v[2], v[3], v[4], v[5],
+                                                             v[6], v[7]};
+}
+
+template <bool kGather>
+int launch_tiles(const GemmArgs& g, hipStream_t st) {
     const bool sw = g.epilogue == QUADS_EPI_SWIGLU;
-    const int64_t nt_n = sw ? (g.N / 2 + v3::BN / 2 - 1) / (v3::BN / 2) : (g.N + v3::BN - 1) / v3::BN;
+    const int64_t nt_n = sw ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     // M-tiles: at most rows / BM + one partial tile per expert that has tiles
     // (with a decode share, only experts above g.dec_rows rows)
     const int64_t big = g.dec_rows > 0 ? g.rows / (g.dec_rows + 1) : g.E;
-    const int64_t nt_m = (g.rows + v3::BM - 1) / v3::BM + (g.offsets ? (big < g.E ? big : g.E) : 0);
+    const int64_t nt_m = (g.rows + BM - 1) / BM + (g.offsets ? (big < g.E ? big : g.E) : 0);
     const int64_t grp = 2 * nt_n;
     const int64_t span = grp * v2::kXcds;
     const int64_t blocks = (nt_m * nt_n + span - 1) / span * span;
     if (blocks >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
     const dim3 grid((unsigned)blocks);
     if (sw)
-        hipLaunchKernelGGL(v3::k_gemm_w4a4_v3<QUADS_EPI_SWIGLU>, grid, dim3(v3::kThreads), 0, st, g,
-                           (int)nt_n, (int)grp);
+        hipLaunchKernelGGL((k_gemm_w4a4_v3<QUADS_EPI_SWIGLU, kGather>), grid, dim3(kThreads), 0, st,
+                           g, (int)nt_n, (int)grp);
     else
-        hipLaunchKernelGGL(v3::k_gemm_w4a4_v3<QUADS_EPI_NONE>, grid, dim3(v3::kThreads), 0, st, g,
-                           (int)nt_n, (int)grp);
+        hipLaunchKernelGGL((k_gemm_w4a4_v3<QUADS_EPI_NONE, kGather>), grid, dim3(kThreads), 0, st,
+                           g, (int)nt_n, (int)grp);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
+}
+
+}  // namespace v3
+
+int launch_gemm_v3(const GemmArgs& g, hipStream_t st) { return v3::launch_tiles<false>(g, st); }
+
+size_t gemm_v3_gather_ws(int64_t K, int64_t k, int64_t E, int64_t N) {
+    const bool shape = K % v3::BK == 0 && K <= v3::BK * v3::kMaxChunksV3 && k > kCapMaxV3 &&
+                       k % v3::BK == 0 && k <= K && K + k > kSingleChainMax &&
+                       N * K / 2 < ((int64_t)1 << 31) && E > 0 && N > 0;
+    return shape ? align_up((size_t)E * (size_t)N * (size_t)k * 2, 256) : 0;
+}
+
+bool gemm_v3_gather_fits(const GemmArgs& g) {
+    return !g.sel_per_expert && g.a_ts_rows == nullptr &&
+           gemm_v3_gather_ws(g.K, g.k, g.E, g.N) > 0;
+}
+
+int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st) {
+    const int64_t nrows = (int64_t)g.E * g.N;
+    const int64_t threads = nrows * (g.k / 8);
+    hipLaunchKernelGGL(v3::k_gather_wsel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
+                       g.w_nib, g.w_scale, g.sel, g.K, g.k, nrows, static_cast<_Float16*>(ws));
+    QUADS_CHECK_LAUNCH();
+    g.w_sel = static_cast<const _Float16*>(ws);
+    return v3::launch_tiles<true>(g, st);
 }
 
 }  // namespace quads

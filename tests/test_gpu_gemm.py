@@ -68,7 +68,11 @@ def _assert_close(got, exp, bound, bf16=False):
 
 
 @pytest.mark.parametrize("m,kd,n,k", [(32, 256, 128, 16), (200, 272, 136, 32), (64, 512, 256, 0),
-                                      (1, 16, 1, 16), (129, 1024, 130, 64)])
+                                      (1, 16, 1, 16), (129, 1024, 130, 64),
+                                      # k > 256 at a long contraction: the tiled kernel
+                                      # with W[:, S] gathered into the workspace
+                                      (300, 1024, 256, 512), (64, 2048, 130, 1024),
+                                      (256, 4096, 128, 2048)])
 def test_dense(Q, m, kd, n, k):
     print(f"dense gemm m={m} K={kd} N={n} k={k}", flush=True)
     rng = np.random.default_rng(m * 7 + kd + n + k)
@@ -221,7 +225,8 @@ def test_grouped_gather_rows(Q, t, h, n, k):
     _assert_close(y, exp, bound)
 
 
-@pytest.mark.parametrize("k,h,feat", [(16, 192, 80), (64, 256, 200), (0, 128, 64)])
+@pytest.mark.parametrize("k,h,feat", [(16, 192, 80), (64, 256, 200), (0, 128, 64),
+                                      (512, 1024, 200), (1024, 2048, 96)])
 def test_grouped_swiglu(Q, k, h, feat):
     ids, x, w = _moe_case(9 + k, 600, 6, 2, h, 2 * feat, k)
     off, rt, pos = OM.pack_routes(ids, 6)
