@@ -65,7 +65,9 @@ TRACE_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_kernel_trace.md"
 PMC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_counters.md")
 GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_quantized_act_amd", "csrc", f)
                 for f in ("gemm.hip", "gemm_v3.hip", "gemm_tiles.h", "common.h")]
-GEMM_KERNEL_KEY = "k_gemm_w4a4_v3<1>"     # the gate/up (SwiGLU) GEMM kernel
+# the gate/up (SwiGLU) GEMM call: the tiled kernel, and the decode kernel that
+# takes the rows past 256 of experts of 257 .. 320 rows
+GEMM_KERNEL_KEYS = ("k_gemm_w4a4_v3<1, false>", "k_gemm_w4a4_decode<1,")
 FLUSH_BYTES = 512 << 20
 
 
@@ -142,8 +144,9 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
             raise SystemExit("no copy kernel dispatch found (run with --copy-probe-mib)")
         return max(vals)
 
-    g_f = sum(pick(fetch, GEMM_KERNEL_KEY)) / len(pick(fetch, GEMM_KERNEL_KEY))
-    g_w = sum(pick(write, GEMM_KERNEL_KEY)) / len(pick(write, GEMM_KERNEL_KEY))
+    # per launch of the call: the mean per dispatch of each of its kernels, summed
+    g_f = sum(sum(pick(fetch, key)) / len(pick(fetch, key)) for key in GEMM_KERNEL_KEYS)
+    g_w = sum(sum(pick(write, key)) / len(pick(write, key)) for key in GEMM_KERNEL_KEYS)
     c_f, c_w = copy_val(fetch), copy_val(write)
     copy_bytes = copy_mib * (1 << 20)
     f_scale, w_scale = copy_bytes / c_f, copy_bytes / c_w
@@ -151,6 +154,10 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
     lines = [
         "# HBM traffic of the gate/up GEMM: MoE FFN, 128 experts, T=4096, hidden 2048, "
         "intermediate 768, top-8, RAC k=64",
+        "",
+        "The call is two launches: the tiled kernel `v3::k_gemm_w4a4_v3<1, false>` and the decode "
+        "kernel `dec::k_gemm_w4a4_decode<1, 2, true>` for the rows past 256 of experts of 257 .. "
+        "320 rows; the figures below add the two kernels' per-dispatch means.",
         "",
         "Commands (repository root, one MI355X), then this summary on any host:",
         "",
@@ -167,8 +174,8 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
         "",
         "| quantity | value |",
         "|---|---|",
-        f"| GEMM FETCH_SIZE per dispatch (KiB) | {g_f:.1f} |",
-        f"| GEMM WRITE_SIZE per dispatch (KiB) | {g_w:.1f} |",
+        f"| GEMM FETCH_SIZE per call (KiB) | {g_f:.1f} |",
+        f"| GEMM WRITE_SIZE per call (KiB) | {g_w:.1f} |",
         f"| copy of {copy_mib} MiB: FETCH_SIZE (KiB) | {c_f:.1f} |",
         f"| copy of {copy_mib} MiB: WRITE_SIZE (KiB) | {c_w:.1f} |",
         f"| scale, read bytes per FETCH_SIZE unit | {f_scale:.2f} |",
@@ -239,11 +246,14 @@ def trace_summary(trace_dir):
         "",
         "Durations are the trace's start-to-end times in microseconds, grouped by kernel and "
         "launch shape (work-groups in x and y, threads per work-group), so that launches of one "
-        "kernel on different workloads show apart.  The gate/up GEMM is "
-        "`v3::k_gemm_w4a4_v3<1>`: the prefill layer's launches are its smallest grid, config "
-        "5's (k = 0, 64, 256) the largest; config 5 at k = 2048 runs `k_gemm_w4a4<1>`.  The "
-        "down GEMM (768 + 64 channels, one accumulator chain) is `v2::k_gemm_w4a4_v2<0>`; "
-        "config 2's GEMM is `v3::k_gemm_w4a4_v3<0>`.",
+        "kernel on different workloads show apart.  The prefill layer's gate/up GEMM is "
+        "`v3::k_gemm_w4a4_v3<1, false>` at (3072, 1) x 512 plus "
+        "`dec::k_gemm_w4a4_decode<1, 2, true>` at (1536, 1) x 128 for the rows past 256 of "
+        "experts of 257 .. 320 rows; config 5's gate/up GEMMs are the tiled kernel at (13824, 1) "
+        "x 512 (`<1, true>`: k = 2048, with the gathered compensation); the decode layer's "
+        "GEMMs are the decode kernel at (1632, 1) and (2176, 1).  The down GEMM (768 + 64 "
+        "channels, one accumulator chain) is `v2::k_gemm_w4a4_v2<0>`; config 2's GEMM is "
+        "`v3::k_gemm_w4a4_v3<0, false>` at (512, 1).",
         "",
         "| kernel | work-groups (x, y) x threads | calls | total (us) | average (us) | min (us) | "
         "max (us) | % |",
@@ -578,7 +588,10 @@ def main():
                    "tokens": T, "experts": E, "hidden": H, "intermediate": I, "top_k": TOPK,
                    "rac_k": KR, "packed_rows": rows, "gemm_operands": "nvfp4 -> exact fp16",
                    "accumulate": "fp32", "parallelism": "single_gpu"},
-        "roofline": {"bound": "mfma", "kernel": "v3::k_gemm_w4a4_v3<1> (gate/up GEMM, SwiGLU epilogue)",
+        "roofline": {"bound": "mfma",
+                     "kernel": "gate/up GEMM call, SwiGLU epilogue: v3::k_gemm_w4a4_v3<1, false> "
+                               "(256-row tiles) + dec::k_gemm_w4a4_decode<1, 2, true> (rows past "
+                               "256 of experts of 257..320 rows)",
                      "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic()},
         "cpu_baseline": cpu,

@@ -53,7 +53,7 @@ __device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int ti
     const int e0 = threadIdx.x * per;
     const int e1 = e0 + per < E ? e0 + per : E;
     int local = 0;
-    for (int e = e0; e < e1; ++e) local += (v2::rows_of(offsets, e, skip) + bm - 1) / bm;
+    for (int e = e0; e < e1; ++e) local += (v2::rows_of(offsets, e, skip, 0) + bm - 1) / bm;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
     int x = local;
     for (int off = 1; off < 64; off <<= 1) {
@@ -67,7 +67,7 @@ __device__ bool find_tile_bm(const int32_t* offsets, int E, int64_t rows, int ti
     for (int i = 0; i < wid; ++i) base += s_scan[i];
     int run = x - local + base;
     for (int e = e0; e < e1; ++e) {
-        const int t = (v2::rows_of(offsets, e, skip) + bm - 1) / bm;
+        const int t = (v2::rows_of(offsets, e, skip, 0) + bm - 1) / bm;
         if (tile >= run && tile < run + t) {     // exactly one thread matches
             s_res[0] = e;
             s_res[1] = offsets[e] + (tile - run) * bm;
@@ -583,7 +583,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     const int tile = (slot / grp) * (kXcds * grp) + (h % kXcds) * grp + slot % grp;
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
-    if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows)) return;
+    if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows,
+                            g.tail_rows))
+        return;
     bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
@@ -718,11 +720,27 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     // 256 x 256-tile kernel; longer chains: the kernels that restart their
     // accumulators every kAccChain channels
     const bool one_chain = K + k <= kSingleChainMax;
-    if (!one_chain && gemm_v3_fits(g)) return launch_gemm_v3(g, st);
+    const bool tiles_v3 = !one_chain && gemm_v3_fits(g);
+    const bool tiles_v2 = one_chain && K % v2::BK == 0 && k % v2::BK == 0;
+    // near 256 rows per expert on average, the experts of 257 .. 320 rows
+    // leave their rows past 256 to the decode kernel (which streams the
+    // expert's weights once for them), so the long-chain kernel's 256-row
+    // tiles stay full.  Measured on the 128-expert layer (32768 packed rows,
+    // half of the experts at 257 .. 301 rows): gate/up (K = 2048 + 64) 365 ->
+    // 295 + 57 us; for the single-chain kernel (down, K = 768 + 64) the
+    // decode share costs more than the tiles save (200 -> 175 + 33 us), so
+    // it keeps its split tiles.
+    if (tiles_v3 && g.dec_rows == 0 && offsets != nullptr && rows <= (int64_t)512 * E &&
+        gemm_decode_tail_fits(g)) {
+        g.tail_rows = kTailRows;
+        const int rc = launch_gemm_decode(g, st);
+        if (rc != QUADS_OK) return rc;
+    }
+    if (tiles_v3) return launch_gemm_v3(g, st);
     if (!one_chain && gemm_v3_gather_fits(g) && ws_bytes >= gemm_v3_gather_ws(K, k, E, N) &&
         ws != nullptr)
         return launch_gemm_v3_gather(g, ws, st);
-    if (one_chain && K % v2::BK == 0 && k % v2::BK == 0) {
+    if (tiles_v2) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
                                                           : (N + v2::BN - 1) / v2::BN;
         // M-tiles: at most rows / BM + one partial tile per expert that has

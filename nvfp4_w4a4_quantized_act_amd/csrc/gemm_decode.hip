@@ -133,6 +133,14 @@ static __host__ __device__ inline int decode_units_max(const GemmArgs& g) {
     return g.E + (g.dec_rows > kDecodeMaxRows ? (int)(g.rows / kDecodeMaxRows) : 0);
 }
 
+// Rows of an n-row expert this kernel takes: its tail (expert_tail) when the
+// tiled kernel takes the full 256-row blocks, else all of it when it has
+// 1 .. dec_rows rows.  They are the expert's last rows.
+__device__ __forceinline__ int decode_rows(const GemmArgs& g, int n) {
+    if (g.tail_rows > 0) return expert_tail(n, g.tail_rows);
+    return n > 0 && n <= g.dec_rows ? n : 0;
+}
+
 // Grid: 8 ceil(units / 8) x slabs work-groups over the units, ranked in
 // expert and row order: block b runs on XCD b % 8 and takes slab
 // (b / 8) % slabs of the unit of rank 8 ((b / 8) / slabs) + b % 8, so all
@@ -172,8 +180,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         const int e0 = lane * per, e1 = e0 + per < g.E ? e0 + per : g.E;
         int na = 0;
         for (int x = e0; x < e1; ++x) {
-            const int n = g.offsets[x + 1] - g.offsets[x];
-            na += n > 0 && n <= g.dec_rows ? (n + kDecodeMaxRows - 1) / kDecodeMaxRows : 0;
+            const int n = decode_rows(g, g.offsets[x + 1] - g.offsets[x]);
+            na += (n + kDecodeMaxRows - 1) / kDecodeMaxRows;
         }
         int inc = na;
 #pragma unroll
@@ -186,16 +194,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         if (rank >= inc - na && rank < inc) {                       // exactly one lane
             int rr = rank - (inc - na);
             for (int x = e0; x < e1; ++x) {
-                const int n = g.offsets[x + 1] - g.offsets[x];
-                const int u = n > 0 && n <= g.dec_rows ? (n + kDecodeMaxRows - 1) / kDecodeMaxRows
-                                                       : 0;
+                const int n = decode_rows(g, g.offsets[x + 1] - g.offsets[x]);
+                const int u = (n + kDecodeMaxRows - 1) / kDecodeMaxRows;
                 if (rr < u) { found = x; part = rr; break; }
                 rr -= u;
             }
         }
         const int src = __ffsll(__ballot(found >= 0)) - 1;
         e = __builtin_amdgcn_readlane(found, src);
-        p0 = g.offsets[e] + kDecodeMaxRows * __builtin_amdgcn_readlane(part, src);
+        const int taken = decode_rows(g, g.offsets[e + 1] - g.offsets[e]);
+        p0 = g.offsets[e + 1] - taken + kDecodeMaxRows * __builtin_amdgcn_readlane(part, src);
         cnt = min(g.offsets[e + 1] - p0, kDecodeMaxRows);
     } else if (rank > 0 || cnt <= 0 || cnt > g.dec_rows) {
         return;                                       // one expert, all rows
@@ -458,6 +466,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
 }
 
 }  // namespace dec
+
+// The decode kernel for the tails of experts just above a multiple of 256
+// rows (tail_rows set by the caller): its shape rules without the
+// rows-per-expert limit.
+bool gemm_decode_tail_fits(const GemmArgs& g) {
+    const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
+    return g.offsets != nullptr && g.K % dec::kChunk == 0 && g.k <= dec::kCapMax &&
+           slabs * 8 * ((g.E + 7) / 8) < ((int64_t)1 << 31) &&
+           (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
+}
 
 bool gemm_decode_fits(const GemmArgs& g) {
     const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;

@@ -31,7 +31,16 @@ struct GemmArgs {
     // The tiled kernel's gathered compensation (k above kCapMaxV3): W[:, S]
     // as exact fp16 values [E, N, k] in the caller's workspace, else null.
     const _Float16* w_sel;
+    // > 0: an expert of 257 .. 256 + tail_rows rows leaves its rows past the
+    // first 256 (its tail) to the decode kernel, so that the 256-row tiled
+    // kernels run one full tile for it instead of two part-filled ones.
+    int tail_rows;
 };
+
+// Rows at the end of an n-row expert that belong to the decode kernel.
+__host__ __device__ inline int expert_tail(int n, int tail_rows) {
+    return tail_rows > 0 && n > 256 && n <= 256 + tail_rows ? n - 256 : 0;
+}
 
 // Once a work-group knows its expert e: point sel and r_ts at that expert's
 // selection and residual scale, so that the kernels read g.sel[i] and
@@ -122,15 +131,16 @@ __device__ __forceinline__ int wave_scan(int x, int lane) {
     return x;
 }
 
-// Experts with at most `skip` rows get no tiles (another kernel takes them).
-__device__ __forceinline__ int rows_of(const int32_t* offsets, int e, int skip) {
+// Rows of expert e the tiled kernel takes: none for an expert of at most
+// `skip` rows, and not its tail (expert_tail) -- the decode kernel takes those.
+__device__ __forceinline__ int rows_of(const int32_t* offsets, int e, int skip, int tail_rows) {
     const int n = offsets[e + 1] - offsets[e];
-    return n > skip ? n : 0;
+    return n > skip ? n - expert_tail(n, tail_rows) : 0;
 }
 
 template <int BMT>
 __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
-                               int* m0_out, int* mend_out, int skip = 0) {
+                               int* m0_out, int* mend_out, int skip = 0, int tail_rows = 0) {
     constexpr int kH = BMT / 32;                  // tile heights 1 .. kH blocks
     if (offsets == nullptr) {
         const int64_t m0 = (int64_t)tile * BMT;
@@ -148,7 +158,7 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, in
     for (int q = 0; q < kH; ++q) cnt[q] = 0;
     for (int e = e0; e < e1; ++e) {
         int t;
-        const int hgt = tile_height(rows_of(offsets, e, skip), BMT, &t);
+        const int hgt = tile_height(rows_of(offsets, e, skip, tail_rows), BMT, &t);
 #pragma unroll
         for (int q = 0; q < kH; ++q) cnt[q] += hgt == q + 1 ? t : 0;
     }
@@ -167,13 +177,13 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, in
             int run = base + x - cnt[q], fe = -1, fm0 = 0, fme = 0;
             if (tile >= run && tile < run + cnt[q]) {
                 for (int e = e0; e < e1; ++e) {
-                    const int n = rows_of(offsets, e, skip);
+                    const int n = rows_of(offsets, e, skip, tail_rows);
                     int t;
                     if (tile_height(n, BMT, &t) != hgt) continue;
                     if (tile < run + t) {
                         fe = e;
                         fm0 = offsets[e] + (tile - run) * hgt * 32;
-                        fme = fm0 + hgt * 32 < offsets[e + 1] ? fm0 + hgt * 32 : offsets[e + 1];
+                        fme = fm0 + hgt * 32 < offsets[e] + n ? fm0 + hgt * 32 : offsets[e] + n;
                         break;
                     }
                     run += t;
@@ -350,6 +360,9 @@ int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st);
 constexpr int kDecodeMaxRows = 128;
 constexpr int kDecodeAllRows = 512;
 bool gemm_decode_fits(const GemmArgs& g);
+bool gemm_decode_tail_fits(const GemmArgs& g);
 int launch_gemm_decode(const GemmArgs& g, hipStream_t st);
+// Tail rows the decode kernel takes from experts just above 256 rows.
+constexpr int kTailRows = 64;
 
 }  // namespace quads

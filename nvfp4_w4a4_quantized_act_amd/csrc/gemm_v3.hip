@@ -495,7 +495,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     const int tile = (slot / grp) * (v2::kXcds * grp) + (h % v2::kXcds) * grp + slot % grp;
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
-    if (!v2::find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows))
+    if (!v2::find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows,
+                                g.tail_rows))
         return;
     bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;

@@ -225,6 +225,34 @@ def test_grouped_gather_rows(Q, t, h, n, k):
     _assert_close(y, exp, bound)
 
 
+@pytest.mark.parametrize("h,k", [(2048, 64), (512, 64), (512, 0)])
+def test_expert_tails(Q, h, k):
+    """Experts of 256, 257, 300, 320 and 321 rows (and smaller ones, and an
+    empty one) near 256 rows per expert on average.  At K = 2048 the rows
+    past 256 of an expert of 257 .. 320 rows go to the decode kernel and the
+    rest to full 256-row tiles of the long-chain kernel; at K = 512 the
+    single-chain kernel splits such experts over two tiles.  Every row is
+    checked, plain and SwiGLU."""
+    counts = np.array([256, 257, 300, 0, 320, 321, 100, 250], np.int64)
+    off = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(off[-1])
+    rng = np.random.default_rng(h + k)
+    x = synth.f32_to_bf16_bits(rng.standard_normal((rows, h)).astype(np.float32))
+    feat = 96
+    w = synth.weights(rng, len(counts), 2 * feat, h)
+    out, wq = _operands(x, w, k)
+    print(f"expert tails K={h} k={k}", flush=True)
+    y = _gpu_gemm(Q, out, wq, 2 * feat, k, offsets=off).cpu().numpy()
+    exp, bound = _oracle(out, wq, k, off)
+    _assert_close(y, exp, bound)
+    hh = _gpu_gemm(Q, out, wq, 2 * feat, k, offsets=off, epilogue=Q.EPI_SWIGLU,
+                   out_dtype=Q.OUT_BF16).cpu().numpy().view(np.uint16)
+    ref = F.bf16_to_f64(OM.swiglu(y.astype(np.float64)))
+    got = F.bf16_to_f64(hh)
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp * 1.0001)
+
+
 @pytest.mark.parametrize("k,h,feat", [(16, 192, 80), (64, 256, 200), (0, 128, 64),
                                       (512, 1024, 200), (1024, 2048, 96)])
 def test_grouped_swiglu(Q, k, h, feat):
