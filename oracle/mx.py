@@ -18,11 +18,23 @@ Definitions (reading: the OCP MX rule with round-to-nearest-even elements):
     value; the sign bit is the sign bit of x;
   * decode: v * 2^E.
 The GEMM is the plain sum over k of the decoded products, in fp64.
+
+RAC on the MX FP4 mode (section 3.3, Eq. (20)-(24), with the MX FP4 format
+the "FP4" paragraph of section 2.2 sets beside NVFP4): the same steps as
+oracle/rac.py with the MX quantizer in place of NVFP4 -- the residual
+r = RN32(x - DQ(Q(x))), the per-channel scores (Eq. (23) squared, the same
+fixed-order sum), S (Eq. (24), ties to the lower index, ascending), and the
+second pass: r[:, S] gathered and MX-quantized with 32-element blocks along
+the compacted index.  Readings: k is a multiple of 32 (whole MX blocks of
+the gathered residual); MX quantization is odd-symmetric (the shared
+exponent ignores signs, rounding is symmetric, the sign bit is copied), so
+Eq. (21) reads X~ = DQ(Q(x)) + scatter_S(DQ(Q(r_S))) as in oracle/rac.py.
 """
 
 import numpy as np
 
 from . import formats as F
+from . import rac as R
 
 MX_BLOCK = 32
 EMAX = {"fp8": 8, "fp4": 2}
@@ -100,4 +112,72 @@ def grouped_gemm(a, w, offsets, row_token=None, fmt="fp8"):
         xa = a_dq[rt[sl]]
         y[sl] = xa @ wd.T
         bound[sl] = np.abs(xa) @ np.abs(wd).T
+    return y, bound
+
+
+def residual(x, codes, scales, fmt="fp4"):
+    """r = RN32(x - DQ(Q(x))) [rows, K] float32 for the MX quantization of x.
+
+    The fp64 difference is exact (x and DQ have few significant bits and
+    the elements that round to zero return x itself); that is asserted."""
+    x = np.asarray(x, dtype=np.float64)
+    dq = dequantize(codes, scales, fmt)
+    diff = x - dq
+    bb = diff - x
+    err = (x - (diff - bb)) + (-dq - bb)         # TwoSum error term
+    if np.any(err != 0):
+        raise AssertionError("x - dq is not exact in fp64")
+    return diff.astype(np.float32)
+
+
+def rac_quantize(x, k, fmt="fp4"):
+    """RAC on exact values x [rows, K] with the MX quantizer: main codes and
+    scales, the fp32 residual, scores, S and the second pass ([rows, k]
+    layout, 32-element blocks along the compacted index)."""
+    x = np.asarray(x, dtype=np.float64)
+    rows, kdim = x.shape
+    if k % MX_BLOCK or not 0 <= k <= kdim:
+        raise ValueError("k must be a multiple of 32 in [0, K]")
+    codes, scales = quantize(x, fmt)
+    r = residual(x, codes, scales, fmt)
+    score = R.channel_scores(r)
+    sel = R.select_channels(score, k)
+    if k:
+        r_codes, r_scales = quantize(r[:, sel].astype(np.float64), fmt)
+    else:
+        r_codes = np.zeros((rows, 0), np.uint8)
+        r_scales = np.zeros((rows, 0), np.uint8)
+    return dict(codes=codes, scales=scales, r=r, score=score, sel=sel, r_codes=r_codes,
+                r_scales=r_scales)
+
+
+def compensated(out, fmt="fp4"):
+    """X~ of Eq. (21) (fp64): the dequantized main codes plus, on S, the
+    dequantized second pass."""
+    xt = dequantize(out["codes"], out["scales"], fmt)
+    if len(out["sel"]):
+        xt[:, out["sel"]] += dequantize(out["r_codes"], out["r_scales"], fmt)
+    return xt
+
+
+def grouped_gemm_rac(a, r, sel, w, offsets, row_token=None, fmt="fp4"):
+    """Y[p, n] = sum_j dq_a[row(p), j] dq_w[e(p), n, j]
+              + sum_i dq_r[row(p), i] dq_w[e(p), n, sel[i]]   (Eq. (21) into Eq. (6)),
+    in fp64, with the bound (the same sums of |products|).  r = (codes, scales)
+    of the second pass, or None for plain MX W4A4."""
+    y, bound = grouped_gemm(a, w, offsets, row_token, fmt)
+    if r is None or len(sel) == 0:
+        return y, bound
+    r_dq = dequantize(r[0], r[1], fmt)
+    offsets = np.asarray(offsets)
+    rows = int(offsets[-1])
+    rt = np.arange(rows) if row_token is None else np.asarray(row_token)
+    for e in range(len(offsets) - 1):
+        sl = slice(offsets[e], offsets[e + 1])
+        if offsets[e] == offsets[e + 1]:
+            continue
+        ws = dequantize(w[0][e], w[1][e], fmt)[:, sel]
+        xr = r_dq[rt[sl]]
+        y[sl] += xr @ ws.T
+        bound[sl] += np.abs(xr) @ np.abs(ws).T
     return y, bound

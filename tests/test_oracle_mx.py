@@ -130,3 +130,84 @@ def test_grouped_gemm_exact_small():
                             for k in range(64))
                 assert abs(Fraction(float(y[p, n])) - exact) <= Fraction(2) ** -40 * (
                     Fraction(float(bound[p, n])) + 1)
+
+
+# ---- RAC on the MX FP4 mode (section 3.3 with the MX FP4 quantizer) -------
+
+def _mx_rac_input(seed, rows=96, kdim=256):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_t(3, size=(rows, kdim))
+    x[:, 5] *= 20.0                                   # outlier channels
+    x[:, (77 % kdim)] *= 12.0
+    return x.astype(np.float32).astype(np.float64)   # fp32 inputs: exact residuals
+
+
+def test_mx_rac_never_increases_error():
+    """|x - X~| <= |x - DQ(Q(x))| element by element (0 is on the element
+    grid, so re-quantizing the residual never moves it further from 0), with
+    equality off S and a strict drop somewhere on S."""
+    x = _mx_rac_input(1)
+    out = M.rac_quantize(x, 64, "fp4")
+    dq = M.dequantize(out["codes"], out["scales"], "fp4")
+    xt = M.compensated(out, "fp4")
+    before, after = np.abs(x - dq), np.abs(x - xt)
+    assert np.all(after <= before)
+    off = np.setdiff1d(np.arange(x.shape[1]), out["sel"])
+    assert np.array_equal(after[:, off], before[:, off])
+    assert (after[:, out["sel"]] < before[:, out["sel"]]).any()
+    # the residual is x - DQ(Q(x)) itself, and S holds the k largest column sums of r^2
+    assert np.array_equal(out["r"].astype(np.float64), x - dq)
+    s = (out["r"].astype(np.float64) ** 2).sum(axis=0)
+    assert s[out["sel"]].min() >= np.delete(s, out["sel"]).max()
+
+
+def test_mx_rac_closed_form_block():
+    """A hand-built case: each 32-block holds one 6.0 and 0.25 elsewhere.  The
+    shared exponent is 0 (6 = 1.5 * 2^2), 0.25 lies midway between the codes 0
+    and 0.5 and rounds to the even code 0, so r = 0.25 there; the gathered
+    residual blocks are all 0.25 (exponent -4, code 4), exact.  So X~ = x on
+    the selected channels, and the scores pick the 0.25 channels of the
+    lowest indices (ties)."""
+    x = np.full((4, 64), 0.25)
+    x[:, 0] = 6.0
+    x[:, 32] = -6.0
+    out = M.rac_quantize(x, 32, "fp4")
+    assert np.all(out["scales"] == 127)
+    dq = M.dequantize(out["codes"], out["scales"], "fp4")
+    assert np.all(dq[:, [0, 32]] == x[:, [0, 32]]) and np.all(np.delete(dq, [0, 32], axis=1) == 0)
+    assert np.array_equal(out["sel"], np.r_[1:32, 33])            # 1..31, then 33
+    assert np.all(out["r_scales"] == 127 - 4)
+    xt = M.compensated(out, "fp4")
+    assert np.array_equal(xt[:, out["sel"]], x[:, out["sel"]])
+
+
+def test_mx_rac_gemm_exact_small():
+    """The compensated GEMM as an exact rational sum on a tiny grouped case,
+    against the compensated activations contracted by hand."""
+    rng = np.random.default_rng(21)
+    a = _mx_rac_input(3, rows=5, kdim=64)
+    out = M.rac_quantize(a, 32, "fp4")
+    w = rng.standard_normal((2, 3, 64))
+    wq = [M.quantize(w[e], "fp4") for e in range(2)]
+    wc = (np.stack([q[0] for q in wq]), np.stack([q[1] for q in wq]))
+    off = np.array([0, 2, 5])
+    rt = np.array([4, 0, 1, 3, 2])
+    y, bound = M.grouped_gemm_rac((out["codes"], out["scales"]),
+                                  (out["r_codes"], out["r_scales"]), out["sel"], wc, off, rt,
+                                  "fp4")
+    xt = M.compensated(out, "fp4")
+    ad = M.dequantize(out["codes"], out["scales"], "fp4")
+    rd = M.dequantize(out["r_codes"], out["r_scales"], "fp4")
+    for p in range(5):
+        e = 0 if p < 2 else 1
+        wd = M.dequantize(wc[0][e], wc[1][e], "fp4")
+        for n in range(3):
+            exact = sum(Fraction(float(xt[rt[p], j])) * Fraction(float(wd[n, j]))
+                        for j in range(64))
+            assert abs(Fraction(float(y[p, n])) - exact) <= Fraction(2) ** -40 * (
+                Fraction(float(bound[p, n])) + 1)
+            b = sum(abs(Fraction(float(ad[rt[p], j])) * Fraction(float(wd[n, j])))
+                    for j in range(64)) + sum(
+                abs(Fraction(float(rd[rt[p], i])) * Fraction(float(wd[n, out["sel"][i]])))
+                for i in range(32))
+            assert abs(Fraction(float(bound[p, n])) - b) <= Fraction(2) ** -40 * (b + 1)
