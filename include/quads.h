@@ -316,6 +316,48 @@ int quads_moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scale, const int3
                       const int32_t* offsets, int32_t E, int64_t N, int fmt, int epilogue,
                       int out_dtype, void* out, void* stream);
 
+/*
+ * RAC on the MX FP4 mode (section 3.3 with the MX FP4 format that the "FP4"
+ * paragraph of section 2.2 sets beside NVFP4).
+ *   x        bf16 [M, K], K % 32 == 0, K <= 8192;  k % 32 == 0, 0 <= k <= K
+ *   codes, scales   MX FP4 of x, identical to quads_mx_quantize
+ *   sel      out int32 [k]: the k channels with the largest sum over rows of
+ *            r^2, r = x - DQ(Q(x)) (exact in fp32), in the fixed order and with
+ *            the tie rule of quads_rac_quantize; ascending
+ *   r_codes, r_scales   out: MX FP4 of the gathered residual R[t, i] =
+ *            r[t, sel[i]] ([M, k/2], [M, k/32]: 32-element blocks along the
+ *            compacted index).  X~ = DQ(Q(x)) + scatter_sel(DQ(R)) is Eq. (21).
+ *   score_out  NULL or out fp64 [K]: the channel scores
+ * Workspace: quads_mx_rac_quantize_ws bytes.  With k == 0 only the codes
+ * (and the scores, when asked) are written; sel, r_codes, r_scales may be NULL.
+ */
+size_t quads_mx_rac_quantize_ws(int64_t M, int64_t K, int32_t k);
+int quads_mx_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                          uint8_t* codes, uint8_t* scales, int32_t* sel,
+                          uint8_t* r_codes, uint8_t* r_scales, double* score_out,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Grouped MX FP4 GEMM with the RAC compensation term (Eq. (21) into Eq. (6)
+ * on the MX FP4 mode): for packed row p of expert e and feature n
+ *   Y[p,n] = sum_{j<K} a[row(p), j] w_e[n, j] + sum_{i<k} r[row(p), i] w_e[n, sel[i]]
+ * with a, r, w the decoded MX FP4 values.  The main sum runs on the
+ * block-scaled FP4 MFMA, the compensation on bf16 MFMAs (MX FP4 values are
+ * exact in bf16) into the same fp32 accumulators.
+ *   a_codes, a_scale, r_codes, r_scale, sel, k   quads_mx_rac_quantize's
+ *              outputs (sel strictly ascending in [0, K)); k == 0 is
+ *              quads_moe_mx_gemm with QUADS_MX_FP4
+ *   the other arguments as in quads_moe_mx_gemm (K % 128 == 0)
+ *   ws         quads_moe_mx_rac_gemm_ws bytes (W[:, S] as bf16, E * N * k * 2)
+ */
+size_t quads_moe_mx_rac_gemm_ws(int32_t E, int64_t N, int32_t k);
+int quads_moe_mx_rac_gemm(const uint8_t* a_codes, const uint8_t* a_scale,
+                          const int32_t* row_token, int64_t rows, int64_t K,
+                          const uint8_t* r_codes, const uint8_t* r_scale, const int32_t* sel,
+                          int32_t k, const uint8_t* w_codes, const uint8_t* w_scale,
+                          const int32_t* offsets, int32_t E, int64_t N, int epilogue,
+                          int out_dtype, void* out, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -68,6 +68,13 @@ _SIGNATURES = {
                                                     _P, _SZ, _P]),
     "quads_moe_combine": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _I64, _I32, _I64, _P, _P]),
     "quads_mx_quantize": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_int, _P, _P, _P]),
+    "quads_mx_rac_quantize_ws": (_SZ, [_I64, _I64, _I32]),
+    "quads_mx_rac_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
+                                             _SZ, _P]),
+    "quads_moe_mx_rac_gemm_ws": (_SZ, [_I32, _I64, _I32]),
+    "quads_moe_mx_rac_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I32, _P, _P,
+                                             _P, _I32, _I64, ctypes.c_int, ctypes.c_int, _P, _P,
+                                             _SZ, _P]),
     "quads_moe_mx_gemm": (ctypes.c_int, [_P, _P, _P, _I64, _I64, _P, _P, _P, _I32, _I64,
                                          ctypes.c_int, ctypes.c_int, ctypes.c_int, _P, _P]),
 }
@@ -388,4 +395,52 @@ def quads_moe_mx_gemm(a, w, n, rows=None, offsets=None, row_token=None, fmt=MX_F
     _check("quads_moe_mx_gemm", lib().quads_moe_mx_gemm(
         _ptr(a_codes), _ptr(a_scale), _ptr(row_token), rows, kd, _ptr(w_codes), _ptr(w_scale),
         _ptr(offsets), e, n, fmt, epilogue, out_dtype, _ptr(out), _stream(dev)))
+    return out
+
+
+def quads_mx_rac_quantize(x, k, want_score=False):
+    """RAC on the MX FP4 mode of bf16 x [M, K] with k channels -> dict of
+    device tensors (codes, scales, sel, r_codes, r_scales[, score])."""
+    x = _bits16(x)
+    m, kd = x.shape
+    dev = x.device
+    out = dict(
+        codes=torch.empty((m, kd // 2), dtype=torch.uint8, device=dev),
+        scales=torch.empty((m, kd // 32), dtype=torch.uint8, device=dev),
+        sel=torch.empty(max(k, 4), dtype=torch.int32, device=dev)[:k],
+        r_codes=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+        r_scales=torch.empty((m, k // 32), dtype=torch.uint8, device=dev),
+    )
+    if want_score:
+        out["score"] = torch.empty(kd, dtype=torch.float64, device=dev)
+    ws, nws = _ws(lib().quads_mx_rac_quantize_ws(m, kd, k), dev)
+    _check("quads_mx_rac_quantize", lib().quads_mx_rac_quantize(
+        _ptr(x), m, kd, k, _ptr(out["codes"]), _ptr(out["scales"]),
+        _ptr(out["sel"]) if k else None, _ptr(out["r_codes"]) if k and m else None,
+        _ptr(out["r_scales"]) if k and m else None, _ptr(out.get("score")), _ptr(ws), nws,
+        _stream(dev)))
+    return out
+
+
+def quads_moe_mx_rac_gemm(a, r, sel, w, n, rows=None, offsets=None, row_token=None,
+                          epilogue=EPI_NONE, out_dtype=OUT_F32):
+    """MX FP4 grouped GEMM with the RAC compensation.  a = (codes, scales),
+    r = (r_codes, r_scales) or None, w = (codes [E, N, K/2], scales [E, N, K/32])."""
+    a_codes, a_scale = a
+    w_codes, w_scale = w
+    e = w_codes.shape[0]
+    kd = a_codes.shape[1] * 2
+    if rows is None:
+        rows = row_token.shape[0] if row_token is not None else a_codes.shape[0]
+    k = 0 if r is None else int(sel.shape[0])
+    dev = a_codes.device
+    ncols = n // 2 if epilogue == EPI_SWIGLU else n
+    dt = torch.float32 if out_dtype == OUT_F32 else torch.int16
+    out = torch.empty((rows, ncols), dtype=dt, device=dev)
+    ws, nws = _ws(lib().quads_moe_mx_rac_gemm_ws(e, n, k), dev)
+    rc, rs = r if r is not None else (None, None)
+    _check("quads_moe_mx_rac_gemm", lib().quads_moe_mx_rac_gemm(
+        _ptr(a_codes), _ptr(a_scale), _ptr(row_token), rows, kd, _ptr(rc) if k else None,
+        _ptr(rs) if k else None, _ptr(sel) if k else None, k, _ptr(w_codes), _ptr(w_scale),
+        _ptr(offsets), e, n, epilogue, out_dtype, _ptr(out), _ptr(ws), nws, _stream(dev)))
     return out

@@ -163,7 +163,14 @@ struct MxArgs {
     const uint8_t* a; const uint8_t* as; const int32_t* row_token; int64_t rows; int K;
     const uint8_t* w; const uint8_t* ws; const int32_t* offsets; int E; int N;
     int epilogue; int out_bf16; void* out;
+    // compensation (RAC on the MX FP4 mode): the second pass of the residual
+    // on the selected channels (MX FP4 [Ta, k/2] codes, [Ta, k/32] scales),
+    // and W[:, S] of every weight row as exact bf16 values [E * N, k]
+    const uint8_t* r_codes; const uint8_t* r_scales; int k; const __bf16* w_sel;
 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 // Loads of stage s into LDS buffer `buf`: code tiles (kLoads 16-byte loads per
 // operand per thread) and scale rows (one 4-byte load per thread: waves 0-3
@@ -257,7 +264,87 @@ __device__ __forceinline__ void main_loop(const MxArgs& g, uint8_t* smem, const 
     }
 }
 
-template <int FMT, int kEpi>
+// 8 MX FP4 codes (one dword) of a block with scale byte sb as exact bf16
+// values: the unscaled E2M1 values times 2^(sb - 127), exact in fp32 (at
+// least 2^-128) and in bf16.
+__device__ __forceinline__ bf16x8 mx_fp4_bf16x8(uint32_t w, uint32_t sb) {
+    const float sc = ldexpf(1.0f, (int)sb - 127);
+    const f32x2 f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0);
+    const f32x2 f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1);
+    const f32x2 f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2);
+    const f32x2 f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3);
+    return (bf16x8){(__bf16)(f0[0] * sc), (__bf16)(f0[1] * sc), (__bf16)(f1[0] * sc),
+                    (__bf16)(f1[1] * sc), (__bf16)(f2[0] * sc), (__bf16)(f2[1] * sc),
+                    (__bf16)(f3[0] * sc), (__bf16)(f3[1] * sc)};
+}
+
+// W[:, S] of every weight row as exact bf16 values [E * N, k]: a thread
+// writes 8 consecutive selected channels of one row.
+__global__ __launch_bounds__(256) void k_mx_gather_wsel(const uint8_t* __restrict__ w,
+                                                        const uint8_t* __restrict__ ws,
+                                                        const int32_t* __restrict__ sel, int K,
+                                                        int k, int64_t nrows,
+                                                        __bf16* __restrict__ out) {
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int per_row = k / 8;
+    if (t >= nrows * per_row) return;
+    const int64_t row = t / per_row;
+    const int j0 = (int)(t - row * per_row) * 8;
+    const uint8_t* crow = w + row * (K / 2);
+    const uint8_t* srow = ws + row * (K / kMxBlock);
+    bf16x8 v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int c = sel[j0 + i];
+        c = c < 0 ? 0 : (c >= K ? K - 1 : c);                 // bounds only: sel < K
+        const uint32_t code = (crow[c >> 1] >> (4 * (c & 1))) & 15u;
+        v[i] = mx_fp4_bf16x8(code, srow[c / kMxBlock])[0];
+    }
+    *reinterpret_cast<bf16x8*>(out + row * k + j0) = v;
+}
+
+// The compensation R x W[:, S] of the wave's output blocks, in bf16 MFMAs
+// (32x32x16, the same accumulator layout as the block-scaled MFMA): lane
+// (i, h) holds channels 16 t + 8 h .. + 7 of row i of both operands.
+template <int kEpi>
+__device__ __forceinline__ void mx_compensation(const MxArgs& g, int e, int m0, int mend, int f0,
+                                                int wm, int wn, int mact, f32x16 acc[4][2]) {
+    constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    const int lane = threadIdx.x & 63, r = lane & 31, h = lane >> 5;
+    int64_t wrow[2];
+#pragma unroll
+    for (int nj = 0; nj < 2; ++nj) {
+        bool ok;
+        const int wr = v2::w_row_v2(wn * 64 + nj * 32 + r, f0, g.N, swiglu, &ok);
+        wrow[nj] = (int64_t)e * g.N + (ok ? wr : 0);
+    }
+    int64_t arow[4];
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+        const int p = m0 + wm * 128 + mi * 32 + r;
+        arow[mi] = p < mend ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
+    }
+    for (int t = 0; t < g.k / 16; ++t) {
+        const int ch = 16 * t + 8 * h;
+        bf16x8 b[2];
+#pragma unroll
+        for (int nj = 0; nj < 2; ++nj)
+            b[nj] = *reinterpret_cast<const bf16x8*>(g.w_sel + wrow[nj] * g.k + ch);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi) {
+            if (mi >= mact) break;
+            const uint32_t code =
+                *reinterpret_cast<const uint32_t*>(g.r_codes + arow[mi] * (g.k / 2) + ch / 2);
+            const bf16x8 a = mx_fp4_bf16x8(code, g.r_scales[arow[mi] * (g.k / kMxBlock) +
+                                                            ch / kMxBlock]);
+#pragma unroll
+            for (int nj = 0; nj < 2; ++nj)
+                acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[nj], a, acc[mi][nj], 0, 0, 0);
+        }
+    }
+}
+
+template <int FMT, int kEpi, bool kComp = false>
 __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxArgs g, int nt_n, int grp) {
     __shared__ __attribute__((aligned(16))) uint8_t smem[2 * Cfg<FMT>::kStage];
     const int hid = blockIdx.x;
@@ -310,6 +397,7 @@ __global__ __launch_bounds__(kThreads) void k_mx_gemm(MxArgs g, int nt_n, int gr
         case 1: main_loop<FMT, 1>(g, smem, a_row, w_row, sc_row, sc_is_a, wm, wn, acc); break;
         default: main_loop<FMT, 0>(g, smem, a_row, w_row, sc_row, sc_is_a, wm, wn, acc); break;
     }
+    if (kComp && g.k > 0 && mact > 0) mx_compensation<kEpi>(g, e, m0, mend, f0, wm, wn, mact, acc);
     GemmArgs ga{};
     ga.N = g.N;
     ga.out = g.out;
@@ -342,15 +430,15 @@ extern "C" int quads_mx_quantize(const uint16_t* x, int64_t M, int64_t K, int fm
     return QUADS_OK;
 }
 
-template <int FMT>
+template <int FMT, bool kComp = false>
 static void launch_mx_gemm(const mx::MxArgs& g, int epilogue, dim3 grid, int nt_n, int grp,
                            hipStream_t s) {
     if (epilogue == QUADS_EPI_SWIGLU)
-        hipLaunchKernelGGL((mx::k_mx_gemm<FMT, QUADS_EPI_SWIGLU>), grid, dim3(mx::kThreads), 0, s,
-                           g, nt_n, grp);
+        hipLaunchKernelGGL((mx::k_mx_gemm<FMT, QUADS_EPI_SWIGLU, kComp>), grid, dim3(mx::kThreads),
+                           0, s, g, nt_n, grp);
     else
-        hipLaunchKernelGGL((mx::k_mx_gemm<FMT, QUADS_EPI_NONE>), grid, dim3(mx::kThreads), 0, s, g,
-                           nt_n, grp);
+        hipLaunchKernelGGL((mx::k_mx_gemm<FMT, QUADS_EPI_NONE, kComp>), grid, dim3(mx::kThreads), 0,
+                           s, g, nt_n, grp);
 }
 
 extern "C" int quads_moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scale,
@@ -385,6 +473,59 @@ extern "C" int quads_moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scale,
         launch_mx_gemm<QUADS_MX_FP8>(g, epilogue, grid, (int)nt_n, (int)grp, s);
     else
         launch_mx_gemm<QUADS_MX_FP4>(g, epilogue, grid, (int)nt_n, (int)grp, s);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+// RAC on the MX FP4 mode: the MX FP4 grouped GEMM plus the compensation term
+// over the selected channels.  Workspace: W[:, S] as bf16, E * N * k * 2
+// bytes.
+extern "C" size_t quads_moe_mx_rac_gemm_ws(int32_t E, int64_t N, int32_t k) {
+    if (E < 1 || N < 1 || k < 0) return 0;
+    return align_up((size_t)E * (size_t)N * (size_t)k * 2, 256);
+}
+
+extern "C" int quads_moe_mx_rac_gemm(const uint8_t* a_codes, const uint8_t* a_scale,
+                                     const int32_t* row_token, int64_t rows, int64_t K,
+                                     const uint8_t* r_codes, const uint8_t* r_scale,
+                                     const int32_t* sel, int32_t k, const uint8_t* w_codes,
+                                     const uint8_t* w_scale, const int32_t* offsets, int32_t E,
+                                     int64_t N, int epilogue, int out_dtype, void* out, void* ws,
+                                     size_t ws_bytes, void* stream) {
+    if (k < 0 || k % 32 || k > K) return QUADS_ESHAPE;
+    if (k > 0 && (!ok_ptr(r_codes) || !ok_ptr(r_scale) || !ok_ptr(sel))) return QUADS_EINVAL;
+    if (k == 0)
+        return quads_moe_mx_gemm(a_codes, a_scale, row_token, rows, K, w_codes, w_scale, offsets,
+                                 E, N, QUADS_MX_FP4, epilogue, out_dtype, out, stream);
+    if (epilogue != QUADS_EPI_NONE && epilogue != QUADS_EPI_SWIGLU) return QUADS_EINVAL;
+    if (out_dtype != QUADS_OUT_F32 && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (epilogue == QUADS_EPI_SWIGLU && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (rows < 0 || rows >= ((int64_t)1 << 31) || K <= 0 || K % mx::BK || K >= ((int64_t)1 << 30))
+        return QUADS_ESHAPE;
+    if (E < 1 || E > 4096 || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
+    if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
+    if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
+    if (!ok_ptr(a_codes) || !ok_ptr(a_scale) || !ok_ptr(w_codes) || !ok_ptr(w_scale) ||
+        !ok_ptr(out))
+        return QUADS_EINVAL;
+    if (ws_bytes < quads_moe_mx_rac_gemm_ws(E, N, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    if (rows == 0) return QUADS_OK;
+    hipStream_t s = (hipStream_t)stream;
+    const int64_t nrows = (int64_t)E * N, threads = nrows * (k / 8);
+    hipLaunchKernelGGL(mx::k_mx_gather_wsel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                       w_codes, w_scale, sel, (int)K, (int)k, nrows, static_cast<__bf16*>(ws));
+    QUADS_CHECK_LAUNCH();
+    mx::MxArgs g{a_codes, a_scale, row_token, rows, (int)K, w_codes, w_scale, offsets, (int)E,
+                 (int)N, epilogue, out_dtype == QUADS_OUT_BF16, out, r_codes, r_scale, (int)k,
+                 static_cast<const __bf16*>(ws)};
+    const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + mx::BN / 2 - 1) / (mx::BN / 2)
+                                                      : (N + mx::BN - 1) / mx::BN;
+    const int64_t nt_m = (rows + mx::BM - 1) / mx::BM + (offsets ? E : 0);
+    const int64_t grp = 2 * nt_n;
+    const int64_t span = grp * v2::kXcds;
+    const dim3 grid((unsigned)((nt_m * nt_n + span - 1) / span * span));
+    launch_mx_gemm<QUADS_MX_FP4, true>(g, epilogue, grid, (int)nt_n, (int)grp, s);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

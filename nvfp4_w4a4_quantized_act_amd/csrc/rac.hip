@@ -808,6 +808,109 @@ __global__ void k_fill_f64(double* p, int n, double v) {
     if (i < n) p[i] = v;
 }
 
+// ------------------------------------------------------- MX FP4 mode --
+// RAC with the MX FP4 quantizer (section 3.3 on the MX FP4 format the "FP4"
+// paragraph of section 2.2 sets beside NVFP4): E2M1 elements with one
+// power-of-two scale per 32 consecutive channels, no tensor scale.  The main
+// codes come from the MX quantizer; the residual, scores and selection are
+// those of the NVFP4 path (the same fixed-order fp64 sums, the same select
+// kernel); the second pass MX-quantizes r[:, S] in 32-element blocks along
+// the compacted index.
+
+// Value of main MX FP4 element (code c, scale byte sb): v * 2^(sb - 127),
+// exact in fp32 (at least 2^-128, at most two significant bits).
+__device__ __forceinline__ float mx_fp4_value(uint32_t c, uint32_t sb) {
+    const float v = ldexpf(e2m1_value(c & 7u), (int)sb - 127);
+    return c & 8u ? -v : v;
+}
+
+// r = x - DQ(Q(x)) of element (row, col): exact in fp32 (x has 8
+// significant bits, the value at most two, and |r| <= |x|).
+__device__ __forceinline__ float mx_residual(const uint16_t* x, const uint8_t* codes,
+                                             const uint8_t* scales, int64_t row, int K, int col) {
+    const uint32_t byte = codes[row * (K / 2) + col / 2];
+    const uint32_t sb = scales[row * (K / 32) + col / 32];
+    const float xv = __uint_as_float((uint32_t)x[row * K + col] << 16);
+    return xv - mx_fp4_value((byte >> (4 * (col & 1))) & 15u, sb);
+}
+
+// Shared exponent of an MX FP4 block from its largest |r| (fp32 bits):
+// floor(log2) - 2, clamped to [-127, 127]; -127 for an all-zero block.
+__device__ __forceinline__ int mx_fp4_exponent(uint32_t bits) {
+    if (bits == 0u) return -127;
+    const int ef = (int)(bits >> 23) & 0xFF;
+    const int fl = ef > 0 ? ef - 127 : -149 + (31 - __builtin_clz(bits & 0x7FFFFFu));
+    const int e = fl - 2;
+    return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
+// Level-0 score partials: thread = channel, rows of one 64-row chunk in
+// order from +0 (the layout of k_rac_pass1's partials, and their max |r|).
+__global__ __launch_bounds__(256) void k_mx_rac_pass1(const uint16_t* __restrict__ x, int64_t M,
+                                                      int K, const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      double* __restrict__ pa,
+                                                      uint32_t* __restrict__ ca) {
+    const int c = blockIdx.x * 256 + threadIdx.x;
+    if (c >= K) return;
+    const int64_t r0 = (int64_t)blockIdx.y * kTileRows;
+    const int64_t r1 = r0 + kTileRows < M ? r0 + kTileRows : M;
+    double acc = 0.0;
+    uint32_t m = 0;
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r) {
+        const float rv = mx_residual(x, codes, scales, r, K, c);
+        acc = acc + (double)rv * (double)rv;                  // the square is exact in fp64
+        const uint32_t u = __float_as_uint(rv) & 0x7FFFFFFFu;
+        m = u > m ? u : m;
+    }
+    pa[(int64_t)blockIdx.y * K + c] = acc;
+    ca[(int64_t)blockIdx.y * K + c] = m;
+}
+
+// Second pass: thread = 8 consecutive selected channels of one row; the four
+// threads of a 32-block (neighbouring lanes: k % 32 == 0) share its maximum.
+// Elements are r * 2^-E (exact), clamped to +-6 and rounded to the nearest
+// E2M1 value, ties to even, by the hardware conversion.
+__global__ __launch_bounds__(256) void k_mx_rac_pass2(const uint16_t* __restrict__ x, int64_t M,
+                                                      int K, const uint8_t* __restrict__ codes,
+                                                      const uint8_t* __restrict__ scales,
+                                                      const int32_t* __restrict__ sel, int k,
+                                                      uint8_t* __restrict__ r_codes,
+                                                      uint8_t* __restrict__ r_scales) {
+    const int per_row = k / 8;
+    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const bool live = t < M * per_row;                        // whole 4-lane groups
+    const int64_t row = live ? t / per_row : 0;
+    const int j0 = live ? (int)(t - row * per_row) * 8 : 0;
+    float rv[8];
+    uint32_t am = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        int c = sel[j0 + i];
+        c = c < 0 ? 0 : (c >= K ? K - 1 : c);                 // bounds only: sel < K
+        rv[i] = live ? mx_residual(x, codes, scales, row, K, c) : 0.0f;
+        const uint32_t u = __float_as_uint(rv[i]) & 0x7FFFFFFFu;
+        am = u > am ? u : am;
+    }
+    uint32_t o = __shfl_xor(am, 1, 64);
+    am = o > am ? o : am;
+    o = __shfl_xor(am, 2, 64);
+    am = o > am ? o : am;
+    const int e = mx_fp4_exponent(am);
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = fminf(fmaxf(ldexpf(rv[i], -e), -6.0f), 6.0f);
+    uint32_t w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[0], v[1], 1.0f, 0);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[2], v[3], 1.0f, 1);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[4], v[5], 1.0f, 2);
+    w = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(w, v[6], v[7], 1.0f, 3);
+    if (live) {
+        *reinterpret_cast<uint32_t*>(r_codes + row * (k / 2) + j0 / 2) = w;
+        if (j0 % 32 == 0) r_scales[row * (k / 32) + j0 / 32] = (uint8_t)(e + 127);
+    }
+}
+
 struct RacWs {
     uint32_t* partial;
     uint32_t* r_table;     // code table of the gathered residual
@@ -1082,3 +1185,63 @@ extern "C" int quads_rac_quantize_experts(const uint16_t* x, int64_t M, int64_t 
     return QUADS_OK;
 }
 
+
+// RAC on the MX FP4 mode.  Workspace: that of quads_rac_quantize (the score
+// partials and their tree).
+extern "C" size_t quads_mx_rac_quantize_ws(int64_t M, int64_t K, int32_t k) {
+    return quads_rac_quantize_ws(M, K, k);
+}
+
+extern "C" int quads_mx_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                     uint8_t* codes, uint8_t* scales, int32_t* sel,
+                                     uint8_t* r_codes, uint8_t* r_scales, double* score_out,
+                                     void* ws, size_t ws_bytes, void* stream) {
+    if (M < 0 || K <= 0 || K % 32 || K > kRacMaxK) return QUADS_ESHAPE;
+    if (k < 0 || k % 32 || k > K) return QUADS_ESHAPE;
+    if (!ok_opt_ptr(score_out)) return QUADS_EINVAL;
+    if (M > 0 && (!ok_ptr(x) || !ok_ptr(codes) || !ok_ptr(scales))) return QUADS_EINVAL;
+    if (k > 0 && !ok_ptr(sel)) return QUADS_EINVAL;
+    if (k > 0 && M > 0 && (!ok_ptr(r_codes) || !ok_ptr(r_scales))) return QUADS_EINVAL;
+    if (ws_bytes < quads_mx_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        if (k > 0) hipLaunchKernelGGL(k_iota_i32, dim3((k + 255) / 256), dim3(256), 0, s, sel, k);
+        if (score_out)
+            hipLaunchKernelGGL(k_fill_f64, dim3((unsigned)((K + 255) / 256)), dim3(256), 0, s,
+                               score_out, (int)K, 0.0);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    int st = quads_mx_quantize(x, M, K, QUADS_MX_FP4, codes, scales, stream);
+    if (st != QUADS_OK) return st;
+    if (k == 0 && score_out == nullptr) return QUADS_OK;
+    RacWs w = rac_ws_layout((char*)ws, M, K);
+    const int64_t c0 = (M + kTileRows - 1) / kTileRows;
+    hipLaunchKernelGGL(k_mx_rac_pass1, dim3((unsigned)((K + 255) / 256), (unsigned)c0), dim3(256), 0,
+                       s, x, M, (int)K, codes, scales, w.pa, w.ca);
+    QUADS_CHECK_LAUNCH();
+    // the fixed-order tree and the selection of the NVFP4 path (the residual
+    // tensor scale and code table it also writes go to workspace, unused)
+    double* pin = w.pa; uint32_t* cin = w.ca;
+    double* pout = w.pb; uint32_t* cout = w.cb;
+    int64_t n = c0;
+    while (n > kSelectFold) {
+        const int64_t g = (n + kScoreFanin - 1) / kScoreFanin;
+        hipLaunchKernelGGL(k_tree_level, dim3((unsigned)((K + 255) / 256), (unsigned)g), dim3(256),
+                           0, s, pin, cin, n, (int)K, pout, cout);
+        QUADS_CHECK_LAUNCH();
+        n = g;
+        double* tp = pin; pin = pout; pout = tp;
+        uint32_t* tc = cin; cin = cout; cout = tc;
+    }
+    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)n, (int)K, (int)k,
+                       sel, reinterpret_cast<float*>(w.partial), score_out, w.r_table);
+    QUADS_CHECK_LAUNCH();
+    if (k > 0) {
+        const int64_t threads = M * (int64_t)(k / 8);
+        hipLaunchKernelGGL(k_mx_rac_pass2, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                           x, M, (int)K, codes, scales, sel, (int)k, r_codes, r_scales);
+        QUADS_CHECK_LAUNCH();
+    }
+    return QUADS_OK;
+}

@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 21
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 25
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -101,6 +101,29 @@ def test_rac_noalloc_validation():
     for mm, kk, k in ((32, 256, 16), (4096, 4096, 128), (4096, 2048, 64), (32768, 768, 64),
                       (16384, 4096, 256), (131072, 1536, 64)):
         assert lib.quads_rac_quantize_ws(mm, kk, k) <= cap, (mm, kk)
+
+
+def test_mx_rac_validation():
+    lib = Q.lib()
+    f = lib.quads_mx_rac_quantize
+    ws = lib.quads_mx_rac_quantize_ws(64, 256, 32)
+    call = lambda m, kd, k, wsz: f(FAKE, m, kd, k, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, wsz,
+                                   None)
+    assert call(64, 256, 16, ws) == -2           # k % 32
+    assert call(64, 240, 32, ws) == -2           # K % 32
+    assert call(64, 256, 288, ws) == -2          # k > K
+    assert call(64, 256, 32, ws - 1) == -3
+    assert f(FAKE, 64, 256, 32, FAKE, FAKE, None, FAKE, FAKE, None, FAKE, ws, None) == -1
+    g = lib.quads_moe_mx_rac_gemm
+    gws = lib.quads_moe_mx_rac_gemm_ws(2, 64, 32)
+    assert gws == 2 * 64 * 32 * 2
+    args = lambda k, kd, wsz: g(FAKE, FAKE, None, 32, kd, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE,
+                                2, 64, 0, 0, FAKE, FAKE, wsz, None)
+    assert args(48, 256, gws) == -2              # k % 32
+    assert args(32, 192, gws) == -2              # K % 128
+    assert args(32, 256, gws - 1) == -3
+    assert g(FAKE, FAKE, None, 32, 256, None, FAKE, FAKE, 32, FAKE, FAKE, FAKE, 2, 64, 0, 0, FAKE,
+             FAKE, gws, None) == -1              # r_codes missing with k > 0
 
 
 def test_weight_qdq_validation():

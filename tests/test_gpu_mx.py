@@ -126,3 +126,84 @@ def test_mx_gemm_grouped(Q, name, fmt):
     got = F.bf16_to_f64(h.cpu().numpy().view(np.uint16))
     ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
     assert np.all(np.abs(got - ref) <= ulp * 1.0001)
+
+
+# ---- RAC on the MX FP4 mode ------------------------------------------------
+
+@pytest.mark.parametrize("m,kd,k", [(64, 256, 32), (300, 512, 128), (37, 64, 64),
+                                    (4096, 2048, 64), (3000, 768, 64)])
+def test_mx_rac_quantize_bit_exact(Q, m, kd, k):
+    """Codes, scales, scores, S and the second pass bit-exact against the
+    oracle (outlier channels, ragged row counts, k = K, the edge rows)."""
+    rng = np.random.default_rng(m + kd + k)
+    x = rng.standard_t(3, size=(m, kd))
+    x[:, rng.choice(kd, max(1, kd // 64), replace=False)] *= 20.0
+    bits = np.concatenate([synth.f32_to_bf16_bits(x.astype(np.float32)), _special_rows(kd)])
+    print(f"mx rac m={bits.shape[0]} K={kd} k={k}", flush=True)
+    g = Q.quads_mx_rac_quantize(_t(bits), k, want_score=True)
+    torch.cuda.synchronize()
+    e = M.rac_quantize(F.bf16_to_f64(bits), k, "fp4")
+    assert np.array_equal(g["scales"].cpu().numpy(), e["scales"])
+    assert np.array_equal(g["codes"].cpu().numpy(), e["codes"])
+    gs = g["score"].cpu().numpy()
+    assert np.array_equal(gs.view(np.uint64), e["score"].view(np.uint64))
+    assert np.array_equal(g["sel"].cpu().numpy(), e["sel"])
+    assert np.array_equal(g["r_scales"].cpu().numpy(), e["r_scales"])
+    assert np.array_equal(g["r_codes"].cpu().numpy(), e["r_codes"])
+
+
+def _mx_rac_operands(Q, bits, k):
+    g = Q.quads_mx_rac_quantize(_t(bits), k)
+    torch.cuda.synchronize()
+    e = M.rac_quantize(F.bf16_to_f64(bits), k, "fp4")
+    assert np.array_equal(g["sel"].cpu().numpy(), e["sel"])
+    return g, e
+
+
+@pytest.mark.parametrize("m,kd,n,k", [(300, 512, 256, 128), (64, 1024, 96, 64),
+                                      (129, 256, 320, 256)])
+def test_mx_rac_gemm_dense(Q, m, kd, n, k):
+    rng = np.random.default_rng(7 * m + kd + n + k)
+    x = rng.standard_t(4, size=(m, kd))
+    x[:, :: max(1, kd // 7)] *= 16.0
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    w, wq = _weights(rng, 1, n, kd, "fp4")
+    g, e = _mx_rac_operands(Q, bits, k)
+    y = Q.quads_moe_mx_rac_gemm((g["codes"], g["scales"]), (g["r_codes"], g["r_scales"]), g["sel"],
+                                (_t(wq[0]), _t(wq[1])), n)
+    torch.cuda.synchronize()
+    exp, bound = M.grouped_gemm_rac((e["codes"], e["scales"]), (e["r_codes"], e["r_scales"]),
+                                    e["sel"], wq, np.array([0, m]), None, "fp4")
+    _check(y.cpu().numpy(), exp, bound, kd + k, "fp4")
+    # and the compensation changes the result (it is not silently skipped)
+    y0, _ = M.grouped_gemm((e["codes"], e["scales"]), wq, np.array([0, m]), None, "fp4")
+    assert np.abs(exp - y0).max() > 0
+
+
+def test_mx_rac_gemm_grouped_swiglu(Q):
+    rng = np.random.default_rng(17)
+    t, e_, topk, kd, n, k = 300, 6, 2, 512, 192, 64
+    x = rng.standard_normal((t, kd))
+    x[:, 3] *= 20.0
+    bits = synth.f32_to_bf16_bits(x.astype(np.float32))
+    ids = np.stack([rng.choice(e_, size=topk, replace=False) for _ in range(t)]).astype(np.int32)
+    ids[ids == 3] = 2                           # expert 3 gets no rows
+    ids[:, 1] = np.where(ids[:, 0] == ids[:, 1], (ids[:, 0] + 1) % e_, ids[:, 1])
+    ids[ids == 3] = 4
+    off, rt, _ = OM.pack_routes(ids, e_)
+    w, wq = _weights(rng, e_, n, kd, "fp4")
+    g, e = _mx_rac_operands(Q, bits, k)
+    wt = (_t(wq[0]), _t(wq[1]))
+    a, r = (g["codes"], g["scales"]), (g["r_codes"], g["r_scales"])
+    y = Q.quads_moe_mx_rac_gemm(a, r, g["sel"], wt, n, rows=int(off[-1]), offsets=_t(off),
+                                row_token=_t(rt))
+    h = Q.quads_moe_mx_rac_gemm(a, r, g["sel"], wt, n, rows=int(off[-1]), offsets=_t(off),
+                                row_token=_t(rt), epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+    torch.cuda.synchronize()
+    exp, bound = M.grouped_gemm_rac((e["codes"], e["scales"]), (e["r_codes"], e["r_scales"]),
+                                    e["sel"], wq, off, rt, "fp4")
+    _check(y.cpu().numpy(), exp, bound, kd + k, "fp4")
+    ref = F.bf16_to_f64(OM.swiglu(y.cpu().numpy().astype(np.float64)))
+    got = F.bf16_to_f64(h.cpu().numpy().view(np.uint16))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(ref), 2.0 ** -126))) - 7)
+    assert np.all(np.abs(got - ref) <= ulp * 1.0001)
