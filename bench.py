@@ -964,13 +964,14 @@ def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
                     "layer_ms has none; the GEMM rates use alone_us (20 back-to-back calls)"}
 
 
-def mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx, w4a4_ms, w4a4_flops, reps=20):
+def mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx, w4a4_ms, w4a4_flops, reps=20, kr=64):
     """The gate/up GEMM of the same layer (same tokens, routing and SwiGLU bf16
     output) as an MX block-scaled GEMM (quads_moe_mx_gemm): FP8 E4M3 elements,
     the FP8 W8A8 baseline of the paper's speed claim, and FP4 E2M1 elements
-    (power-of-two scales per 32: not NVFP4).  Activations are MX-quantized
-    from the same bf16 x; timed with events over `reps` launches.  Reported
-    beside the W4A4+RAC gate/up GEMM of the timed steps."""
+    (power-of-two scales per 32: not NVFP4), and MX FP4 with RAC (k = kr
+    channels, the compensation fused into the same GEMM).  Activations are
+    MX-quantized from the same bf16 x; timed with events over `reps`
+    launches.  Reported beside the W4A4+RAC gate/up GEMM of the timed steps."""
     off, rt, _ = Q.quads_moe_pack(ids, E)
     out = {"workload": "gate/up GEMM, 32768 packed rows x 1536 x 2048, SwiGLU bf16 out",
            "w4a4_rac": {"us": w4a4_ms * 1e3,
@@ -994,6 +995,42 @@ def mx_comparator(torch, Q, x, ids, E, I, rows, w13_mx, w4a4_ms, w4a4_flops, rep
         flops = 2.0 * rows * (2 * I) * x.shape[1]
         out[name] = {"us": us, "TFLOP/s": flops / (us * 1e-6) / 1e12,
                      "w4a4_rac_time_ratio": w4a4_ms * 1e3 / us}
+    # MX FP4 with RAC (k channels): the MX RAC quantizer and the compensated
+    # block-scaled GEMM, beside NVFP4 W4A4+RAC
+    if "mxfp4" in w13_mx:
+        wc, wsc, _ = w13_mx["mxfp4"]
+        keep = {}
+
+        def rac():
+            keep["a"] = Q.quads_mx_rac_quantize(x, kr)
+        rac()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            rac()
+        e1.record()
+        torch.cuda.synchronize()
+        rac_us = e0.elapsed_time(e1) * 1e3 / reps
+        a = keep["a"]
+
+        def run_rac():
+            return Q.quads_moe_mx_rac_gemm((a["codes"], a["scales"]), (a["r_codes"], a["r_scales"]),
+                                           a["sel"], (wc, wsc), 2 * I, rows=rows, offsets=off,
+                                           row_token=rt, epilogue=Q.EPI_SWIGLU,
+                                           out_dtype=Q.OUT_BF16)
+        run_rac()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            run_rac()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        flops = 2.0 * rows * (2 * I) * (x.shape[1] + kr)
+        out["mxfp4_rac"] = {"k": kr, "rac_quantize_us": rac_us, "us": us,
+                            "TFLOP/s": flops / (us * 1e-6) / 1e12,
+                            "w4a4_rac_time_ratio": w4a4_ms * 1e3 / us}
     return out
 
 

@@ -24,7 +24,8 @@ Beside them, the approximate MX modes of gfx950's block-scaled MFMA (one
 power-of-two E8M0 scale per 32 elements instead of an E4M3 scale per 16; FP4
 E2M1 and FP8 E4M3 elements, both operands quantized by quads_mx_quantize, the
 product by quads_moe_mx_gemm): their distance to Y_16, the same product
-format-for-format, with no trainer-side reference of their own.
+format-for-format, with no trainer-side reference of their own; and MX FP4
+with RAC (quads_mx_rac_quantize and quads_moe_mx_rac_gemm) for each k > 0.
 
 Workloads: dense = X [4096, 4096] Student-t(3) with 41 outlier channels x20,
 W [4096, 4096] N(0, 0.02); moe = the gate/up GEMM of the MoE layer, X [4096,
@@ -70,9 +71,11 @@ def _mx_errors(y, y_16):
                 max_qat=None, max_bf16=float(np.abs(y - y_16).max() / np.abs(y_16).max()))
 
 
-def _mx_rows(Q, torch, x_t, w_t, n, rows, y_16, meta, offsets=None, row_token=None):
+def _mx_rows(Q, torch, x_t, w_t, n, rows, y_16, meta, offsets=None, row_token=None,
+             fractions=FRACTIONS):
     """Rows of the MX modes: x and w quantized to MX, the block-scaled GEMM
-    (fp32 out), its distance to the bf16 product."""
+    (fp32 out), its distance to the bf16 product; then MX FP4 with RAC
+    (quads_mx_rac_quantize, quads_moe_mx_rac_gemm) for every k > 0."""
     out = []
     e, _, kdim = w_t.shape
     for name, fmt in (("mxfp4", Q.MX_FP4), ("mxfp8", Q.MX_FP8)):
@@ -83,6 +86,19 @@ def _mx_rows(Q, torch, x_t, w_t, n, rows, y_16, meta, offsets=None, row_token=No
                                 out_dtype=Q.OUT_F32)
         torch.cuda.synchronize()
         out.append(dict(meta, format=name, frac=0.0, k=0,
+                        **_mx_errors(y.cpu().numpy().astype(np.float64), y_16)))
+    wc, wsc = Q.quads_mx_quantize(w_t.reshape(e * n, kdim), Q.MX_FP4)
+    wq = (wc.view(e, n, -1), wsc.view(e, n, -1))
+    for f in fractions:
+        k = channels_for(f, kdim)
+        if k == 0:
+            continue
+        a = Q.quads_mx_rac_quantize(x_t, k)
+        y = Q.quads_moe_mx_rac_gemm((a["codes"], a["scales"]), (a["r_codes"], a["r_scales"]),
+                                    a["sel"], wq, n, rows=rows, offsets=offsets,
+                                    row_token=row_token, out_dtype=Q.OUT_F32)
+        torch.cuda.synchronize()
+        out.append(dict(meta, format="mxfp4+rac", frac=f, k=k,
                         **_mx_errors(y.cpu().numpy().astype(np.float64), y_16)))
     return out
 
@@ -116,7 +132,8 @@ def sweep_dense(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
         y = _gpu_gemm(Q, torch, x_t, k, (nib, scale, ts), n, m)
         out.append(dict(workload="dense", M=m, K=kdim, N=n, format="nvfp4", frac=f, k=k,
                         **_errors(y, y_qat, y_16)))
-    out += _mx_rows(Q, torch, x_t, w_t, n, m, y_16, dict(workload="dense", M=m, K=kdim, N=n))
+    out += _mx_rows(Q, torch, x_t, w_t, n, m, y_16, dict(workload="dense", M=m, K=kdim, N=n),
+                    fractions=fractions)
     return out
 
 
@@ -154,7 +171,7 @@ def sweep_moe(Q, torch, synth, dev, fractions=FRACTIONS, **overrides):
                         frac=f, k=k, **_errors(y, y_qat, y_16)))
     out += _mx_rows(Q, torch, x_t, w_t, n, rows, y_16,
                     dict(workload="moe_gate_up", T=t, E=e, K=kdim, N=n, rows=rows),
-                    offsets=off_t, row_token=rt_t)
+                    offsets=off_t, row_token=rt_t, fractions=fractions)
     return out
 
 

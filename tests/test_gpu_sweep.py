@@ -2,7 +2,8 @@
 at reduced sizes: the error figures the sweep reports from the library's RAC
 and GEMM equal the oracle's figures for the same inputs, for every k, and
 fall with k; the figures of the approximate MX modes (FP4 and FP8 elements,
-E8M0 per 32) equal the oracle's MX figures."""
+E8M0 per 32, and MX FP4 with RAC for every k) equal the oracle's MX figures,
+and MX FP4's error falls with k too."""
 
 import numpy as np
 import pytest
@@ -74,16 +75,32 @@ def _oracle_mx(x_bits, w_bits, offsets, row_token):
                                row_token, fmt)
         out["mx" + fmt] = (np.linalg.norm(y - y_16) / np.linalg.norm(y_16),
                            np.abs(y - y_16).max() / np.abs(y_16).max())
+    wc, wsc = OX.quantize(wf.reshape(e * n, kdim), "fp4")
+    wq = (wc.reshape(e, n, -1), wsc.reshape(e, n, -1))
+    for f in S.FRACTIONS:
+        k = S.channels_for(f, kdim)
+        if k == 0:
+            continue
+        o = OX.rac_quantize(x, k, "fp4")
+        y, _ = OX.grouped_gemm_rac((o["codes"], o["scales"]), (o["r_codes"], o["r_scales"]),
+                                   o["sel"], wq, offsets, row_token, "fp4")
+        out[("mxfp4+rac", k)] = (np.linalg.norm(y - y_16) / np.linalg.norm(y_16),
+                                 np.abs(y - y_16).max() / np.abs(y_16).max())
     return out
 
 
 def _compare_mx(got, exp):
-    rows = [g for g in got if g["format"] != "nvfp4"]
+    rows = [g for g in got if g["format"] in ("mxfp4", "mxfp8")]
     assert [g["format"] for g in rows] == ["mxfp4", "mxfp8"]
-    for g in rows:
-        rel, mx = exp[g["format"]]
+    rac = [g for g in got if g["format"] == "mxfp4+rac"]
+    assert len(rac) == len(S.FRACTIONS) - 1
+    for g in rows + rac:
+        rel, mx = exp[g["format"] if g["format"] != "mxfp4+rac" else (g["format"], g["k"])]
         assert abs(g["rel_bf16"] - rel) <= 1e-3 * rel + 1e-6, (g, rel)
         assert abs(g["max_bf16"] - mx) <= 1e-3 * mx + 1e-6, (g, mx)
+    # RAC lowers the MX FP4 error as k grows
+    errs = [rows[0]["rel_bf16"]] + [g["rel_bf16"] for g in rac]
+    assert all(a > b for a, b in zip(errs, errs[1:])), errs
     # the exact NVFP4 path without RAC, against the same bf16 product
     nv = [g for g in got if g["format"] == "nvfp4" and g["k"] == 0][0]
     print("rel. error vs bf16: nvfp4 %.5f, mxfp4 %.5f, mxfp8 %.5f"
