@@ -364,4 +364,25 @@ inline int amax_groups(int64_t n) {
     return (int)g;
 }
 
+// Direct HBM -> LDS loads (lane i's bytes land at LDS address m0 + i * size).
+// Written as inline assembly so that the compiler does not see an LDS write:
+// its conservative wait (every LDS read after such a load waits for it) would
+// make each stage wait for the next stage's prefetch.  A kernel that uses them
+// waits for its own loads explicitly (s_waitcnt vmcnt) before reading the
+// bytes they bring.
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+__device__ __forceinline__ uint32_t lds_addr(void* l) {
+    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
+}
+// `l` is an LDS byte address (wave-uniform)
+__device__ __forceinline__ void g2l16(const void* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void g2l4(const void* g, uint32_t l) {
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(l), "v"(g)
+                 : "memory", "m0");
+}
+
 }  // namespace quads

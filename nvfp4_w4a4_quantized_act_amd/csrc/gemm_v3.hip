@@ -72,6 +72,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kFlush = 8;            // chunks per accumulation segment (1024 channels)
 constexpr int kCapLd = kCapMaxV3 + 8;  // halfs per captured row (16-byte pad)
 constexpr int kMaxChunksV3 = 64;       // K <= 8192
+constexpr int kWin = 8;                // chunks per staged scale window (64 bytes per row)
 
 // Activation codes of one chunk for the lane's two row fragments: channels
 // 32 q .. 32 q + 31 (16 bytes) and the scale bytes of blocks 2 q, 2 q + 1.
@@ -126,16 +127,22 @@ struct Ctx {
     const uint8_t* w_nib;
     const uint8_t* w_sc;
     int nk;                   // chunks
+    // staged scales: the scale bytes of the lane's row of each fragment and of
+    // its weight row (the main loop's scale windows)
+    const uint8_t* a_srow[2];
+    const uint8_t* w_srow;
 };
 
-template <int MACT>
+// Codes of chunk c for the lane's fragments; their scale bytes too unless the
+// main loop reads them from its staged window (kScales false).
+template <int MACT, bool kScales>
 __device__ __forceinline__ void load_a(const Ctx& x, int c, ARaw& r) {
     const int cc = c < x.nk ? c : x.nk - 1;            // past the end: a redundant load
 #pragma unroll
     for (int f = 0; f < 2; ++f) {
         if (f < MACT) {
             r.c[f] = *reinterpret_cast<const uint4*>(x.a_nib + x.a_off[f] + 64 * cc);
-            r.s[f] = *reinterpret_cast<const uint16_t*>(x.a_sc + x.s_off[f] + 8 * cc);
+            if (kScales) r.s[f] = *reinterpret_cast<const uint16_t*>(x.a_sc + x.s_off[f] + 8 * cc);
         }
     }
 }
@@ -143,7 +150,31 @@ __device__ __forceinline__ void load_a(const Ctx& x, int c, ARaw& r) {
 __device__ __forceinline__ void load_w(const Ctx& x, int c, WRaw& r) {
     const int cc = c < x.nk ? c : x.nk - 1;
     r.c = *reinterpret_cast<const uint4*>(x.w_nib + 64 * cc);
-    r.s = *reinterpret_cast<const uint16_t*>(x.w_sc + 8 * cc);
+}
+
+// Scale windows.  Each wave stages, per 8-chunk window, the 64 scale bytes
+// of each row it reads: of its two activation fragments and of its 16
+// weight rows, one 1 KB block each, by one direct load per block in which
+// lane (r, q) brings the 16 bytes of chunks w0 + 2 q, w0 + 2 q + 1 of row r
+// (a piece that would run past the last chunk starts at chunk nk - 2
+// instead).  Every lane then reads its own two scale bytes of a chunk from
+// LDS: one load of 16 bytes per lane per 8 chunks instead of one of 2 bytes
+// per chunk, which is what the vector memory pipeline's cost follows.
+__device__ __forceinline__ int win_piece(int w0, int q, int nk) {
+    const int p = w0 + 2 * q;
+    return p < nk - 2 ? p : nk - 2;
+}
+__device__ __forceinline__ void stage_window(const uint8_t* srow, int w0, int q, int nk,
+                                             uint32_t lds) {
+    g2l16(srow + 8 * win_piece(w0, q, nk), lds);
+}
+// The two scale bytes of chunk c for lane (r, quarter qq) of a block whose
+// window starts at chunk w0.
+__device__ __forceinline__ uint32_t window_scales(const char* blk, int w0, int c, int r, int qq,
+                                                  int nk) {
+    const int q = (c - w0) >> 1;
+    const int half = c - win_piece(w0, q, nk);
+    return *reinterpret_cast<const uint16_t*>(blk + (16 * q + r) * 16 + 8 * half + 2 * qq);
 }
 
 // Convert this thread's weight codes of a chunk (row wr, channels 32 h ..
@@ -199,7 +230,8 @@ __device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
 
 template <int kEpi, int MACT, bool LATE, bool kGather>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
-                                         const int* s_sel, const int* s_cs, const Ctx& x,
+                                         char* swin, const int* s_sel, const int* s_cs,
+                                         const Ctx& x,
                                          int wr, int wh, int64_t wfull,
                                          int kc, int wave, int lane, const int64_t src[2],
                                          int m0, int mend, int f0, int e) {
@@ -235,11 +267,19 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
 
     ARaw a0, a1;
     WRaw w0, w1;
-    // prologue: chunk 0's codes and chunk 1's weight codes requested, chunk
-    // 0's weights converted
+    // this wave's scale windows: [fragment 0][fragment 1][weight rows], 1 KB each
+    const uint32_t swin_lds = lds_addr(swin);
+    const int r16 = lane & 15;
+    // prologue: the first scale windows staged, chunk 0's codes and chunk 1's
+    // weight codes requested, chunk 0's weights converted
+#pragma unroll
+    for (int f = 0; f < MACT; ++f) stage_window(x.a_srow[f], 0, rq, nk, swin_lds + 1024 * f);
+    stage_window(x.w_srow, 0, wh, nk, swin_lds + 2048);
     load_w(x, 0, w0);
-    load_a<MACT>(x, 0, a0);
+    load_a<MACT, false>(x, 0, a0);
     load_w(x, 1, w1);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    w0.s = window_scales(swin + 2048, 0, 0, r16, wh, nk);
     store_w(w0, wbuf, wr, wh);
     __syncthreads();
 
@@ -249,7 +289,29 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     // buffer after step 0; weight fragments read one step ahead of the MFMAs
     auto chunk = [&](int c, ARaw& ac, ARaw& an, WRaw& wn, WRaw& wn2) {
         if (c >= nk) return;
-        load_a<MACT>(x, c + 1, an);
+        // scale bytes of this chunk's activations and of the next chunk's
+        // weights from the staged windows; a window staged in the previous
+        // chunk is waited for first (with it, the codes this chunk needs)
+        const int cw = c % kWin;
+        if (cw == 0 || cw == kWin - 1) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int f = 0; f < MACT; ++f)
+            ac.s[f] = window_scales(swin + 1024 * f, c - cw, c, r16, rq, nk);
+        if (c + 1 < nk)
+            wn.s = window_scales(swin + 2048, (c + 1) - (c + 1) % kWin, c + 1, r16, wh, nk);
+        // the next windows, once this wave has read the last bytes of the
+        // ones they replace
+        if (cw == kWin - 1 && c + 1 < nk) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int f = 0; f < MACT; ++f)
+                stage_window(x.a_srow[f], c + 1, rq, nk, swin_lds + 1024 * f);
+        }
+        if (cw == kWin - 2 && c + 2 < nk) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            stage_window(x.w_srow, c + 2, wh, nk, swin_lds + 2048);
+        }
+        load_a<MACT, false>(x, c + 1, an);
         load_w(x, c + 2, wn2);
         if (c == nk - 1 && kc > 0) {
 #pragma unroll
@@ -332,13 +394,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
             *reinterpret_cast<uint4*>(base + 3072) = v.d;
         };
         ARaw r0, r1;
-        load_a<MACT>(xr, 0, r0);
+        load_a<MACT, true>(xr, 0, r0);
         WsRaw wv = load_ws(0);
         store_ws(wv, wbuf);
         __syncthreads();
         auto cchunk = [&](int cc, ARaw& rc, ARaw& rn) {
             if (cc >= nkc) return;
-            load_a<MACT>(xr, cc + 1, rn);
+            load_a<MACT, true>(xr, cc + 1, rn);
             wv = load_ws(cc + 1);
             __builtin_amdgcn_sched_barrier(0);
             const char* wb = wb_lane + (cc & 1) * (BN * BK * 2);
@@ -487,6 +549,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     __shared__ __align__(16) _Float16 cap[BN * kCapLd];
     __shared__ int s_sel[kCapMaxV3];
     __shared__ int s_cs[kMaxChunksV3 + 1];
+    __shared__ __align__(16) char swin[kWaves * 3 * 1024];
     // XCD-aware numbering: hardware id h runs on XCD h % 8; tiles are dealt in
     // groups of `grp` consecutive tiles (M-tile major: one M tile's N tiles
     // share its activation rows) per XCD
@@ -524,6 +587,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     x.nk = g.K / BK;
     x.w_nib = g.w_nib + wfull * (g.K / 2) + 16 * wh;
     x.w_sc = g.w_scale + wfull * (g.K / kBlock) + 2 * wh;
+    x.w_srow = g.w_scale + wfull * (g.K / kBlock);
     // the lane's activation rows (a row past the tile reads row 0; its
     // results are never stored)
     const int r = lane & 15, q = lane >> 4;
@@ -534,6 +598,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
         src[f] = p < mend ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
         x.a_off[f] = src[f] * (g.K / 2) + 16 * q;
         x.s_off[f] = src[f] * (g.K / kBlock) + 2 * q;
+        x.a_srow[f] = g.a_scale + src[f] * (g.K / kBlock);
     }
     x.a_nib = g.a_nib;
     x.a_sc = g.a_scale;
@@ -564,7 +629,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     switch (mact + (wave >= 4 ? 4 : 0)) {
 #define QUADS_V3_TILE(M, L)                                                                     \
     case M + (L ? 4 : 0):                                                                       \
-        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, s_sel, s_cs, x, wr, wh, wfull, kc, wave,   \
+        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, swin + 3072 * wave, s_sel, s_cs, x, wr, wh,\
+                                      wfull, kc, wave,                                          \
                                       lane, src, m0, mend, f0, e);                              \
         break;
         QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)

@@ -139,26 +139,6 @@ __device__ __forceinline__ int lds_pos(int r, int c) {
     return FMT == kFp8 ? (c ^ ((r >> 1) & 7)) : (c ^ ((r >> 2) & 3));
 }
 
-// Direct HBM -> LDS loads (lane i's bytes land at LDS address m0 + i * size).
-// Written as inline assembly so that the compiler does not see an LDS write:
-// its conservative wait (every LDS read after such a load waits for it) would
-// make each stage wait for the next stage's prefetch.  The kernel waits for
-// its own loads explicitly (s_waitcnt vmcnt(0)) before each barrier.
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-__device__ __forceinline__ uint32_t lds_addr(void* l) {
-    return __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_ptr_t)l);
-}
-// `l` is an LDS byte address (wave-uniform)
-__device__ __forceinline__ void g2l16(const void* g, uint32_t l) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(l), "v"(g)
-                 : "memory", "m0");
-}
-__device__ __forceinline__ void g2l4(const void* g, uint32_t l) {
-    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dword %1, off" ::"s"(l), "v"(g)
-                 : "memory", "m0");
-}
-
 struct MxArgs {
     const uint8_t* a; const uint8_t* as; const int32_t* row_token; int64_t rows; int K;
     const uint8_t* w; const uint8_t* ws; const int32_t* offsets; int E; int N;
