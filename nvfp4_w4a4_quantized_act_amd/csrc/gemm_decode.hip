@@ -30,6 +30,15 @@
 // k0 + 64 + 8j + u: both operands take the same channels in the same slots,
 // so the MFMAs sum exactly the products of Eq. (6).
 //
+// Scale windows (K of at least two chunks).  The block scales are not
+// loaded with the codes: per 4-chunk window each wave brings the 32 scale
+// bytes of every row it reads (its two weight blocks and its token rows)
+// with one 16-byte direct-to-LDS load per lane -- lane (r, h) the scales of
+// chunks w0 + 2 h, w0 + 2 h + 1 of row r -- into one of two LDS buffers, four
+// chunks ahead, and each step reads its scale dwords from there.  A 4-byte
+// load per lane per piece costs the vector memory pipeline as much as a
+// 16-byte one, so this takes a third of the load instructions away.
+//
 // Accumulation.  The MFMA accumulators restart from zero every kAccChain
 // channels and are added into fp32 totals (gfx950's f16 MFMA rounds once per
 // group of 8 products, so a chain of 1024 channels is 128 roundings).
@@ -68,14 +77,31 @@ struct Piece {
 // The loads are unconditional: a lane without a row reads a valid row and its
 // values are zeroed at conversion time through a zero block scale (v * 0 = 0
 // for every code), so no branch makes the compiler drain the loads in flight.
+template <bool kWin>
 __device__ __forceinline__ Piece load_piece(const uint8_t* nib, const uint8_t* sc,
                                             uint32_t nib_off, uint32_t sc_off) {
     const uint4* q = reinterpret_cast<const uint4*>(nib + nib_off);
     Piece p;
     p.lo = q[0];
     p.hi = q[1];
-    p.sc = *reinterpret_cast<const uint32_t*>(sc + sc_off);
+    p.sc = kWin ? 0u : *reinterpret_cast<const uint32_t*>(sc + sc_off);
     return p;
+}
+
+// Scale windows: piece h of the window starting at chunk w0 covers chunks
+// ps, ps + 1 with ps = min(w0 + 2 h, nch - 2) (no read past a row's scales).
+constexpr int kWinChunks = 4;
+__device__ __forceinline__ int win_start(int w0, int h, int nch) {
+    const int p = w0 + 2 * h;
+    return p < nch - 2 ? p : nch - 2;
+}
+// The scale dword of chunk c for lane (r, h) of a window block (1 KB) whose
+// window starts at chunk w0.
+__device__ __forceinline__ uint32_t win_scales(const char* blk, int w0, int c, int r, int h,
+                                               int nch) {
+    const int pi = (c - w0) >> 1;
+    const int half = c - win_start(w0, pi, nch);
+    return *reinterpret_cast<const uint32_t*>(blk + (32 * pi + r) * 16 + 8 * half + 4 * h);
 }
 
 __device__ __forceinline__ uint32_t word(const Piece& p, int j) {
@@ -155,9 +181,11 @@ __device__ __forceinline__ int decode_rows(const GemmArgs& g, int n) {
 // kRing (2, 3 or 4): chunks in flight per wave, chosen so that the chunk count
 // is a multiple of it where it can be (the loads past the last chunk are
 // wasted work).
-template <int kEpi, int kRing, bool kSplit>
+template <int kEpi, int kRing, bool kSplit, bool kWin>
 __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
+    // scale windows: [wave][buffer][weight block 0, weight block 1, token rows]
+    __shared__ __align__(16) char swin[kWaves][2][3][1024];
     // compensation weight columns, per wave and row block: [row][channel]
     __shared__ __align__(16) _Float16 capt[kWaves][2][32][kCapLd];
     // a chunk's weight pieces, word-major, while its compensation columns are taken
@@ -220,6 +248,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
     const uint8_t* wnib = g.w_nib + (int64_t)e * g.N * kn;
     const uint8_t* wsc = g.w_scale + (int64_t)e * g.N * ks;
     uint32_t wrow_n[2], wrow_s[2];
+    const uint8_t* wsrow[2];
     bool wv[2];
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
@@ -235,6 +264,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         row = wv[q] ? row : 0;
         wrow_n[q] = (uint32_t)row * kn + 32 * h;
         wrow_s[q] = (uint32_t)row * ks + 4 * h;
+        wsrow[q] = wsc + (uint64_t)row * ks;
     }
 
     const int nch = g.K / kChunk;
@@ -273,16 +303,31 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         const int64_t src = rv ? (g.row_token ? (int64_t)g.row_token[p] : (int64_t)p) : 0;
         auto ldw = [&](Piece& w0, Piece& w1, int c) {
             const uint32_t cl = (uint32_t)(c < nch ? c : nch - 1);
-            w0 = load_piece(wnib, wsc, wrow_n[0] + 64 * cl, wrow_s[0] + 8 * cl);
-            w1 = load_piece(wnib, wsc, wrow_n[1] + 64 * cl, wrow_s[1] + 8 * cl);
+            w0 = load_piece<kWin>(wnib, wsc, wrow_n[0] + 64 * cl, wrow_s[0] + 8 * cl);
+            w1 = load_piece<kWin>(wnib, wsc, wrow_n[1] + 64 * cl, wrow_s[1] + 8 * cl);
         };
         // the token row: a per-lane base (the activation tensor may exceed 4 GB)
         const uint8_t* an = g.a_nib + src * kn + 32 * h;
         const uint8_t* as = g.a_scale + src * ks + 4 * h;
+        const uint8_t* asrow = g.a_scale + src * ks;
         auto lda = [&](Piece& a, int c) {
             const uint32_t cl = (uint32_t)(c < nch ? c : nch - 1);
-            a = load_piece(an, as, 64 * cl, 8 * cl);
+            a = load_piece<kWin>(an, as, 64 * cl, 8 * cl);
         };
+        // the scale window of chunks w0 .. w0 + 3 into buffer `b`
+        const uint32_t swin_lds = lds_addr(&swin[wave][0][0][0]);
+        auto stage_win = [&](int w0, int b) {
+            if (!kWin) return;
+            const int ps = win_start(w0, h, nch);
+            const uint32_t l = swin_lds + 3072 * b;
+            g2l16(wsrow[0] + 8 * ps, l);
+            g2l16(wsrow[1] + 8 * ps, l + 1024);
+            g2l16(asrow + 8 * ps, l + 2048);
+        };
+        // the previous pass's last window reads are done before the buffers
+        // are written again
+        if (kWin && c0 > 0) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        stage_win(0, 0);
         Piece w0a, w1a, aa, w0b, w1b, ab, w0c, w1c, ac, w0d, w1d, ad;
         ldw(w0a, w1a, 0);
         lda(aa, 0);
@@ -311,6 +356,24 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         int ci = 0;                                   // next compensation channel to capture
         auto step = [&](Piece& w0, Piece& w1, Piece& a, int c) {
             if (c < nch) {
+                if (kWin) {
+                    const int wb = (c / kWinChunks) & 1;
+                    const int w0c = c - c % kWinChunks;
+                    // this chunk's codes have arrived (the compiler waits for
+                    // them here), and with them its window, requested before
+                    // them; then its scale dwords
+                    asm volatile("" ::"v"(w0.lo.x), "v"(w1.lo.x), "v"(a.lo.x) : "memory");
+                    const char* blk = &swin[wave][wb][0][0];
+                    w0.sc = win_scales(blk, w0c, c, r, h, nch);
+                    w1.sc = win_scales(blk + 1024, w0c, c, r, h, nch);
+                    a.sc = win_scales(blk + 2048, w0c, c, r, h, nch);
+                    // the next window, into the buffer the previous one used
+                    // (last read one chunk ago)
+                    if (c % kWinChunks == 0 && c + kWinChunks < nch) {
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        stage_win(c + kWinChunks, wb ^ 1);
+                    }
+                }
                 if (c0 == 0 && ci < g.k &&
                     __builtin_amdgcn_readlane(sel_lo, ci) < kChunk * (c + 1)) {
                     // capture W[:, sel[i]] for the selected channels in this
@@ -496,8 +559,17 @@ int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
     // its totals take registers, so that variant keeps two chunks in flight
     // per wave (two waves per SIMD instead of one: the same loads in flight)
     const bool split = g.K + g.k > kSingleChainMax;
-#define QUADS_DEC(EPI, RING, SPLIT) \
-    hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<EPI, RING, SPLIT>), grid, block, 0, st, g)
+    // scale windows need two chunks per row (a window piece covers two)
+    const bool win = nch >= 2;
+#define QUADS_DEC(EPI, RING, SPLIT)                                                             \
+    do {                                                                                        \
+        if (win)                                                                                \
+            hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<EPI, RING, SPLIT, true>), grid, block,  \
+                               0, st, g);                                                       \
+        else                                                                                    \
+            hipLaunchKernelGGL((dec::k_gemm_w4a4_decode<EPI, RING, SPLIT, false>), grid, block, \
+                               0, st, g);                                                       \
+    } while (0)
     if (split) {
         if (sw) QUADS_DEC(QUADS_EPI_SWIGLU, 2, true);
         else QUADS_DEC(QUADS_EPI_NONE, 2, true);

@@ -224,9 +224,26 @@ __device__ void select_keys(const unsigned long long* s_key, const uint32_t* s_c
         if (tid < 256) s_hist[tid] = 0;
         __syncthreads();
         const unsigned long long prefix = s_prefix;
-        for (int j = tid; j < K; j += 1024) {
-            const unsigned long long key = s_key[j];
-            if ((key & mask) == prefix) atomicAdd(&s_hist[(int)((key >> shift) & 0xFF)], 1);
+        // histogram of the digit under the prefix.  The keys are scores of
+        // one tensor, so the first digits of most of them agree and plain LDS
+        // atomics would queue on one or two bins: lanes of a wave that share
+        // a bin add their count once (up to four distinct bins per wave),
+        // the rest one by one.
+        const int lane = tid & 63;
+        for (int j0 = 0; j0 < K; j0 += 1024) {
+            const int j = j0 + tid;
+            const unsigned long long key = j < K ? s_key[j] : 0ull;
+            const bool in = j < K && (key & mask) == prefix;
+            const int bin = (int)((key >> shift) & 0xFF);
+            unsigned long long pend = __ballot(in);
+            for (int it = 0; it < 4 && pend != 0ull; ++it) {
+                const int leader = __ffsll((long long)pend) - 1;
+                const int lb = __shfl(bin, leader, 64);
+                const unsigned long long same = __ballot(in && bin == lb) & pend;
+                if (lane == leader) atomicAdd(&s_hist[lb], __popcll(same));
+                pend &= ~same;
+            }
+            if ((pend >> lane) & 1ull) atomicAdd(&s_hist[bin], 1);
         }
         __syncthreads();
         if (tid < 64) {
