@@ -156,7 +156,7 @@ def traffic_summary(fetch_dir, write_dir, copy_mib):
         "intermediate 768, top-8, RAC k=64",
         "",
         "The call is two launches: the tiled kernel `v3::k_gemm_w4a4_v3<1, false>` and the decode "
-        "kernel `dec::k_gemm_w4a4_decode<1, 2, true>` for the rows past 256 of experts of 257 .. "
+        "kernel `dec::k_gemm_w4a4_decode<1, 2, true, true>` for the rows past 256 of experts of 257 .. "
         "320 rows; the figures below add the two kernels' per-dispatch means.",
         "",
         "Commands (repository root, one MI355X), then this summary on any host:",
@@ -248,7 +248,7 @@ def trace_summary(trace_dir):
         "launch shape (work-groups in x and y, threads per work-group), so that launches of one "
         "kernel on different workloads show apart.  The prefill layer's gate/up GEMM is "
         "`v3::k_gemm_w4a4_v3<1, false>` at (3072, 1) x 512 plus "
-        "`dec::k_gemm_w4a4_decode<1, 2, true>` at (1536, 1) x 128 for the rows past 256 of "
+        "`dec::k_gemm_w4a4_decode<1, 2, true, true>` at (1536, 1) x 128 for the rows past 256 of "
         "experts of 257 .. 320 rows; config 5's gate/up GEMMs are the tiled kernel at (13824, 1) "
         "x 512 (`<1, true>`: k = 2048, with the gathered compensation); the decode layer's "
         "GEMMs are the decode kernel at (1632, 1) and (2176, 1).  The down GEMM (768 + 64 "
@@ -590,7 +590,7 @@ def main():
                    "accumulate": "fp32", "parallelism": "single_gpu"},
         "roofline": {"bound": "mfma",
                      "kernel": "gate/up GEMM call, SwiGLU epilogue: v3::k_gemm_w4a4_v3<1, false> "
-                               "(256-row tiles) + dec::k_gemm_w4a4_decode<1, 2, true> (rows past "
+                               "(256-row tiles) + dec::k_gemm_w4a4_decode<1, 2, true, true> (rows past "
                                "256 of experts of 257..320 rows)",
                      "achieved": gu_tflops, "peak": PEAK_FP16_TFLOPS, "unit": "TFLOP/s",
                      "frac": gu_tflops / PEAK_FP16_TFLOPS, "traffic": measured_traffic()},
