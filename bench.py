@@ -64,7 +64,7 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_gemm_gate_up_t
 TRACE_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_kernel_trace.md")
 PMC_FILE = os.path.join(ROOT, "profiles", "moe_ffn_e128_t4096_counters.md")
 GEMM_SOURCES = [os.path.join(ROOT, "nvfp4_w4a4_quantized_act_amd", "csrc", f)
-                for f in ("gemm.hip", "gemm_v3.hip", "gemm_tiles.h", "common.h")]
+                for f in ("gemm.hip", "gemm_v3.hip", "gemm_decode.hip", "gemm_tiles.h", "common.h")]
 # the gate/up (SwiGLU) GEMM call: the tiled kernel, and the decode kernel that
 # takes the rows past 256 of experts of 257 .. 320 rows
 GEMM_KERNEL_KEYS = ("k_gemm_w4a4_v3<1, false>", "k_gemm_w4a4_decode<1,")
