@@ -427,21 +427,50 @@ __device__ __forceinline__ void mma_kk(const _Float16* sa_base, const _Float16* 
             acc[mi][nj] = __builtin_amdgcn_mfma_f32_32x32x16_f16(b[nj], a[mi], acc[mi][nj], 0, 0, 0);
 }
 
-// Copies the weight columns of the selected channels that fall in this
+// Capture of the weight columns of the selected channels that fall in a
 // stage (k0 .. k0 + 63) from the stage's W tile into ws_s (column = index
-// into sel): thread rows crow, channels of parity cpar.  Lane i of every wave
+// into sel): thread rows crow, indices of parity cpar.  Lane i of every wave
 // holds my_sel = sel[i] (kc <= 64 channels), so the stage's channels are one
-// ballot and their indices come from readlane: no memory loads.
-__device__ __forceinline__ void capture(const _Float16* cur_w, _Float16* ws_s, int my_sel,
-                                        int k0, int crow, int cpar) {
-    unsigned long long m = __ballot(my_sel >= k0 && my_sel < k0 + BK);
+// ballot and their indices come from readlane: no memory loads.  The first
+// kCapBatch values are read before the stage's MFMAs and written after them
+// (their LDS latency hides behind the MFMAs instead of standing before the
+// stage's barrier); further ones, if any, are copied one by one at the end.
+constexpr int kCapBatch = 4;
+struct CapBatch {
+    unsigned long long rest;      // channels not in the batch (sel indices)
+    int ic[kCapBatch];            // sel index of each batch entry, -1: none
+    _Float16 v[kCapBatch];
+};
+
+__device__ __forceinline__ void capture_read(const _Float16* cur_w, int my_sel, int k0, int crow,
+                                             int cpar, CapBatch& b) {
+    unsigned long long m = __ballot(my_sel >= k0 && my_sel < k0 + BK) &
+                           (cpar ? 0xAAAAAAAAAAAAAAAAull : 0x5555555555555555ull);
+#pragma unroll
+    for (int u = 0; u < kCapBatch; ++u) {
+        b.ic[u] = -1;
+        if (m) {
+            const int ic = __ffsll(m) - 1;
+            m &= m - 1;
+            const int c = __builtin_amdgcn_readlane(my_sel, ic) - k0;
+            b.ic[u] = ic;
+            b.v[u] = cur_w[swz(crow, c >> 3) + (c & 7)];
+        }
+    }
+    b.rest = m;
+}
+
+__device__ __forceinline__ void capture_write(const _Float16* cur_w, _Float16* ws_s, int my_sel,
+                                              int k0, int crow, CapBatch& b) {
+#pragma unroll
+    for (int u = 0; u < kCapBatch; ++u)
+        if (b.ic[u] >= 0) ws_s[swz(crow, b.ic[u] >> 3) + (b.ic[u] & 7)] = b.v[u];
+    unsigned long long m = b.rest;
     while (m) {
         const int ic = __ffsll(m) - 1;
         m &= m - 1;
-        if ((ic & 1) == cpar) {
-            const int c = __builtin_amdgcn_readlane(my_sel, ic) - k0;
-            ws_s[swz(crow, ic >> 3) + (ic & 7)] = cur_w[swz(crow, c >> 3) + (c & 7)];
-        }
+        const int c = __builtin_amdgcn_readlane(my_sel, ic) - k0;
+        ws_s[swz(crow, ic >> 3) + (ic & 7)] = cur_w[swz(crow, c >> 3) + (c & 7)];
     }
 }
 
@@ -549,6 +578,8 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
     for (int it = 0; it < nk; ++it) {
         _Float16* cur = smem + (it & 1) * kStage;
         _Float16* nxt = smem + ((it & 1) ^ 1) * kStage;
+        CapBatch cb;
+        if (kc > 0) capture_read(cur + BM * BK, my_sel, it * BK, crow, cpar, cb);
         stage<MACT, ALIVE, LATE>(cur, nxt, a0, b0, lr, lh, wm, wn, fo, acc);
         if (ALIVE) {
             const bool past = it + 2 >= nk;
@@ -557,7 +588,7 @@ __device__ __forceinline__ void main_stages(const GemmArgs& g, _Float16* smem, _
             a0 = load_raw(an, as, 32 * lh, true);
         }
         b0 = load_raw(w_nib_row, w_sc_row, min((it + 2) * BK, klast) + 32 * lh, true);
-        if (kc > 0) capture(cur + BM * BK, ws_s, my_sel, it * BK, crow, cpar);
+        if (kc > 0) capture_write(cur + BM * BK, ws_s, my_sel, it * BK, crow, cb);
         __syncthreads();
     }
     if (kc == 0) return;

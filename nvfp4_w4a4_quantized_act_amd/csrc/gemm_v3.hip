@@ -54,6 +54,8 @@
 // chunks go by; after the main chunks, R x W[:, S] runs in the accumulators
 // (restarted from zero) and the epilogue forms
 //   Y = totals * s_tA s_tW[e] + acc * s_tR s_tW[e].
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_tiles.h"
 
@@ -231,7 +233,7 @@ __device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
 template <int kEpi, int MACT, bool LATE, bool kGather>
 __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
                                          char* swin, const int* s_sel, const int* s_cs,
-                                         const Ctx& x,
+                                         const uint32_t* s_capd, const Ctx& x,
                                          int wr, int wh, int64_t wfull,
                                          int kc, int wave, int lane, const int64_t src[2],
                                          int m0, int mend, int f0, int e) {
@@ -250,20 +252,45 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     uint32_t rcode[2][2] = {{0u, 0u}, {0u, 0u}}, rsb[2][2] = {{0u, 0u}, {0u, 0u}};
     const int rq = lane >> 4;
     const char* wb_lane = wbuf + lane * 16;
-    // capture: the selected channels s_cs[c] .. s_cs[c + 1] - 1 lie in chunk c
+    // capture: the selected channels s_cs[c] .. s_cs[c + 1] - 1 lie in chunk
+    // c; thread group p (= cap_par) copies those of index ci + p + 4 j.  The
+    // first two come from the chunk's descriptor s_capd[4 c + p] (read a
+    // chunk ahead): their values are read at the chunk's start and written
+    // after its MFMAs, so the LDS latency hides behind them; any further
+    // ones are copied one by one at the end of the chunk.
     const int cap_row = threadIdx.x & (BN - 1), cap_par = threadIdx.x >> 7;   // capture roles
-    auto capture = [&](const char* wb, int c) {
-        if (kc == 0) return;
-        int ci = s_cs[c], ce = s_cs[c + 1];
-        ci = ci < 0 ? 0 : (ci > kc ? kc : ci);                 // bounds only: sel ascending
-        ce = ce < ci ? ci : (ce > kc ? kc : ce);
-        for (int i = ci + cap_par; i < ce; i += kThreads / BN) {
-            int ch = s_sel[i] - BK * c;
-            ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);
-            cap[cap_row * kCapLd + i] = *reinterpret_cast<const _Float16*>(
-                wb + wblock_off(cap_row, ch & ~7) + 2 * (ch & 7));
+    auto cap_read = [&](const char* wb, uint32_t d, _Float16& v0, _Float16& v1) {
+        const uint32_t n = d >> 30;
+        if (n >= 1) {
+            const int ch = d & 127;
+            v0 = *reinterpret_cast<const _Float16*>(wb + wblock_off(cap_row, ch & ~7) +
+                                                    2 * (ch & 7));
+        }
+        if (n >= 2) {
+            const int ch = (d >> 15) & 127;
+            v1 = *reinterpret_cast<const _Float16*>(wb + wblock_off(cap_row, ch & ~7) +
+                                                    2 * (ch & 7));
         }
     };
+    auto cap_write2 = [&](uint32_t d, _Float16 v0, _Float16 v1) {
+        const uint32_t n = d >> 30;
+        if (n >= 1) cap[cap_row * kCapLd + ((d >> 7) & 255)] = v0;
+        if (n >= 2) cap[cap_row * kCapLd + ((d >> 22) & 255)] = v1;
+    };
+    auto cap_write = [&](const char* wb, int c, uint32_t d, _Float16 v0, _Float16 v1) {
+        {
+            int ci = s_cs[c], ce = s_cs[c + 1];
+            ci = ci < 0 ? 0 : (ci > kc ? kc : ci);             // bounds only: sel ascending
+            ce = ce < ci ? ci : (ce > kc ? kc : ce);
+            for (int i = ci + cap_par + 8; i < ce; i += kThreads / BN) {
+                int ch = s_sel[i] - BK * c;
+                ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);
+                cap[cap_row * kCapLd + i] = *reinterpret_cast<const _Float16*>(
+                    wb + wblock_off(cap_row, ch & ~7) + 2 * (ch & 7));
+            }
+        }
+    };
+    uint32_t capd = 0u;
 
     ARaw a0, a1;
     WRaw w0, w1;
@@ -282,12 +309,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     w0.s = window_scales(swin + 2048, 0, 0, r16, wh, nk);
     store_w(w0, wbuf, wr, wh);
     __syncthreads();
+    if (kc > 0) capd = s_capd[cap_par];
 
     // chunk c: activation codes of c + 1 and weight codes of c + 2 requested
     // (chunk c - 1's activation slot and chunk c's weight slot, converted in
     // chunk c - 1, are free); chunk c + 1's weights converted into the other
     // buffer after step 0; weight fragments read one step ahead of the MFMAs
-    auto chunk = [&](int c, ARaw& ac, ARaw& an, WRaw& wn, WRaw& wn2) {
+    auto chunk = [&](int c, ARaw& ac, ARaw& an, WRaw& wn, WRaw& wn2, auto tail) {
         if (c >= nk) return;
         // scale bytes of this chunk's activations and of the next chunk's
         // weights from the staged windows; a window staged in the previous
@@ -299,6 +327,13 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
             ac.s[f] = window_scales(swin + 1024 * f, c - cw, c, r16, rq, nk);
         if (c + 1 < nk)
             wn.s = window_scales(swin + 2048, (c + 1) - (c + 1) % kWin, c + 1, r16, wh, nk);
+        // this chunk's captured values requested, the next chunk's descriptor
+        const uint32_t cd = __builtin_amdgcn_readfirstlane(capd);
+        _Float16 cv0 = (_Float16)0.0f, cv1 = (_Float16)0.0f;
+        if (kc > 0) {
+            cap_read(wbuf + (c & 1) * (BN * BK * 2), cd, cv0, cv1);
+            if (c + 1 < nk) capd = s_capd[4 * (c + 1) + cap_par];
+        }
         // the next windows, once this wave has read the last bytes of the
         // ones they replace
         if (cw == kWin - 1 && c + 1 < nk) {
@@ -313,7 +348,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
         }
         load_a<MACT, false>(x, c + 1, an);
         load_w(x, c + 2, wn2);
-        if (c == nk - 1 && kc > 0) {
+        if (decltype(tail)::value && c == nk - 1 && kc > 0) {
 #pragma unroll
             for (int s2 = 0; s2 < 2; ++s2) {
                 const int ch = 32 * s2 + 8 * rq;
@@ -327,6 +362,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
                 }
             }
         }
+        if (kc > 0) cap_write2(cd, cv0, cv1);
         // keep the requests here, a whole chunk ahead of their use (left to
         // itself the scheduler sinks them towards their use and the chunk
         // then waits on their latency)
@@ -348,17 +384,22 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
         }
         __builtin_amdgcn_s_setprio(0);
         if (!LATE && c + 1 < nk) store_w(wn, wnext, wr, wh);
-        capture(wbuf + (c & 1) * (BN * BK * 2), c);
+        if (kc > 0 && cd >> 30 == 3) cap_write(wbuf + (c & 1) * (BN * BK * 2), c, cd, cv0, cv1);
         if ((c + 1) % kFlush == 0 || c + 1 == nk) {
             add_set<MACT>(T, X);
             zero_set<MACT>(X);
         }
         __syncthreads();
     };
-    for (int c = 0; c < nk; c += 2) {
-        chunk(c, a0, a1, w1, w0);
-        chunk(c + 1, a1, a0, w0, w1);
+    // the last two chunks apart: only they request the compensation's first
+    // residual codes, which then stay out of the loop's live registers
+    int c0 = 0;
+    for (; c0 + 2 < nk; c0 += 2) {
+        chunk(c0, a0, a1, w1, w0, std::false_type{});
+        chunk(c0 + 1, a1, a0, w0, w1, std::false_type{});
     }
+    chunk(c0, a0, a1, w1, w0, std::true_type{});
+    chunk(c0 + 1, a1, a0, w0, w1, std::true_type{});
 
     const bool comp = (kGather ? g.k : kc) > 0 && s_tr > 0.0f;
     if (kGather && comp) {
@@ -549,6 +590,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     __shared__ __align__(16) _Float16 cap[BN * kCapLd];
     __shared__ int s_sel[kCapMaxV3];
     __shared__ int s_cs[kMaxChunksV3 + 1];
+    __shared__ uint32_t s_capd[4 * kMaxChunksV3];
     __shared__ __align__(16) char swin[kWaves * 3 * 1024];
     // XCD-aware numbering: hardware id h runs on XCD h % 8; tiles are dealt in
     // groups of `grp` consecutive tiles (M-tile major: one M tile's N tiles
@@ -623,14 +665,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
             cap[(i / (kpad - kc)) * kCapLd + kc + i % (kpad - kc)] = (_Float16)0.0f;
     }
     __syncthreads();
+    // capture descriptors, one per chunk c and thread group p: the number of
+    // selected indices ci + p + 4 j in chunk c (3: more than two), and the
+    // first two as (index, channel in the chunk); bits 0-6 / 7-14 the first
+    // channel / index, 15-21 / 22-29 the second, 30-31 the number
+    if (kc > 0 && tid < 4 * x.nk) {
+        const int c = tid >> 2, p = tid & 3;
+        int ci = s_cs[c], ce = s_cs[c + 1];
+        ci = ci < 0 ? 0 : (ci > kc ? kc : ci);                 // bounds only: sel ascending
+        ce = ce < ci ? ci : (ce > kc ? kc : ce);
+        const int n = ce > ci + p ? (ce - ci - p + 3) / 4 : 0;
+        uint32_t d = (uint32_t)(n < 3 ? n : 3) << 30;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j < n) {
+                const int i = ci + p + 4 * j;
+                int ch = s_sel[i] - BK * c;
+                ch = ch < 0 ? 0 : (ch > BK - 1 ? BK - 1 : ch);
+                d |= ((uint32_t)ch | (uint32_t)i << 7) << (15 * j);
+            }
+        }
+        s_capd[tid] = d;
+    }
 
     int mact = (mend - (m0 + 32 * wave) + 15) / 16;
     mact = __builtin_amdgcn_readfirstlane(mact < 0 ? 0 : (mact > 2 ? 2 : mact));
     switch (mact + (wave >= 4 ? 4 : 0)) {
 #define QUADS_V3_TILE(M, L)                                                                     \
     case M + (L ? 4 : 0):                                                                       \
-        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, swin + 3072 * wave, s_sel, s_cs, x, wr, wh,\
-                                      wfull, kc, wave,                                          \
+        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, swin + 3072 * wave, s_sel, s_cs, s_capd, x,  \
+                                      wr, wh, wfull, kc, wave,                                  \
                                       lane, src, m0, mend, f0, e);                              \
         break;
         QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)
