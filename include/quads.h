@@ -88,6 +88,21 @@ int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* t
                          void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * quads_nvfp4_quantize with the dynamic tensor scale of Eq. (9) taken from
+ * a producer's partial maxima of |x| instead of a max pass over x (one pass
+ * over x instead of two), e.g. the ones quads_moe_w4a4_gemm_amax writes for
+ * its SwiGLU output.
+ *   amax_part  uint32 [groups], groups >= 1: bf16 magnitude bit patterns
+ *              (|x| as bf16 bits & 0x7FFF) whose maximum is that of every
+ *              element of x; nib, scale and ts_out are then those of
+ *              quads_nvfp4_quantize(ts_in = NULL) bit for bit
+ * No workspace.  M == 0 writes ts_out = 0.
+ */
+int quads_nvfp4_quantize_partials(const uint16_t* x, int64_t M, int64_t K,
+                                  const uint32_t* amax_part, int64_t groups, uint8_t* nib,
+                                  uint8_t* scale, float* ts_out, void* stream);
+
+/*
  * Per-row (per-token) variant of the NVFP4 activation quantization: each
  * row of x is quantized as a tensor of its own, with its own dynamic tensor
  * scale s_t[m] = RN32(max_j |x[m, j]| / 2688) and then the block and element
@@ -126,6 +141,21 @@ int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32_t k,
                        uint8_t* nib, uint8_t* scale, float* ts,
                        int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
                        double* score_out, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * quads_rac_quantize with max|x| (the tensor scale of the main NVFP4 pass)
+ * from a producer's partial maxima, as in quads_nvfp4_quantize_partials:
+ * the max pass over x is skipped.  amax_part [groups] must have the maximum
+ * of |x| (bf16 magnitude bits); every output is then that of
+ * quads_rac_quantize bit for bit (inputs of at most 64 rows and 16384
+ * elements take the one-launch path, which reads the maximum from x
+ * itself).  Workspace and other arguments as quads_rac_quantize.
+ */
+int quads_rac_quantize_partials(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                const uint32_t* amax_part, int64_t groups,
+                                uint8_t* nib, uint8_t* scale, float* ts,
+                                int32_t* sel, uint8_t* r_nib, uint8_t* r_scale, float* r_ts,
+                                double* score_out, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * quads_rac_quantize without a workspace argument, for callers that cannot
@@ -238,6 +268,37 @@ int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale, const floa
                         const int32_t* offsets, int32_t E, int64_t N,
                         int epilogue, int out_dtype, void* out,
                         void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * The SwiGLU form of quads_moe_w4a4_gemm (epilogue QUADS_EPI_SWIGLU, bf16
+ * out) that also hands the next quantizer the maximum of its output h, so
+ * that quantizing h (the down projection's input, Eq. (9) or section 3.3 at
+ * the second site) needs no separate max pass: every work-group of the
+ * call writes the largest |h| it stored, as bf16 magnitude bits, into its
+ * own slot of amax_part (no atomics), and slots no work-group takes are
+ * written 0.  The maximum over amax_part[0 .. amax_groups) is then
+ * max |h| exactly; pass (amax_part, amax_groups) to
+ * quads_nvfp4_quantize_partials or quads_rac_quantize_partials.
+ *   amax_part    out uint32 [amax_groups], amax_groups >= the value of
+ *                quads_moe_w4a4_gemm_amax_groups for the call's sizes
+ *                (QUADS_EWORKSPACE if smaller)
+ *   every other argument, the workspace and the error bound as in
+ *   quads_moe_w4a4_gemm with epilogue = QUADS_EPI_SWIGLU and out_dtype =
+ *   QUADS_OUT_BF16.  rows == 0 writes nothing.
+ * quads_moe_w4a4_gemm_amax_groups: the slot count for these sizes (the
+ * work-groups of the call's launches, the largest over calls with or
+ * without offsets and workspace), or 0 for sizes the GEMM rejects.
+ */
+int64_t quads_moe_w4a4_gemm_amax_groups(int64_t rows, int64_t K, int32_t k, int32_t E,
+                                        int64_t N);
+int quads_moe_w4a4_gemm_amax(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
+                             const int32_t* row_token, int64_t rows, int64_t K,
+                             const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
+                             const int32_t* sel, int32_t k,
+                             const uint8_t* w_nib, const uint8_t* w_scale, const float* w_ts,
+                             const int32_t* offsets, int32_t E, int64_t N, void* out,
+                             uint32_t* amax_part, int64_t amax_groups,
+                             void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Grouped W4A4 GEMM with per-row activation tensor scales (the activations

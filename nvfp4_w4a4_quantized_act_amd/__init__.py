@@ -16,7 +16,9 @@ import torch
 
 __all__ = [
     "QuadsError", "lib", "library_path",
-    "quads_nvfp4_quantize", "quads_nvfp4_quantize_rows", "quads_rac_quantize",
+    "quads_nvfp4_quantize", "quads_nvfp4_quantize_partials", "quads_nvfp4_quantize_rows",
+    "quads_rac_quantize", "quads_rac_quantize_partials", "quads_moe_w4a4_gemm_amax",
+    "quads_moe_w4a4_gemm_amax_groups",
     "quads_rac_quantize_experts", "quads_moe_w4a4_gemm_sel_experts",
     "quads_nvfp4_weight_qdq", "quads_moe_pack", "quads_moe_w4a4_gemm",
     "quads_moe_w4a4_gemm_rowscale", "quads_moe_combine",
@@ -41,10 +43,13 @@ _SIGNATURES = {
     "quads_version": (ctypes.c_char_p, []),
     "quads_nvfp4_quantize_ws": (_SZ, [_I64, _I64]),
     "quads_nvfp4_quantize": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "quads_nvfp4_quantize_partials": (ctypes.c_int, [_P, _I64, _I64, _P, _I64, _P, _P, _P, _P]),
     "quads_nvfp4_quantize_rows": (ctypes.c_int, [_P, _I64, _I64, _P, _P, _P, _P]),
     "quads_rac_quantize_ws": (_SZ, [_I64, _I64, _I32]),
     "quads_rac_quantize": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _P,
                                           _P, _P, _SZ, _P]),
+    "quads_rac_quantize_partials": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _I64, _P, _P, _P,
+                                                   _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "quads_rac_quantize_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I32, _P, _P, _P, _P, _P, _P,
                                                   _P, _P, _P]),
     "quads_rac_quantize_experts_ws": (_SZ, [_I64, _I64, _I32, _I32]),
@@ -63,6 +68,10 @@ _SIGNATURES = {
     "quads_moe_w4a4_gemm": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _I32,
                                            _P, _P, _P, _P, _I32, _I64, ctypes.c_int,
                                            ctypes.c_int, _P, _P, _SZ, _P]),
+    "quads_moe_w4a4_gemm_amax_groups": (_I64, [_I64, _I64, _I32, _I32, _I64]),
+    "quads_moe_w4a4_gemm_amax": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P, _I32,
+                                                _P, _P, _P, _P, _I32, _I64, _P, _P, _I64, _P,
+                                                _SZ, _P]),
     "quads_moe_w4a4_gemm_rowscale": (ctypes.c_int, [_P, _P, _P, _P, _I64, _I64, _P, _P, _P, _P,
                                                     _I32, _I64, ctypes.c_int, ctypes.c_int, _P,
                                                     _P, _SZ, _P]),
@@ -144,6 +153,21 @@ def quads_nvfp4_quantize(x, ts_in=None):
     return nib, scale, ts
 
 
+def quads_nvfp4_quantize_partials(x, amax_part):
+    """NVFP4 of bf16 x [M, K] with max|x| from partial maxima (uint32 bf16 magnitude bits
+    [groups], e.g. from quads_moe_w4a4_gemm_amax) -> (nib, scale, ts)."""
+    x = _bits16(x)
+    m, k = x.shape
+    dev = x.device
+    nib = torch.empty((m, k // 2), dtype=torch.uint8, device=dev)
+    scale = torch.empty((m, k // 16), dtype=torch.uint8, device=dev)
+    ts = torch.empty(4, dtype=torch.float32, device=dev)[:1]
+    _check("quads_nvfp4_quantize_partials", lib().quads_nvfp4_quantize_partials(
+        _ptr(x), m, k, _ptr(amax_part), int(amax_part.numel()), _ptr(nib), _ptr(scale), _ptr(ts),
+        _stream(dev)))
+    return nib, scale, ts
+
+
 def quads_nvfp4_quantize_rows(x):
     """NVFP4 of bf16 x [M, K] with one tensor scale per row -> (nib uint8 [M, K/2],
     scale uint8 [M, K/16], ts fp32 [M])."""
@@ -178,6 +202,32 @@ def quads_rac_quantize(x, k, want_score=False):
     ws, nws = _ws(lib().quads_rac_quantize_ws(m, kd, k), dev)
     _check("quads_rac_quantize", lib().quads_rac_quantize(
         _ptr(x), m, kd, k, _ptr(out["nib"]), _ptr(out["scale"]), _ptr(out["ts"]),
+        _ptr(out["sel"]) if k else None, _ptr(out["r_nib"]) if k and m else None,
+        _ptr(out["r_scale"]) if k and m else None, _ptr(out["r_ts"]), _ptr(out.get("score")),
+        _ptr(ws), nws, _stream(dev)))
+    return out
+
+
+def quads_rac_quantize_partials(x, k, amax_part, want_score=False):
+    """quads_rac_quantize with max|x| from partial maxima (uint32 [groups])."""
+    x = _bits16(x)
+    m, kd = x.shape
+    dev = x.device
+    out = dict(
+        nib=torch.empty((m, kd // 2), dtype=torch.uint8, device=dev),
+        scale=torch.empty((m, kd // 16), dtype=torch.uint8, device=dev),
+        ts=torch.empty(4, dtype=torch.float32, device=dev)[:1],
+        sel=torch.empty(max(k, 4), dtype=torch.int32, device=dev)[:k],
+        r_nib=torch.empty((m, k // 2), dtype=torch.uint8, device=dev),
+        r_scale=torch.empty((m, k // 16), dtype=torch.uint8, device=dev),
+        r_ts=torch.empty(4, dtype=torch.float32, device=dev)[:1],
+    )
+    if want_score:
+        out["score"] = torch.empty(kd, dtype=torch.float64, device=dev)
+    ws, nws = _ws(lib().quads_rac_quantize_ws(m, kd, k), dev)
+    _check("quads_rac_quantize_partials", lib().quads_rac_quantize_partials(
+        _ptr(x), m, kd, k, _ptr(amax_part), int(amax_part.numel()), _ptr(out["nib"]),
+        _ptr(out["scale"]), _ptr(out["ts"]),
         _ptr(out["sel"]) if k else None, _ptr(out["r_nib"]) if k and m else None,
         _ptr(out["r_scale"]) if k and m else None, _ptr(out["r_ts"]), _ptr(out.get("score")),
         _ptr(ws), nws, _stream(dev)))
@@ -300,6 +350,38 @@ def quads_moe_w4a4_gemm(a, w, n, rows=None, r=None, sel=None, offsets=None, row_
         _ptr(sel) if k else None, k, _ptr(w_nib), _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e,
         n, epilogue, out_dtype, _ptr(out), _ptr(ws), nws, _stream(dev)))
     return out
+
+
+def quads_moe_w4a4_gemm_amax_groups(rows, kd, k, e, n):
+    """Partial-maximum slots of a SwiGLU GEMM call of these sizes (0: sizes rejected)."""
+    return int(lib().quads_moe_w4a4_gemm_amax_groups(rows, kd, k, e, n))
+
+
+def quads_moe_w4a4_gemm_amax(a, w, n, rows=None, r=None, sel=None, offsets=None,
+                             row_token=None, out=None, amax_part=None):
+    """SwiGLU W4A4 GEMM (bf16 h [rows, N/2]) that also writes the partial maxima of |h|.
+    Returns (h, amax_part uint32 [groups])."""
+    a_nib, a_scale, a_ts = a
+    w_nib, w_scale, w_ts = w
+    e = w_nib.shape[0]
+    kd = a_nib.shape[1] * 2
+    if rows is None:
+        rows = row_token.shape[0] if row_token is not None else a_nib.shape[0]
+    k = 0 if r is None else int(sel.shape[0])
+    dev = a_nib.device
+    if out is None:
+        out = torch.empty((rows, n // 2), dtype=torch.int16, device=dev)
+    if amax_part is None:
+        groups = max(quads_moe_w4a4_gemm_amax_groups(rows, kd, k, e, n), 1)
+        amax_part = torch.empty(groups, dtype=torch.int32, device=dev)
+    ws, nws = _ws(lib().quads_moe_w4a4_gemm_ws(rows, kd, k, e, n), dev)
+    rn, rs, rt = r if r is not None else (None, None, None)
+    _check("quads_moe_w4a4_gemm_amax", lib().quads_moe_w4a4_gemm_amax(
+        _ptr(a_nib), _ptr(a_scale), _ptr(a_ts), _ptr(row_token), rows, kd,
+        _ptr(rn) if k else None, _ptr(rs) if k else None, _ptr(rt) if k else None,
+        _ptr(sel) if k else None, k, _ptr(w_nib), _ptr(w_scale), _ptr(w_ts), _ptr(offsets), e,
+        n, _ptr(out), _ptr(amax_part), int(amax_part.numel()), _ptr(ws), nws, _stream(dev)))
+    return out, amax_part
 
 
 def quads_moe_w4a4_gemm_rowscale(a, w, n, rows=None, offsets=None, row_token=None,

@@ -203,9 +203,10 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
 }
 
 // Tensor scale of segment `seg` from its partial maxima (or the caller's fixed
-// scale), computed by the whole work-group (at most 8 partials per thread,
-// loaded together) into *s_out (LDS; s_red holds one value per wave).
-__device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, int groups,
+// scale), computed by the whole work-group (sixteen partials per thread
+// loaded together, as many rounds as `groups` needs) into *s_out (LDS; s_red
+// holds one value per wave).
+__device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, int64_t groups,
                                                       const float* ts_in, int seg, float* s_out,
                                                       uint32_t* s_red) {
     const int nw = (blockDim.x + 63) >> 6;
@@ -213,15 +214,18 @@ __device__ __forceinline__ void tensor_scale_prologue(const uint32_t* partial, i
         if (threadIdx.x == 0) *s_out = ts_in[0];
         return;
     }
-    uint32_t v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-        const int i = threadIdx.x + q * blockDim.x;
-        v[q] = i < groups ? partial[(int64_t)seg * groups + i] : 0u;
-    }
+    const uint32_t* p = partial + (int64_t)seg * groups;
     uint32_t m = 0;
+    for (int64_t b = 0; b < groups; b += 16 * (int64_t)blockDim.x) {
+        uint32_t v[16];
 #pragma unroll
-    for (int q = 0; q < 8; ++q) m = v[q] > m ? v[q] : m;
+        for (int q = 0; q < 16; ++q) {
+            const int64_t i = b + threadIdx.x + q * (int64_t)blockDim.x;
+            v[q] = i < groups ? p[i] : 0u;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) m = v[q] > m ? v[q] : m;
+    }
     m = wave_max_u32(m);
     if ((threadIdx.x & 63) == 0) s_red[threadIdx.x >> 6] = m;
     __syncthreads();

@@ -163,8 +163,10 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     __shared__ int s_res[4];
     int e, m0, mend;
     if (!find_tile_bm(g.offsets, g.E, g.rows, blockIdx.y, kBM, s_scan, s_res, &e, &m0, &mend,
-                      g.dec_rows))
+                      g.dec_rows)) {
+        if (g.amax) amax_group_none(g);
         return;
+    }
     bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = blockIdx.x * (swiglu ? kBN / 2 : kBN);
@@ -255,6 +257,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
     const float s_ta = tensor_scale_a(g), s_tw = g.w_ts[e];
     const float ca = s_ta * s_tw;
     const float cr = g.k > 0 ? g.r_ts[0] * s_tw : 0.0f;
+    uint32_t hmax = 0;                               // largest |h| stored (SwiGLU)
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
@@ -274,8 +277,9 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
                 if (feat < g.N / 2) {
                     const float gt = y[0], up = y[1];
                     const float hval = silu_mul(gt, up);
-                    ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] =
-                        (uint16_t)bf16_rne_from_f32(hval);
+                    const uint32_t hb = bf16_rne_from_f32(hval);
+                    ((uint16_t*)g.out)[(int64_t)prow * (g.N / 2) + feat] = (uint16_t)hb;
+                    hmax = umax32(hmax, hb & 0x7FFFu);
                 }
             } else {
 #pragma unroll
@@ -291,6 +295,7 @@ __global__ __launch_bounds__(256) void k_gemm_w4a4(GemmArgs g) {
             }
         }
     }
+    if (swiglu && g.amax) amax_group_store(g, hmax, reinterpret_cast<uint32_t*>(sA));
 }
 
 
@@ -615,8 +620,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
     if (!find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows,
-                            g.tail_rows))
+                            g.tail_rows)) {
+        if (g.amax) amax_group_none(g);
         return;
+    }
     bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
@@ -687,7 +694,9 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v2(GemmArgs g, int nt_n,
     }
 
     // epilogue
-    epilogue<kEpi>(g, acc, cscale * g.w_ts[e], m0, mend, f0, wm, wn, mact, lane);
+    const uint32_t hmax = epilogue<kEpi>(g, acc, cscale * g.w_ts[e], m0, mend, f0, wm, wn, mact,
+                                         lane);
+    if (swiglu && g.amax) amax_group_store(g, hmax, reinterpret_cast<uint32_t*>(ws_s));
 }
 
 }  // namespace v2
@@ -705,46 +714,19 @@ extern "C" size_t quads_moe_w4a4_gemm_ws(int64_t rows, int64_t K, int32_t k, int
     return gemm_v3_gather_ws(K, k, E, N);
 }
 
-// Both entry points: a_ts_rows is null (one tensor scale a_ts[0]) or the
-// per-row scales [Ta] (then a_ts == a_ts_rows and k == 0).
-static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
-                     const float* a_ts_rows, int sel_per_expert, const int32_t* row_token,
-                     int64_t rows, int64_t K,
-                     const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
-                     const int32_t* sel, int32_t k, const uint8_t* w_nib,
-                     const uint8_t* w_scale, const float* w_ts, const int32_t* offsets,
-                     int32_t E, int64_t N, int epilogue, int out_dtype, void* out, void* ws,
-                     size_t ws_bytes, void* stream) {
-    (void)ws;
-    if (epilogue != QUADS_EPI_NONE && epilogue != QUADS_EPI_SWIGLU) return QUADS_EINVAL;
-    if (out_dtype != QUADS_OUT_F32 && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
-    if (epilogue == QUADS_EPI_SWIGLU && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
-    if (rows < 0 || rows >= ((int64_t)1 << 31) || K <= 0 || K % kBlock || K >= ((int64_t)1 << 30))
-        return QUADS_ESHAPE;
-    if (k < 0 || k % kBlock || k > K) return QUADS_ESHAPE;
-    if (E < 1 || E > kGemmMaxE || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
-    if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
-    if (offsets == nullptr && E != 1) return QUADS_EINVAL;
-    if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
-    if (!ok_ptr(a_nib) || !ok_ptr(a_scale) || !ok_ptr(a_ts) || !ok_ptr(w_nib) ||
-        !ok_ptr(w_scale) || !ok_ptr(w_ts) || !ok_ptr(out))
-        return QUADS_EINVAL;
-    if (k > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale) || !ok_ptr(r_ts) || !ok_ptr(sel)))
-        return QUADS_EINVAL;
-    const size_t need = quads_moe_w4a4_gemm_ws(rows, K, k, E, N);
-    if (ws_bytes < need || (need > 0 && !ok_ptr(ws))) return QUADS_EWORKSPACE;
-    if (rows == 0) return QUADS_OK;
-    GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
-               w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
-               out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows, sel_per_expert};
-    hipStream_t st = (hipStream_t)stream;
+// The kernels of one call, in launch order (see LaunchPlan).
+static int gemm_dispatch(GemmArgs g, void* ws, size_t ws_bytes, hipStream_t st, LaunchPlan* lp) {
+    const int64_t rows = g.rows;
+    const int64_t K = g.K, k = g.k, E = g.E, N = g.N;
+    const int epilogue = g.epilogue;
+    const int32_t* offsets = g.offsets;
     if (gemm_decode_fits(g)) {
         // few rows per expert: the decode kernel takes every expert with at
         // most kDecodeMaxRows rows, or all of them at most kDecodeAllRows
         // rows in all; when some expert may have more than it takes, the
         // tiled kernel below takes those
         g.dec_rows = rows <= kDecodeAllRows ? (int)rows : kDecodeMaxRows;
-        const int rc = launch_gemm_decode(g, st);
+        const int rc = launch_gemm_decode(g, st, lp);
         if (rc != QUADS_OK || rows <= g.dec_rows) return rc;
     }
     // one accumulator chain is short enough for the error bound: the
@@ -764,13 +746,13 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     if (tiles_v3 && g.dec_rows == 0 && offsets != nullptr && rows <= (int64_t)512 * E &&
         gemm_decode_tail_fits(g)) {
         g.tail_rows = kTailRows;
-        const int rc = launch_gemm_decode(g, st);
+        const int rc = launch_gemm_decode(g, st, lp);
         if (rc != QUADS_OK) return rc;
     }
-    if (tiles_v3) return launch_gemm_v3(g, st);
+    if (tiles_v3) return launch_gemm_v3(g, st, lp);
     if (!one_chain && gemm_v3_gather_fits(g) && ws_bytes >= gemm_v3_gather_ws(K, k, E, N) &&
         ws != nullptr)
-        return launch_gemm_v3_gather(g, ws, st);
+        return launch_gemm_v3_gather(g, ws, st, lp);
     if (tiles_v2) {
         const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + v2::BN / 2 - 1) / (v2::BN / 2)
                                                           : (N + v2::BN - 1) / v2::BN;
@@ -780,7 +762,11 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
         const int64_t nt_m = (rows + v2::BM - 1) / v2::BM + (offsets ? (big < E ? big : E) : 0);
         const int64_t grp = 2 * nt_n;
         const int64_t span = grp * v2::kXcds;
-        const dim3 grid2((unsigned)((nt_m * nt_n + span - 1) / span * span));
+        const int64_t blocks = (nt_m * nt_n + span - 1) / span * span;
+        g.amax_base = lp->blocks;
+        lp->blocks += blocks;
+        if (lp->dry) return QUADS_OK;
+        const dim3 grid2((unsigned)blocks);
         if (epilogue == QUADS_EPI_SWIGLU)
             hipLaunchKernelGGL(v2::k_gemm_w4a4_v2<QUADS_EPI_SWIGLU>, grid2, dim3(v2::kThreads), 0,
                                st, g, (int)nt_n, (int)grp);
@@ -794,6 +780,9 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
                                                           : (N + kBN - 1) / kBN;
     const int64_t big = g.dec_rows > 0 ? rows / (g.dec_rows + 1) : E;
     int64_t ntiles_m = (rows + kBM - 1) / kBM + (offsets ? (big < E ? big : E) : 0);
+    g.amax_base = lp->blocks;
+    lp->blocks += ntiles_n * ntiles_m;
+    if (lp->dry) return QUADS_OK;
     const dim3 grid((unsigned)ntiles_n, (unsigned)ntiles_m);
     if (epilogue == QUADS_EPI_SWIGLU)
         hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_SWIGLU>, grid, dim3(256), 0, st, g);
@@ -801,6 +790,55 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
         hipLaunchKernelGGL(k_gemm_w4a4<QUADS_EPI_NONE>, grid, dim3(256), 0, st, g);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
+}
+
+
+// Both entry points: a_ts_rows is null (one tensor scale a_ts[0]) or the
+// per-row scales [Ta] (then a_ts == a_ts_rows and k == 0).
+static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* a_ts,
+                     const float* a_ts_rows, int sel_per_expert, const int32_t* row_token,
+                     int64_t rows, int64_t K,
+                     const uint8_t* r_nib, const uint8_t* r_scale, const float* r_ts,
+                     const int32_t* sel, int32_t k, const uint8_t* w_nib,
+                     const uint8_t* w_scale, const float* w_ts, const int32_t* offsets,
+                     int32_t E, int64_t N, int epilogue, int out_dtype, void* out,
+                     uint32_t* amax, int64_t amax_groups, void* ws, size_t ws_bytes,
+                     void* stream) {
+    if (epilogue != QUADS_EPI_NONE && epilogue != QUADS_EPI_SWIGLU) return QUADS_EINVAL;
+    if (out_dtype != QUADS_OUT_F32 && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (epilogue == QUADS_EPI_SWIGLU && out_dtype != QUADS_OUT_BF16) return QUADS_EINVAL;
+    if (rows < 0 || rows >= ((int64_t)1 << 31) || K <= 0 || K % kBlock || K >= ((int64_t)1 << 30))
+        return QUADS_ESHAPE;
+    if (k < 0 || k % kBlock || k > K) return QUADS_ESHAPE;
+    if (E < 1 || E > kGemmMaxE || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
+    if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
+    if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
+    if (!ok_ptr(a_nib) || !ok_ptr(a_scale) || !ok_ptr(a_ts) || !ok_ptr(w_nib) ||
+        !ok_ptr(w_scale) || !ok_ptr(w_ts) || !ok_ptr(out))
+        return QUADS_EINVAL;
+    if (k > 0 && (!ok_ptr(r_nib) || !ok_ptr(r_scale) || !ok_ptr(r_ts) || !ok_ptr(sel)))
+        return QUADS_EINVAL;
+    const size_t need = quads_moe_w4a4_gemm_ws(rows, K, k, E, N);
+    if (ws_bytes < need || (need > 0 && !ok_ptr(ws))) return QUADS_EWORKSPACE;
+    if (amax != nullptr && (epilogue != QUADS_EPI_SWIGLU || !ok_ptr(amax) || amax_groups < 1))
+        return QUADS_EINVAL;
+    if (rows == 0) return QUADS_OK;
+    GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
+               w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
+               out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows, sel_per_expert};
+    hipStream_t st = (hipStream_t)stream;
+    if (amax != nullptr) {
+        // the work-groups of every launch of the call, one slot each
+        LaunchPlan dry{true, 0};
+        const int rc = gemm_dispatch(g, ws, ws_bytes, st, &dry);
+        if (rc != QUADS_OK) return rc;
+        if (dry.blocks > amax_groups) return QUADS_EWORKSPACE;
+        g.amax = amax;
+        g.amax_end = amax_groups;
+    }
+    LaunchPlan lp{false, 0};
+    return gemm_dispatch(g, ws, ws_bytes, st, &lp);
 }
 
 extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
@@ -812,8 +850,52 @@ extern "C" int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale,
                                    int64_t N, int epilogue, int out_dtype, void* out, void* ws,
                                    size_t ws_bytes, void* stream) {
     return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 0, row_token, rows, K, r_nib, r_scale, r_ts,
-                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out, ws,
-                     ws_bytes, stream);
+                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out,
+                     nullptr, 0, ws, ws_bytes, stream);
+}
+
+// Partial-maximum slots of a SwiGLU call of these sizes: the work-groups of
+// its launches, the largest over a call with or without offsets (E == 1)
+// and with or without a workspace.
+extern "C" int64_t quads_moe_w4a4_gemm_amax_groups(int64_t rows, int64_t K, int32_t k, int32_t E,
+                                                   int64_t N) {
+    if (rows < 1 || rows >= ((int64_t)1 << 31) || K <= 0 || K % kBlock ||
+        K >= ((int64_t)1 << 30) || k < 0 || k % kBlock || k > K || E < 1 || E > kGemmMaxE ||
+        N < 2 || N % 2 || N >= ((int64_t)1 << 30))
+        return 0;
+    static const int32_t dummy_offsets[1] = {0};
+    char dummy_ws[1];
+    int64_t most = 0;
+    for (int with_offsets = 0; with_offsets < 2; ++with_offsets) {
+        if (!with_offsets && E != 1) continue;
+        for (int with_ws = 0; with_ws < 2; ++with_ws) {
+            GemmArgs g{};
+            g.rows = rows; g.K = (int)K; g.k = (int)k; g.E = (int)E; g.N = (int)N;
+            g.epilogue = QUADS_EPI_SWIGLU; g.out_bf16 = 1;
+            g.offsets = with_offsets ? dummy_offsets : nullptr;
+            LaunchPlan dry{true, 0};
+            const size_t wsb = with_ws ? quads_moe_w4a4_gemm_ws(rows, K, k, E, N) : 0;
+            if (gemm_dispatch(g, with_ws ? dummy_ws : nullptr, wsb, nullptr, &dry) != QUADS_OK)
+                continue;
+            most = dry.blocks > most ? dry.blocks : most;
+        }
+    }
+    return most;
+}
+
+extern "C" int quads_moe_w4a4_gemm_amax(const uint8_t* a_nib, const uint8_t* a_scale,
+                                        const float* a_ts, const int32_t* row_token, int64_t rows,
+                                        int64_t K, const uint8_t* r_nib, const uint8_t* r_scale,
+                                        const float* r_ts, const int32_t* sel, int32_t k,
+                                        const uint8_t* w_nib, const uint8_t* w_scale,
+                                        const float* w_ts, const int32_t* offsets, int32_t E,
+                                        int64_t N, void* out, uint32_t* amax_part,
+                                        int64_t amax_groups, void* ws, size_t ws_bytes,
+                                        void* stream) {
+    if (!ok_ptr(amax_part)) return QUADS_EINVAL;
+    return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 0, row_token, rows, K, r_nib, r_scale, r_ts,
+                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, QUADS_EPI_SWIGLU,
+                     QUADS_OUT_BF16, out, amax_part, amax_groups, ws, ws_bytes, stream);
 }
 
 extern "C" int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t* a_scale,
@@ -826,7 +908,7 @@ extern "C" int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t*
     if (!ok_ptr(a_ts_rows)) return QUADS_EINVAL;
     return gemm_w4a4(a_nib, a_scale, a_ts_rows, a_ts_rows, 0, row_token, rows, K, nullptr, nullptr,
                      nullptr, nullptr, 0, w_nib, w_scale, w_ts, offsets, E, N, epilogue,
-                     out_dtype, out, ws, ws_bytes, stream);
+                     out_dtype, out, nullptr, 0, ws, ws_bytes, stream);
 }
 
 extern "C" int quads_moe_w4a4_gemm_sel_experts(const uint8_t* a_nib, const uint8_t* a_scale,
@@ -841,6 +923,6 @@ extern "C" int quads_moe_w4a4_gemm_sel_experts(const uint8_t* a_nib, const uint8
     if (!ok_ptr(offsets)) return QUADS_EINVAL;
     if (k > 0 && !ok_ptr(r_ts)) return QUADS_EINVAL;
     return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 1, nullptr, rows, K, r_nib, r_scale, r_ts,
-                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out, ws,
-                     ws_bytes, stream);
+                     sel, k, w_nib, w_scale, w_ts, offsets, E, N, epilogue, out_dtype, out,
+                     nullptr, 0, ws, ws_bytes, stream);
 }

@@ -217,7 +217,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             const int y = __shfl_up(inc, off, 64);
             if (lane >= off) inc += y;
         }
-        if (rank >= __builtin_amdgcn_readlane(inc, 63)) return;   // uniform: past the last
+        if (rank >= __builtin_amdgcn_readlane(inc, 63)) {         // uniform: past the last
+            if (g.amax) amax_group_none(g);
+            return;
+        }
         int found = -1, part = 0;
         if (rank >= inc - na && rank < inc) {                       // exactly one lane
             int rr = rank - (inc - na);
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         p0 = g.offsets[e + 1] - taken + kDecodeMaxRows * __builtin_amdgcn_readlane(part, src);
         cnt = min(g.offsets[e + 1] - p0, kDecodeMaxRows);
     } else if (rank > 0 || cnt <= 0 || cnt > g.dec_rows) {
+        if (g.amax) amax_group_none(g);
         return;                                       // one expert, all rows
     }
     bind_expert(g, e);
@@ -282,6 +286,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
         s_sel[wave][lane] = sel_lo;
     }
 
+    uint32_t hmax = 0;                                // largest |h| stored (SwiGLU)
     for (int c0 = 0; c0 < cnt; c0 += kRows) {
         const bool rv = c0 + r < cnt;
         const int p = p0 + c0 + r;
@@ -484,12 +489,16 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
                     uint16_t* o = (uint16_t*)g.out + (int64_t)p * nh + feat;
                     if (feat + 3 < nh && (nh & 3) == 0) {
                         *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                        hmax = umax32(hmax, umax32(bf16x2_mag_max(p01), bf16x2_mag_max(p23)));
                     } else {
                         const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu,
                                                 p23 >> 16};
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                            if (feat + u < nh) {
+                                o[u] = (uint16_t)hb[u];
+                                hmax = umax32(hmax, hb[u] & 0x7FFFu);
+                            }
                     }
                 } else {
 #pragma unroll
@@ -526,6 +535,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             }
         }
     }
+    if (swiglu && g.amax) amax_group_store(g, hmax, reinterpret_cast<uint32_t*>(&swin[0][0][0][0]));
 }
 
 }  // namespace dec
@@ -548,10 +558,13 @@ bool gemm_decode_fits(const GemmArgs& g) {
            (int64_t)g.N * g.K / 2 < ((int64_t)1 << 31);
 }
 
-int launch_gemm_decode(const GemmArgs& g, hipStream_t st) {
+int launch_gemm_decode(GemmArgs g, hipStream_t st, LaunchPlan* lp) {
     const int64_t slabs = g.epilogue == QUADS_EPI_SWIGLU ? (g.N / 2 + 63) / 64 : (g.N + 127) / 128;
-    const dim3 grid((unsigned)(slabs * 8 * ((dec::decode_units_max(g) + 7) / 8))),
-        block(dec::kThreads);
+    const int64_t blocks = slabs * 8 * ((dec::decode_units_max(g) + 7) / 8);
+    g.amax_base = lp->blocks;
+    lp->blocks += blocks;
+    if (lp->dry) return QUADS_OK;
+    const dim3 grid((unsigned)blocks), block(dec::kThreads);
     const int nch = g.K / dec::kChunk;
     const bool ring3 = nch % 4 != 0 && nch % 3 == 0;
     const bool sw = g.epilogue == QUADS_EPI_SWIGLU;

@@ -35,7 +35,53 @@ struct GemmArgs {
     // first 256 (its tail) to the decode kernel, so that the 256-row tiled
     // kernels run one full tile for it instead of two part-filled ones.
     int tail_rows;
+    // Non-null (SwiGLU only): each work-group of the launch writes the
+    // largest |h| it stores (bf16 magnitude bits, 0 if none) to
+    // amax[amax_base + its linear id]; work-group 0 also zeroes amax
+    // [amax_base + grid size, amax_end), the slots past the call's last
+    // launch, so that every one of the caller's amax_end slots is written.
+    uint32_t* amax;
+    int64_t amax_base, amax_end;
 };
+
+__device__ __forceinline__ uint32_t umax32(uint32_t a, uint32_t b) { return a > b ? a : b; }
+
+// The magnitudes of two packed bf16 values, the larger one.
+__device__ __forceinline__ uint32_t bf16x2_mag_max(uint32_t p) {
+    const uint32_t lo = p & 0x7FFFu, hi = (p >> 16) & 0x7FFFu;
+    return lo > hi ? lo : hi;
+}
+
+// One partial maximum per work-group (see GemmArgs::amax): the threads'
+// values m folded through s_amax, one word per wave of LDS that the
+// work-group no longer reads (a barrier comes first).  Every thread of the
+// work-group calls it.
+__device__ __forceinline__ void amax_group_store(const GemmArgs& g, uint32_t m,
+                                                 uint32_t* s_amax) {
+    const int64_t id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
+    for (int64_t i = g.amax_base + nblk + threadIdx.x; id == 0 && i < g.amax_end; i += blockDim.x)
+        g.amax[i] = 0u;
+    m = wave_max_u32(m);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s_amax[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int i = 0; i < (int)((blockDim.x + 63) >> 6); ++i) r = s_amax[i] > r ? s_amax[i] : r;
+        g.amax[g.amax_base + id] = r;
+    }
+}
+
+// The same for a work-group that stores nothing and leaves early (called by
+// every thread; no barrier).
+__device__ __forceinline__ void amax_group_none(const GemmArgs& g) {
+    const int64_t id = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+    const int64_t nblk = (int64_t)gridDim.x * gridDim.y;
+    for (int64_t i = g.amax_base + nblk + threadIdx.x; id == 0 && i < g.amax_end; i += blockDim.x)
+        g.amax[i] = 0u;
+    if (threadIdx.x == 0) g.amax[g.amax_base + id] = 0u;
+}
 
 // Rows at the end of an n-row expert that belong to the decode kernel.
 __host__ __device__ inline int expert_tail(int n, int tail_rows) {
@@ -205,7 +251,8 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, in
 template <bool kFull>
 __device__ __forceinline__ void swiglu_store(const GemmArgs& g, const f32x16 acc[4][2], float ca,
                                              int m0, int mend, int f0, int wm, int wn, int mact,
-                                             int lane, bool* need) {
+                                             int lane, bool* need, uint32_t* mx) {
+    uint32_t m = 0;
     const int prow_l = m0 + wm * 128 + (lane & 31);
     const int nq = 4 * (lane >> 5);
     bool nd = false;
@@ -236,31 +283,38 @@ __device__ __forceinline__ void swiglu_store(const GemmArgs& g, const f32x16 acc
             uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
             if (feat + 3 < nh && (nh & 3) == 0) {
                 *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                m = umax32(m, umax32(bf16x2_mag_max(p01), bf16x2_mag_max(p23)));
             } else {
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
-                    if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                    if (feat + u < nh) {
+                        o[u] = (uint16_t)hb[u];
+                        m = umax32(m, hb[u] & 0x7FFFu);
+                    }
             }
         }
     }
     *need = nd;
+    *mx = m;
 }
 
 // Epilogue of a 256 x 256 tile: acc scaled by ca; SwiGLU to bf16 or plain
 // fp32 / bf16 stores, four consecutive features per lane.
+// Returns the largest |h| the thread stored (SwiGLU; else 0).
 template <int kEpi>
-__device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][2], float ca,
-                                         int m0, int mend, int f0, int wm, int wn, int mact,
-                                         int lane) {
+__device__ __forceinline__ uint32_t epilogue(const GemmArgs& g, const f32x16 acc[4][2], float ca,
+                                             int m0, int mend, int f0, int wm, int wn, int mact,
+                                             int lane) {
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     if (swiglu) {
         // rare: a gate below -44.36 somewhere in the wave's tile -- the same
         // outputs again with the full form (equal values elsewhere)
         bool need;
-        swiglu_store<false>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need);
+        uint32_t m;
+        swiglu_store<false>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need, &m);
         if (__ballot(need) != 0ull)
-            swiglu_store<true>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need);
-        return;
+            swiglu_store<true>(g, acc, ca, m0, mend, f0, wm, wn, mact, lane, &need, &m);
+        return m;
     }
     const int prow_l = m0 + wm * 128 + (lane & 31);
     const int nq = 4 * (lane >> 5);
@@ -307,6 +361,7 @@ __device__ __forceinline__ void epilogue(const GemmArgs& g, const f32x16 acc[4][
             }
         }
     }
+    return 0u;
 }
 
 
@@ -350,18 +405,26 @@ constexpr int kSingleChainMax = 1152;
 // Tiled kernel for many rows per expert (gemm_v3.hip): K a multiple of 128,
 // at most kCapMaxV3 compensation channels.
 constexpr int kCapMaxV3 = 256;
+// The launches of one GEMM call.  `dry`: count their work-groups without
+// launching; otherwise each launch takes the next `blocks` as its
+// GemmArgs::amax_base (the partial-maximum slots of the call, in launch
+// order) and adds its work-group count.
+struct LaunchPlan {
+    bool dry;
+    int64_t blocks;
+};
 bool gemm_v3_fits(const GemmArgs& g);
-int launch_gemm_v3(const GemmArgs& g, hipStream_t st);
+int launch_gemm_v3(GemmArgs g, hipStream_t st, LaunchPlan* lp);
 // Long chains with k above kCapMaxV3 (k % 128 == 0, one shared selection):
 // the tiled kernel with W[:, S] gathered into `ws` (gemm_v3_gather_ws bytes).
 size_t gemm_v3_gather_ws(int64_t K, int64_t k, int64_t E, int64_t N);
 bool gemm_v3_gather_fits(const GemmArgs& g);
-int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st);
+int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st, LaunchPlan* lp);
 constexpr int kDecodeMaxRows = 128;
 constexpr int kDecodeAllRows = 512;
 bool gemm_decode_fits(const GemmArgs& g);
 bool gemm_decode_tail_fits(const GemmArgs& g);
-int launch_gemm_decode(const GemmArgs& g, hipStream_t st);
+int launch_gemm_decode(GemmArgs g, hipStream_t st, LaunchPlan* lp);
 // Tail rows the decode kernel takes from experts just above 256 rows.
 constexpr int kTailRows = 64;
 

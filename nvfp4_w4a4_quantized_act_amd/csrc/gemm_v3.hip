@@ -230,8 +230,9 @@ __device__ __forceinline__ void zero_set(f32x4 acc[2][8]) {
         for (int n = 0; n < 8; ++n) acc[f][n] = (f32x4){0.f, 0.f, 0.f, 0.f};
 }
 
+// Returns the largest |h| the thread stored (SwiGLU; else 0).
 template <int kEpi, int MACT, bool LATE, bool kGather>
-__device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
+__device__ __forceinline__ uint32_t run_tile(const GemmArgs& g, char* wbuf, _Float16* cap,
                                          char* swin, const int* s_sel, const int* s_cs,
                                          const uint32_t* s_capd, const Ctx& x,
                                          int wr, int wh, int64_t wfull,
@@ -500,7 +501,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     }
 
     // epilogue: y = T s_tA s_tW + X s_tR s_tW
-    if (MACT == 0) return;
+    if (MACT == 0) return 0u;
     const float cr = comp ? s_tr * s_tw : 0.0f;
     const int r = lane & 15, q = lane >> 4;
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
@@ -508,9 +509,11 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
     if (swiglu) {
         const int nh = g.N / 2;
         bool need = false;
+        uint32_t hmax = 0;                             // largest |h| of the last pass
 #pragma unroll
         for (int pass = 0; pass < 2; ++pass) {
             if (pass == 1 && __ballot(need) == 0ull) break;
+            hmax = 0;
 #pragma unroll
             for (int f = 0; f < MACT; ++f) {
                 const int prow = prow0 + 16 * f;
@@ -535,16 +538,20 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
                     uint16_t* o = (uint16_t*)g.out + (int64_t)prow * nh + feat;
                     if (feat + 3 < nh && (nh & 3) == 0) {
                         *reinterpret_cast<uint2*>(o) = make_uint2(p01, p23);
+                        hmax = umax32(hmax, umax32(bf16x2_mag_max(p01), bf16x2_mag_max(p23)));
                     } else {
                         const uint32_t hb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
 #pragma unroll
                         for (int u = 0; u < 4; ++u)
-                            if (feat + u < nh) o[u] = (uint16_t)hb[u];
+                            if (feat + u < nh) {
+                                o[u] = (uint16_t)hb[u];
+                                hmax = umax32(hmax, hb[u] & 0x7FFFu);
+                            }
                     }
                 }
             }
         }
-        return;
+        return hmax;
     }
 #pragma unroll
     for (int f = 0; f < MACT; ++f) {
@@ -582,6 +589,7 @@ __device__ __forceinline__ void run_tile(const GemmArgs& g, char* wbuf, _Float16
             }
         }
     }
+    return 0u;
 }
 
 template <int kEpi, bool kGather>
@@ -601,8 +609,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
     const int tile_m = tile / nt_n, tile_n = tile - tile_m * nt_n;
     int e, m0, mend;
     if (!v2::find_tile_wave<BM>(g.offsets, g.E, g.rows, tile_m, &e, &m0, &mend, g.dec_rows,
-                                g.tail_rows))
+                                g.tail_rows)) {
+        if (g.amax) amax_group_none(g);
         return;
+    }
     bind_expert(g, e);
     constexpr bool swiglu = kEpi == QUADS_EPI_SWIGLU;
     const int f0 = tile_n * (swiglu ? BN / 2 : BN);
@@ -690,18 +700,20 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_v3(GemmArgs g, int nt_n,
 
     int mact = (mend - (m0 + 32 * wave) + 15) / 16;
     mact = __builtin_amdgcn_readfirstlane(mact < 0 ? 0 : (mact > 2 ? 2 : mact));
+    uint32_t hmax = 0;
     switch (mact + (wave >= 4 ? 4 : 0)) {
 #define QUADS_V3_TILE(M, L)                                                                     \
     case M + (L ? 4 : 0):                                                                       \
-        run_tile<kEpi, M, L, kGather>(g, wbuf, cap, swin + 3072 * wave, s_sel, s_cs, s_capd, x,  \
-                                      wr, wh, wfull, kc, wave,                                  \
-                                      lane, src, m0, mend, f0, e);                              \
+        hmax = run_tile<kEpi, M, L, kGather>(g, wbuf, cap, swin + 3072 * wave, s_sel, s_cs,     \
+                                             s_capd, x, wr, wh, wfull, kc, wave, lane, src, m0, \
+                                             mend, f0, e);                                      \
         break;
         QUADS_V3_TILE(2, false) QUADS_V3_TILE(1, false) QUADS_V3_TILE(2, true)
         QUADS_V3_TILE(1, true) QUADS_V3_TILE(0, true)
         default: QUADS_V3_TILE(0, false)
 #undef QUADS_V3_TILE
     }
+    if (swiglu && g.amax) amax_group_store(g, hmax, s_capd);
 }
 
 }  // namespace v3
@@ -743,7 +755,7 @@ __global__ __launch_bounds__(256) void k_gather_wsel(const uint8_t* __restrict__
 }
 
 template <bool kGather>
-int launch_tiles(const GemmArgs& g, hipStream_t st) {
+int launch_tiles(GemmArgs g, hipStream_t st, LaunchPlan* lp) {
     const bool sw = g.epilogue == QUADS_EPI_SWIGLU;
     const int64_t nt_n = sw ? (g.N / 2 + BN / 2 - 1) / (BN / 2) : (g.N + BN - 1) / BN;
     // M-tiles: at most rows / BM + one partial tile per expert that has tiles
@@ -754,6 +766,9 @@ int launch_tiles(const GemmArgs& g, hipStream_t st) {
     const int64_t span = grp * v2::kXcds;
     const int64_t blocks = (nt_m * nt_n + span - 1) / span * span;
     if (blocks >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
+    g.amax_base = lp->blocks;
+    lp->blocks += blocks;
+    if (lp->dry) return QUADS_OK;
     const dim3 grid((unsigned)blocks);
     if (sw)
         hipLaunchKernelGGL((k_gemm_w4a4_v3<QUADS_EPI_SWIGLU, kGather>), grid, dim3(kThreads), 0, st,
@@ -767,7 +782,9 @@ int launch_tiles(const GemmArgs& g, hipStream_t st) {
 
 }  // namespace v3
 
-int launch_gemm_v3(const GemmArgs& g, hipStream_t st) { return v3::launch_tiles<false>(g, st); }
+int launch_gemm_v3(GemmArgs g, hipStream_t st, LaunchPlan* lp) {
+    return v3::launch_tiles<false>(g, st, lp);
+}
 
 size_t gemm_v3_gather_ws(int64_t K, int64_t k, int64_t E, int64_t N) {
     const bool shape = K % v3::BK == 0 && K <= v3::BK * v3::kMaxChunksV3 && k > kCapMaxV3 &&
@@ -781,14 +798,15 @@ bool gemm_v3_gather_fits(const GemmArgs& g) {
            gemm_v3_gather_ws(g.K, g.k, g.E, g.N) > 0;
 }
 
-int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st) {
+int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st, LaunchPlan* lp) {
     const int64_t nrows = (int64_t)g.E * g.N;
     const int64_t threads = nrows * (g.k / 8);
+    if (lp->dry) return v3::launch_tiles<true>(g, st, lp);
     hipLaunchKernelGGL(v3::k_gather_wsel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                        g.w_nib, g.w_scale, g.sel, g.K, g.k, nrows, static_cast<_Float16*>(ws));
     QUADS_CHECK_LAUNCH();
     g.w_sel = static_cast<const _Float16*>(ws);
-    return v3::launch_tiles<true>(g, st);
+    return v3::launch_tiles<true>(g, st, lp);
 }
 
 }  // namespace quads

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restri
     __shared__ float s_st;
     __shared__ uint32_t s_red[2];
     const int seg = blockIdx.x;
-    tensor_scale_prologue(partial, groups, ts_in, seg, &s_st, s_red);   // groups <= 8 * 128
+    tensor_scale_prologue(partial, groups, ts_in, seg, &s_st, s_red);
     __syncthreads();
     const float s_t = s_st;
     if (threadIdx.x == 0) ts_out[seg] = s_t;
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256) void k_quantize_bf16(
     if (kFold) {
         __shared__ float s_st;
         __shared__ uint32_t s_red[4];
-        tensor_scale_prologue(table, groups, ts_in, 0, &s_st, s_red);     // groups <= 8 * 256
+        tensor_scale_prologue(table, groups, ts_in, 0, &s_st, s_red);
         __syncthreads();
         s_t = s_st;
         build_threshold_table(s_t, reinterpret_cast<uint32_t(*)[8]>(s_tab), true);
@@ -372,6 +372,31 @@ extern "C" int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, con
     const int qg = quant_grid(n / kBlock), qr = resident_groups(k_quantize_bf16<false, true>);
     hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < qr ? qg : qr, 1), dim3(256), 0, s,
                        x, n, ts_out, partial, nib, scale, (uint16_t*)nullptr, 0, ts_in);
+    QUADS_CHECK_LAUNCH();
+    return QUADS_OK;
+}
+
+// The dynamic-scale quantizer with max|x| from a producer's partial maxima
+// (bf16 magnitude bits, e.g. quads_moe_w4a4_gemm_amax): one launch, every
+// work-group folding them into the tensor scale itself.
+extern "C" int quads_nvfp4_quantize_partials(const uint16_t* x, int64_t M, int64_t K,
+                                             const uint32_t* amax_part, int64_t groups,
+                                             uint8_t* nib, uint8_t* scale, float* ts_out,
+                                             void* stream) {
+    if (M < 0 || K <= 0 || K % kBlock) return QUADS_ESHAPE;
+    if (groups < 1 || groups >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
+    if (!ok_ptr(ts_out) || !ok_ptr(amax_part)) return QUADS_EINVAL;
+    if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale))) return QUADS_EINVAL;
+    hipStream_t s = (hipStream_t)stream;
+    if (M == 0) {
+        hipLaunchKernelGGL(k_fill_f32, dim3(1), dim3(64), 0, s, ts_out, 1, 0.0f);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
+    }
+    const int64_t n = M * K;
+    const int qg = quant_grid(n / kBlock), qr = resident_groups(k_quantize_bf16<false, true>);
+    hipLaunchKernelGGL((k_quantize_bf16<false, true>), dim3(qg < qr ? qg : qr, 1), dim3(256), 0, s,
+                       x, n, ts_out, amax_part, nib, scale, (uint16_t*)nullptr, (int)groups);
     QUADS_CHECK_LAUNCH();
     return QUADS_OK;
 }

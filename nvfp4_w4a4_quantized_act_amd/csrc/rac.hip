@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void k_rac_pass1(
     __shared__ float s_r[kTileRows / 2][kP1Cols + 4];  // one half of the chunk at a time
     __shared__ float s_st;
     __shared__ uint32_t s_red[4];
-    tensor_scale_prologue(partial, groups, nullptr, 0, &s_st, s_red);   // groups <= 8 * 256
+    tensor_scale_prologue(partial, groups, nullptr, 0, &s_st, s_red);
     __syncthreads();
     const float s_t = s_st;
     build_threshold_table(s_t, s_tab, true);
@@ -978,9 +978,12 @@ static int rac_check_args(const uint16_t* x, int64_t M, int64_t K, int32_t k, ui
 
 // The launches of quads_rac_quantize once the arguments are checked; `ws`
 // holds at least quads_rac_quantize_ws(M, K, k) bytes of device memory.
+// With amax_part, max|x| comes from those `part_groups` partial maxima
+// instead of a max pass over x.
 static int rac_run(const uint16_t* x, int64_t M, int64_t K, int32_t k, uint8_t* nib,
                    uint8_t* scale, float* ts, int32_t* sel, uint8_t* r_nib, uint8_t* r_scale,
-                   float* r_ts, double* score_out, void* ws, hipStream_t s) {
+                   float* r_ts, double* score_out, void* ws, hipStream_t s,
+                   const uint32_t* amax_part = nullptr, int64_t part_groups = 0) {
     if (M == 0) {
         launch_fill_f32(ts, 1, 0.0f, s);
         launch_fill_f32(r_ts, 1, 0.0f, s);
@@ -999,16 +1002,21 @@ static int rac_run(const uint16_t* x, int64_t M, int64_t K, int32_t k, uint8_t* 
         return QUADS_OK;
     }
     RacWs w = rac_ws_layout((char*)ws, M, K);
-    const int groups = amax_groups(M * K);
-    launch_amax_partial(x, M * K, 1, w.partial, groups, s);
-    QUADS_CHECK_LAUNCH();
+    const uint32_t* partial = amax_part;
+    int groups = (int)part_groups;
+    if (partial == nullptr) {
+        groups = amax_groups(M * K);
+        launch_amax_partial(x, M * K, 1, w.partial, groups, s);
+        QUADS_CHECK_LAUNCH();
+        partial = w.partial;
+    }
     const bool want_scores = k > 0 || score_out != nullptr;
     const int64_t c0 = (M + kTileRows - 1) / kTileRows;
     const int64_t ctiles = (K + kP1Cols - 1) / kP1Cols;
     int64_t gx = 2048 / ctiles;
     gx = gx < 1 ? 1 : (gx > c0 ? c0 : gx);
     hipLaunchKernelGGL(k_rac_pass1, dim3((unsigned)gx, (unsigned)ctiles), dim3(256), 0, s, x, M,
-                       (int)K, w.partial, groups, ts, nib, scale,
+                       (int)K, partial, groups, ts, nib, scale,
                        want_scores ? w.pa : nullptr, want_scores ? w.ca : nullptr);
     QUADS_CHECK_LAUNCH();
     if (!want_scores) {                            // neither S nor the scores are wanted
@@ -1056,6 +1064,22 @@ extern "C" int quads_rac_quantize(const uint16_t* x, int64_t M, int64_t K, int32
     if (ws_bytes < quads_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
     return rac_run(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out, ws,
                    (hipStream_t)stream);
+}
+
+extern "C" int quads_rac_quantize_partials(const uint16_t* x, int64_t M, int64_t K, int32_t k,
+                                           const uint32_t* amax_part, int64_t groups,
+                                           uint8_t* nib, uint8_t* scale, float* ts,
+                                           int32_t* sel, uint8_t* r_nib, uint8_t* r_scale,
+                                           float* r_ts, double* score_out, void* ws,
+                                           size_t ws_bytes, void* stream) {
+    const int st = rac_check_args(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts,
+                                  score_out);
+    if (st != QUADS_OK) return st;
+    if (groups < 1 || groups >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
+    if (!ok_ptr(amax_part)) return QUADS_EINVAL;
+    if (ws_bytes < quads_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
+    return rac_run(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out, ws,
+                   (hipStream_t)stream, amax_part, groups);
 }
 
 // Workspace of quads_rac_quantize_noalloc.  In host code `scratch` names a

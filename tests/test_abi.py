@@ -21,7 +21,7 @@ def _declared():
 def test_library_exports_every_declared_symbol():
     lib = Q.lib()
     names = _declared()
-    assert "quads_moe_w4a4_gemm" in names and len(names) == 25
+    assert "quads_moe_w4a4_gemm" in names and len(names) == 29
     missing = [n for n in names if not hasattr(lib, n)]
     assert not missing, missing
     assert lib.quads_version().startswith(b"quads-mi355x")
@@ -164,6 +164,54 @@ def test_gemm_validation():
     assert call(offsets=None) == -1            # offsets required for E > 1
     assert call(sel=None) == -1                # sel required for k > 0
     assert call(out=MIS) == -1
+
+
+def test_gemm_amax_slots():
+    """Slot count of the SwiGLU GEMM with partial maxima: the work-groups of its launches,
+    worked out here from the launch rules (host logic only)."""
+    lib = Q.lib()
+    f = lib.quads_moe_w4a4_gemm_amax_groups
+    # 128-expert layer gate/up (32768 packed rows, K = 2048 + 64): the decode kernel for the
+    # experts' tails, 12 slabs x 8 x ceil(128 / 8), then the tiled kernel, 12 N-tiles x
+    # (128 + 128) M-tiles rounded up to whole spans of 2 x 12 x 8 work-groups
+    assert f(32768, 2048, 64, 128, 1536) == 12 * 8 * 16 + 3072
+    # the decode step (512 packed rows): the decode kernel alone, 128 + 512 / 128 units
+    assert f(512, 2048, 64, 128, 1536) == 12 * 8 * 17
+    # a single chain (K + k <= 1152), 256 x 256 tiles: 3 N-tiles x (5 + 4) M-tiles, rounded
+    # up to a whole span of 2 x 3 x 8 work-groups
+    assert f(4 * 256 + 64, 768, 64, 4, 384 * 2) == 48
+    assert f(0, 2048, 64, 128, 1536) == 0                 # rejected sizes
+    assert f(512, 2048, 64, 128, 1535) == 0               # SwiGLU needs even N
+    g = lib.quads_moe_w4a4_gemm_amax
+    ws = lib.quads_moe_w4a4_gemm_ws(512, 2048, 64, 128, 1536)
+
+    def call(groups=1632, amax=FAKE, k=64):
+        return g(FAKE, FAKE, FAKE, None, 512, 2048, FAKE, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE,
+                 FAKE, 128, 1536, FAKE, amax, groups, FAKE, ws, None)
+    assert call(amax=None) == -1
+    assert call(amax=MIS) == -1
+    assert call(groups=0) == -1
+    assert call(groups=1631) == -3                        # fewer slots than work-groups
+    assert call(k=8) == -2
+
+
+def test_partials_validation():
+    lib = Q.lib()
+    f = lib.quads_nvfp4_quantize_partials
+    assert f(FAKE, 4, 32, FAKE, 0, FAKE, FAKE, FAKE, None) == -2           # groups >= 1
+    assert f(FAKE, 4, 30, FAKE, 8, FAKE, FAKE, FAKE, None) == -2           # K % 16
+    assert f(FAKE, 4, 32, MIS, 8, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 4, 32, None, 8, FAKE, FAKE, FAKE, None) == -1
+    g = lib.quads_rac_quantize_partials
+    ws = lib.quads_rac_quantize_ws(64, 256, 16)
+
+    def call(groups=8, amax=FAKE, wsz=ws, k=16):
+        return g(FAKE, 64, 256, k, amax, groups, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None,
+                 FAKE, wsz, None)
+    assert call(groups=0) == -2
+    assert call(amax=None) == -1
+    assert call(k=8) == -2
+    assert call(wsz=ws - 1) == -3
 
 
 def test_gemm_rowscale_validation():
