@@ -8,8 +8,10 @@ the layer through the library:
 
   quads_rac_quantize(hidden)            NVFP4 + RAC at the gate/up input
   quads_moe_pack(topk_ids)              token -> expert packing
-  quads_moe_w4a4_gemm(gate/up, SwiGLU)  grouped W4A4 GEMM + compensation, bf16 h
-  quads_rac_quantize(h)                 NVFP4 + RAC at the down input
+  quads_moe_w4a4_gemm_amax(gate/up)     grouped W4A4 GEMM + compensation, SwiGLU bf16 h,
+                                        and per-work-group maxima of |h|
+  quads_rac_quantize_partials(h)        NVFP4 + RAC at the down input, max|h| from those
+                                        maxima (no max pass over h)
   quads_moe_w4a4_gemm(down)             grouped W4A4 GEMM + compensation, bf16 out
   quads_moe_combine                     routing-weighted sum per token
 
@@ -439,6 +441,9 @@ def main():
     nev = 7
     timers, gemm_timers = [], []
     last = {}
+    # the gate/up GEMM's partial maxima of |h|, one slot per work-group
+    amax_buf = torch.zeros(Q.quads_moe_w4a4_gemm_amax_groups(rows, H, KR, E, 2 * I),
+                           dtype=torch.int32, device=dev)
 
     def step(mode):
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(nev)] if mode else None
@@ -451,12 +456,12 @@ def main():
         mark(1)
         off, rt, pos = Q.quads_moe_pack(ids, E)
         mark(2)
-        h = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), w13q, 2 * I, rows=rows,
-                                  r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"],
-                                  offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
-                                  out_dtype=Q.OUT_BF16)
+        h, hmax = Q.quads_moe_w4a4_gemm_amax((a["nib"], a["scale"], a["ts"]), w13q, 2 * I,
+                                             rows=rows, r=(a["r_nib"], a["r_scale"], a["r_ts"]),
+                                             sel=a["sel"], offsets=off, row_token=rt,
+                                             amax_part=amax_buf)
         mark(3)
-        b = Q.quads_rac_quantize(h, KR)
+        b = Q.quads_rac_quantize_partials(h, KR, hmax)
         mark(4)
         y2 = Q.quads_moe_w4a4_gemm((b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
                                    r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"],
@@ -519,10 +524,10 @@ def main():
     la = last["a"]
 
     def gate_up_alone():
-        return Q.quads_moe_w4a4_gemm((la["nib"], la["scale"], la["ts"]), w13q, 2 * I, rows=rows,
-                                     r=(la["r_nib"], la["r_scale"], la["r_ts"]), sel=la["sel"],
-                                     offsets=last["off"], row_token=last["rt"],
-                                     epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+        return Q.quads_moe_w4a4_gemm_amax((la["nib"], la["scale"], la["ts"]), w13q, 2 * I,
+                                          rows=rows, r=(la["r_nib"], la["r_scale"], la["r_ts"]),
+                                          sel=la["sel"], offsets=last["off"],
+                                          row_token=last["rt"], amax_part=amax_buf)
     cold_step = _cold_us(torch, lambda: step(None), flush, 20)
     cold_gemm = _cold_us(torch, gate_up_alone, flush, 20)
     warm_gemm_us = _back_to_back_us(torch, gate_up_alone, 20)
@@ -549,7 +554,7 @@ def main():
         _progress("config 2 done")
         cfg5, h5 = config5(np, torch, Q, d5, x5, dev)
         _progress("config 5 done")
-        quant["down_input_131072x1536"] = quantizer_rate(np, torch, Q, h5)
+        quant["down_input_131072x1536"] = quantizer_rate(np, torch, Q, h5[0], part=h5[1])
         del h5
     del x5
     decode = comparator = per_expert = None
@@ -690,12 +695,15 @@ def rac_overhead(torch, Q, x, ids, tw, w13q, w2q, E, I, H, KR, rows, step, reps=
     """The layer with plain NVFP4 W4A4 at both GEMM inputs (k = 0: the
     quantizer, no residual pass and no compensation) beside the RAC layer
     (k = 64), both timed as `reps` back-to-back steps with no events inside."""
+    buf = torch.zeros(Q.quads_moe_w4a4_gemm_amax_groups(rows, H, 0, E, 2 * I),
+                      dtype=torch.int32, device=x.device)
+
     def plain():
         a = Q.quads_nvfp4_quantize(x)
         off, rt, pos = Q.quads_moe_pack(ids, E)
-        h = Q.quads_moe_w4a4_gemm(a, w13q, 2 * I, rows=rows, offsets=off, row_token=rt,
-                                  epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
-        b = Q.quads_nvfp4_quantize(h)
+        h, hmax = Q.quads_moe_w4a4_gemm_amax(a, w13q, 2 * I, rows=rows, offsets=off,
+                                             row_token=rt, amax_part=buf)
+        b = Q.quads_nvfp4_quantize_partials(h, hmax)
         y2 = Q.quads_moe_w4a4_gemm(b, w2q, H, rows=rows, offsets=off, out_dtype=Q.OUT_BF16)
         return Q.quads_moe_combine(y2, pos, tw, y_dtype=Q.OUT_BF16)
 
@@ -712,15 +720,18 @@ def rac_overhead(torch, Q, x, ids, tw, w13q, w2q, E, I, H, KR, rows, step, reps=
     ms_plain = timed(plain)
     ms_rac = timed(lambda: step(None))
     return {"layer_k0_ms": ms_plain, "layer_k64_ms": ms_rac, "ratio": ms_rac / ms_plain,
-            "note": "k = 0 is plain NVFP4 W4A4 (quads_nvfp4_quantize, GEMMs without "
-                    "compensation); k = 64 is the benchmark step; each timed as back-to-back "
-                    "layers"}
+            "note": "k = 0 is plain NVFP4 W4A4 (quads_nvfp4_quantize at the gate/up input, "
+                    "quads_nvfp4_quantize_partials on h with the gate/up GEMM's maxima, GEMMs "
+                    "without compensation); k = 64 is the benchmark step; each timed as "
+                    "back-to-back layers"}
 
 
-def quantizer_rate(np, torch, Q, x, reps=20):
+def quantizer_rate(np, torch, Q, x, reps=20, part=None):
     """quads_nvfp4_quantize on bf16 x [M, K]: algorithmic bytes (2 read + 0.5625
     written per element) per call, with the dynamic tensor scale (a max pass,
-    then the quantize pass) and with a given tensor scale (one pass).  Warm:
+    then the quantize pass) and with a given tensor scale (one pass); with
+    `part` (the partial maxima of x its producer, the gate/up GEMM, wrote)
+    also quads_nvfp4_quantize_partials, the dynamic scale in one pass.  Warm:
     `reps` calls on the same input.  Cold: the calls cycle through copies of
     the input spaced at least 512 MiB apart (each call's input was last read
     before 512 MiB of other inputs), back to back.  Calls go straight to the C
@@ -763,6 +774,17 @@ def quantizer_rate(np, torch, Q, x, reps=20):
         it = iter(range(10 ** 9))
         out[name + "_cold"] = rate(_back_to_back_us(
             torch, lambda: call(xs[next(it) % ncopy], ts_in), ncopy * max(2, reps // ncopy)))
+    if part is not None:
+        def call_p(xi):
+            st = lib.quads_nvfp4_quantize_partials(P(xi), m, k, P(part), int(part.numel()),
+                                                   P(nib), P(sc), P(ts), stream)
+            if st != 0:
+                raise RuntimeError(f"quads_nvfp4_quantize_partials failed with status {st}")
+        call_p(x)
+        out["producer_partials"] = rate(_back_to_back_us(torch, lambda: call_p(x), reps))
+        it = iter(range(10 ** 9))
+        out["producer_partials_cold"] = rate(_back_to_back_us(
+            torch, lambda: call_p(xs[next(it) % ncopy]), ncopy * max(2, reps // ncopy)))
     y = torch.empty_like(x)
     out["device_copy"] = rate(_back_to_back_us(torch, lambda: y.copy_(x), reps), 4.0 * m * k)
     it = iter(range(10 ** 9))
@@ -816,7 +838,7 @@ def config5(np, torch, Q, d5, x, dev, reps=5):
     quantization (quads_nvfp4_quantize for k = 0, else quads_rac_quantize)
     and the gate/up GEMM with the SwiGLU bf16 epilogue, each timed back to
     back.  Returns the figures and the k = 64 SwiGLU output (the down site's
-    input, [131072, 1536] bf16)."""
+    input, [131072, 1536] bf16) with the GEMM's partial maxima of it."""
     E, H, I = 64, 4096, 1536
     ids = torch.from_numpy(d5["topk_ids"]).to(dev)
     gen = torch.Generator(device=dev)
@@ -842,10 +864,12 @@ def config5(np, torch, Q, d5, x, dev, reps=5):
         else:
             av, rv, sel = a, None, None
 
+        buf = torch.zeros(Q.quads_moe_w4a4_gemm_amax_groups(rows, H, k, E, 2 * I),
+                          dtype=torch.int32, device=dev)
+
         def gemm():
-            keep["h"] = Q.quads_moe_w4a4_gemm(av, w13q, 2 * I, rows=rows, r=rv, sel=sel,
-                                              offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
-                                              out_dtype=Q.OUT_BF16)
+            keep["h"] = Q.quads_moe_w4a4_gemm_amax(av, w13q, 2 * I, rows=rows, r=rv, sel=sel,
+                                                   offsets=off, row_token=rt, amax_part=buf)
         us = _back_to_back_us(torch, gemm, reps)
         fl = 2.0 * rows * 2 * I * (H + k)
         qb = 2.5625 * x.shape[0] * H + 0.5625 * x.shape[0] * k
@@ -882,6 +906,8 @@ def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
     I = N13 // 2
     rows = T * TOPK
     keep = {}
+    amax_buf = torch.zeros(Q.quads_moe_w4a4_gemm_amax_groups(rows, H, KR, E, N13),
+                           dtype=torch.int32, device=dev)
 
     def layer(evs=None):
         def mark(i):
@@ -892,12 +918,12 @@ def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
         mark(1)
         off, rt, pos = Q.quads_moe_pack(ids, E)
         mark(2)
-        h = Q.quads_moe_w4a4_gemm((a["nib"], a["scale"], a["ts"]), w13q, N13, rows=rows,
-                                  r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"],
-                                  offsets=off, row_token=rt, epilogue=Q.EPI_SWIGLU,
-                                  out_dtype=Q.OUT_BF16)
+        h, hmax = Q.quads_moe_w4a4_gemm_amax((a["nib"], a["scale"], a["ts"]), w13q, N13,
+                                             rows=rows, r=(a["r_nib"], a["r_scale"], a["r_ts"]),
+                                             sel=a["sel"], offsets=off, row_token=rt,
+                                             amax_part=amax_buf)
         mark(3)
-        b = Q.quads_rac_quantize(h, KR)
+        b = Q.quads_rac_quantize_partials(h, KR, hmax)
         mark(4)
         y2 = Q.quads_moe_w4a4_gemm((b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
                                    r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"],
@@ -934,10 +960,10 @@ def decode_layer(np, torch, Q, synth, dev, w13q, w2q, reps=50):
     # each GEMM alone, back to back on the last layer's inputs (no event
     # between launches): its rate on the active experts' weight bytes
     gemms = {
-        "gemm_gate_up_swiglu": (wb_gu, lambda: Q.quads_moe_w4a4_gemm(
+        "gemm_gate_up_swiglu": (wb_gu, lambda: Q.quads_moe_w4a4_gemm_amax(
             (a["nib"], a["scale"], a["ts"]), w13q, N13, rows=rows,
             r=(a["r_nib"], a["r_scale"], a["r_ts"]), sel=a["sel"], offsets=off, row_token=rt,
-            epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)),
+            amax_part=amax_buf)),
         "gemm_down": (wb_dn, lambda: Q.quads_moe_w4a4_gemm(
             (b["nib"], b["scale"], b["ts"]), w2q, H, rows=rows,
             r=(b["r_nib"], b["r_scale"], b["r_ts"]), sel=b["sel"], offsets=off,

@@ -92,10 +92,11 @@ int quads_nvfp4_quantize(const uint16_t* x, int64_t M, int64_t K, const float* t
  * a producer's partial maxima of |x| instead of a max pass over x (one pass
  * over x instead of two), e.g. the ones quads_moe_w4a4_gemm_amax writes for
  * its SwiGLU output.
- *   amax_part  uint32 [groups], groups >= 1: bf16 magnitude bit patterns
- *              (|x| as bf16 bits & 0x7FFF) whose maximum is that of every
- *              element of x; nib, scale and ts_out are then those of
- *              quads_nvfp4_quantize(ts_in = NULL) bit for bit
+ *   amax_part  uint32 [groups] (4-byte aligned), groups >= 1: bf16
+ *              magnitude bit patterns (|x| as bf16 bits & 0x7FFF) whose
+ *              maximum is that of every element of x; nib, scale and ts_out
+ *              are then those of quads_nvfp4_quantize(ts_in = NULL) bit for
+ *              bit
  * No workspace.  M == 0 writes ts_out = 0.
  */
 int quads_nvfp4_quantize_partials(const uint16_t* x, int64_t M, int64_t K,
@@ -279,7 +280,7 @@ int quads_moe_w4a4_gemm(const uint8_t* a_nib, const uint8_t* a_scale, const floa
  * written 0.  The maximum over amax_part[0 .. amax_groups) is then
  * max |h| exactly; pass (amax_part, amax_groups) to
  * quads_nvfp4_quantize_partials or quads_rac_quantize_partials.
- *   amax_part    out uint32 [amax_groups], amax_groups >= the value of
+ *   amax_part    out uint32 [amax_groups] (4-byte aligned), amax_groups >=
  *                quads_moe_w4a4_gemm_amax_groups for the call's sizes
  *                (QUADS_EWORKSPACE if smaller)
  *   every other argument, the workspace and the error bound as in

@@ -346,6 +346,8 @@ int set_hip_error(hipError_t e);
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 inline bool ok_ptr(const void* p) { return p != nullptr && aligned16(p); }
 inline bool ok_opt_ptr(const void* p) { return p == nullptr || aligned16(p); }
+// Arrays read and written one 32-bit word at a time.
+inline bool ok_ptr4(const void* p) { return p != nullptr && ((uintptr_t)p & 3u) == 0; }
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 

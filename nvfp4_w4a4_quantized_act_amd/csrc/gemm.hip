@@ -821,7 +821,7 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
         return QUADS_EINVAL;
     const size_t need = quads_moe_w4a4_gemm_ws(rows, K, k, E, N);
     if (ws_bytes < need || (need > 0 && !ok_ptr(ws))) return QUADS_EWORKSPACE;
-    if (amax != nullptr && (epilogue != QUADS_EPI_SWIGLU || !ok_ptr(amax) || amax_groups < 1))
+    if (amax != nullptr && (epilogue != QUADS_EPI_SWIGLU || !ok_ptr4(amax) || amax_groups < 1))
         return QUADS_EINVAL;
     if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
@@ -892,7 +892,7 @@ extern "C" int quads_moe_w4a4_gemm_amax(const uint8_t* a_nib, const uint8_t* a_s
                                         int64_t N, void* out, uint32_t* amax_part,
                                         int64_t amax_groups, void* ws, size_t ws_bytes,
                                         void* stream) {
-    if (!ok_ptr(amax_part)) return QUADS_EINVAL;
+    if (!ok_ptr4(amax_part)) return QUADS_EINVAL;
     return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 0, row_token, rows, K, r_nib, r_scale, r_ts,
                      sel, k, w_nib, w_scale, w_ts, offsets, E, N, QUADS_EPI_SWIGLU,
                      QUADS_OUT_BF16, out, amax_part, amax_groups, ws, ws_bytes, stream);

@@ -385,7 +385,7 @@ extern "C" int quads_nvfp4_quantize_partials(const uint16_t* x, int64_t M, int64
                                              void* stream) {
     if (M < 0 || K <= 0 || K % kBlock) return QUADS_ESHAPE;
     if (groups < 1 || groups >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
-    if (!ok_ptr(ts_out) || !ok_ptr(amax_part)) return QUADS_EINVAL;
+    if (!ok_ptr(ts_out) || !ok_ptr4(amax_part)) return QUADS_EINVAL;
     if (M > 0 && (!ok_ptr(x) || !ok_ptr(nib) || !ok_ptr(scale))) return QUADS_EINVAL;
     hipStream_t s = (hipStream_t)stream;
     if (M == 0) {

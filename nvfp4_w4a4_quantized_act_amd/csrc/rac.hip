@@ -1076,7 +1076,7 @@ extern "C" int quads_rac_quantize_partials(const uint16_t* x, int64_t M, int64_t
                                   score_out);
     if (st != QUADS_OK) return st;
     if (groups < 1 || groups >= ((int64_t)1 << 31)) return QUADS_ESHAPE;
-    if (!ok_ptr(amax_part)) return QUADS_EINVAL;
+    if (!ok_ptr4(amax_part)) return QUADS_EINVAL;
     if (ws_bytes < quads_rac_quantize_ws(M, K, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
     return rac_run(x, M, K, k, nib, scale, ts, sel, r_nib, r_scale, r_ts, score_out, ws,
                    (hipStream_t)stream, amax_part, groups);

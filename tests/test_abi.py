@@ -35,6 +35,7 @@ def test_status_strings():
 
 FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced (checks fail first)
 MIS = ctypes.c_void_p(0x10004)           # misaligned
+MIS2 = ctypes.c_void_p(0x10002)          # misaligned for a 32-bit word
 
 
 def test_quantize_validation():
@@ -189,7 +190,7 @@ def test_gemm_amax_slots():
         return g(FAKE, FAKE, FAKE, None, 512, 2048, FAKE, FAKE, FAKE, FAKE, k, FAKE, FAKE, FAKE,
                  FAKE, 128, 1536, FAKE, amax, groups, FAKE, ws, None)
     assert call(amax=None) == -1
-    assert call(amax=MIS) == -1
+    assert call(amax=MIS2) == -1
     assert call(groups=0) == -1
     assert call(groups=1631) == -3                        # fewer slots than work-groups
     assert call(k=8) == -2
@@ -200,7 +201,7 @@ def test_partials_validation():
     f = lib.quads_nvfp4_quantize_partials
     assert f(FAKE, 4, 32, FAKE, 0, FAKE, FAKE, FAKE, None) == -2           # groups >= 1
     assert f(FAKE, 4, 30, FAKE, 8, FAKE, FAKE, FAKE, None) == -2           # K % 16
-    assert f(FAKE, 4, 32, MIS, 8, FAKE, FAKE, FAKE, None) == -1
+    assert f(FAKE, 4, 32, MIS2, 8, FAKE, FAKE, FAKE, None) == -1
     assert f(FAKE, 4, 32, None, 8, FAKE, FAKE, FAKE, None) == -1
     g = lib.quads_rac_quantize_partials
     ws = lib.quads_rac_quantize_ws(64, 256, 16)

@@ -5,7 +5,9 @@ hidden 2048, intermediate 768, k = 64) runs as a whole layer, stage by stage,
 through the same calls and launch configuration the benchmark times: RAC(x)
 bit-exact, pack bit-exact, the gate/up GEMM with the SwiGLU bf16 epilogue,
 RAC(h) bit-exact on the GPU's h, the down GEMM with bf16 output, combine.
-All 128 experts carry NVFP4 weights; 16 sampled experts (the 8 tallest, all
+The gate/up GEMM is the form that also writes the partial maxima of |h|, and
+RAC(h) takes max|h| from them, as the benchmark runs it.  All 128 experts
+carry NVFP4 weights; 16 sampled experts (the 8 tallest, all
 above 256 rows so each spans two row tiles, the 4 shortest and 4 from the
 middle) are checked row by row against the oracle, and every other expert on
 its first and last packed row.
@@ -149,8 +151,8 @@ def test_config4_decode_layer(Q):
     a, r, sel = _ops(e, K)
     y1 = Q.quads_moe_w4a4_gemm(a, w13_t, 2 * I, rows=rows, r=r, sel=sel, offsets=_t(off),
                                row_token=_t(rt))
-    h = Q.quads_moe_w4a4_gemm(a, w13_t, 2 * I, rows=rows, r=r, sel=sel, offsets=_t(off),
-                              row_token=_t(rt), epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+    h, hmax = Q.quads_moe_w4a4_gemm_amax(a, w13_t, 2 * I, rows=rows, r=r, sel=sel,
+                                         offsets=_t(off), row_token=_t(rt))
     torch.cuda.synchronize()
     y1 = y1.cpu().numpy()
     _check_rows(y1, e, K, w13, off, rt, experts)
@@ -161,7 +163,7 @@ def test_config4_decode_layer(Q):
 
     print("config4: rac(h)", flush=True)
     hb = _np_bits(h)
-    gh = Q.quads_rac_quantize(h, K)
+    gh = Q.quads_rac_quantize_partials(h, K, hmax)       # max|h| from the GEMM's maxima
     eh = OR.rac_quantize(F.bf16_to_f64(hb), K)
     torch.cuda.synchronize()
     _assert_rac_equal(gh, eh)
@@ -249,8 +251,8 @@ def test_config3_layer(Q):
     a, r, sel = _ops(e, K)
     y1 = Q.quads_moe_w4a4_gemm(a, w13_t, 2 * I, rows=rows, r=r, sel=sel, offsets=_t(off),
                                row_token=_t(rt))
-    h = Q.quads_moe_w4a4_gemm(a, w13_t, 2 * I, rows=rows, r=r, sel=sel, offsets=_t(off),
-                              row_token=_t(rt), epilogue=Q.EPI_SWIGLU, out_dtype=Q.OUT_BF16)
+    h, hmax = Q.quads_moe_w4a4_gemm_amax(a, w13_t, 2 * I, rows=rows, r=r, sel=sel,
+                                         offsets=_t(off), row_token=_t(rt))
     torch.cuda.synchronize()
     y1 = y1.cpu().numpy()
     _check_expert_rows(y1, e, K, w13, off, rt, experts)
@@ -264,7 +266,7 @@ def test_config3_layer(Q):
 
     print("config3: rac(h)", flush=True)
     hb = _np_bits(h)
-    gh = Q.quads_rac_quantize(h, K)
+    gh = Q.quads_rac_quantize_partials(h, K, hmax)       # max|h| from the GEMM's maxima
     eh = OR.rac_quantize(F.bf16_to_f64(hb), K)
     torch.cuda.synchronize()
     _assert_rac_equal(gh, eh)
