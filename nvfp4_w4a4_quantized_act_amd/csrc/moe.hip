@@ -2,10 +2,13 @@
 //
 // Packing is a stable counting sort of the T*topk (token, slot) pairs by
 // expert id.  Up to 4096 pairs and 512 experts: one work-group, one launch
-// (k_pack_small).  Otherwise three launches: per-chunk histograms, one
-// work-group that turns them into expert offsets and per-chunk bases, and a
-// scatter in which one wave walks its chunk 64 entries at a time, ranking
-// equal ids with ballots so that equal ids keep their flattened order.
+// (k_pack_small).  Up to 16384 per-chunk counts (e.g. 32768 pairs over 128
+// experts): per-chunk histograms, then a scatter whose work-groups each sum
+// the histograms into their own chunk's bases (k_pack_scatter_prefix).
+// Otherwise three launches: per-chunk histograms, one work-group that turns
+// them into expert offsets and per-chunk bases, and a scatter in which one
+// wave walks its chunk 64 entries at a time, ranking equal ids with ballots
+// so that equal ids keep their flattened order.
 //
 // Combine: out[t] = sum over slots (in order) of w[t, slot] * y[pos[t, slot]],
 // eight output features per thread, fp32 fused multiply-adds.
@@ -175,6 +178,146 @@ __global__ __launch_bounds__(64) void k_pack_scatter(const int32_t* __restrict__
     }
 }
 
+// Mid-size inputs (nchunks * E <= kPackPrefixMax counts, E % 4 == 0): the
+// scatter work-group of chunk c finds its experts' first packed rows itself
+// -- the column totals of the per-chunk counts, scanned over experts, plus
+// the counts of chunks before c -- so no scan launch runs between the count
+// and the scatter.  The counts come in with 16-byte loads, all of a
+// thread's in flight together, and are summed with LDS atomics; work-group 0
+// writes offsets.  Then wave 0 walks the chunk as k_pack_scatter does.
+constexpr int kPackPrefixMax = 16384;
+constexpr int kPackPrefixLoads = kPackPrefixMax / 4 / 256;     // 16 per thread
+
+__global__ __launch_bounds__(256) void k_pack_scatter_prefix(
+    const int32_t* __restrict__ ids, int64_t n, int topk, int E, int nchunks,
+    const int32_t* __restrict__ cnt, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ row_token, int32_t* __restrict__ pos) {
+    __shared__ int s_tot[kPackPrefixMax / 4];     // E <= nchunks * E / 4 here
+    __shared__ int s_next[kPackPrefixMax / 4];
+    __shared__ int s_wave[4];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int c = blockIdx.x;
+    for (int e = tid; e < E; e += 256) {
+        s_tot[e] = 0;
+        s_next[e] = 0;
+    }
+    const int nq = nchunks * E / 4;
+    uint4 v[kPackPrefixLoads];
+#pragma unroll
+    for (int u = 0; u < kPackPrefixLoads; ++u) {
+        const int q = tid + 256 * u;
+        v[u] = q < nq ? reinterpret_cast<const uint4*>(cnt)[q] : make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();
+    if (1024 % E == 0) {
+        // E divides the 1024 counts of a load round: the thread's four
+        // experts are the same in every round, so it sums in registers, the
+        // lanes holding the same experts add up by shuffles, and one lane per
+        // expert quad and wave adds into LDS
+        int tot[4] = {0, 0, 0, 0}, below[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int u = 0; u < kPackPrefixLoads; ++u) {
+            const int q = tid + 256 * u;
+            const int a[4] = {(int)v[u].x, (int)v[u].y, (int)v[u].z, (int)v[u].w};
+            const bool before = q < nq && 4 * q / E < c;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tot[i] += a[i];                            // zero past the counts
+                below[i] += before ? a[i] : 0;
+            }
+        }
+        for (int off = 32; off >= E / 4 && off > 0; off >>= 1) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                tot[i] += __shfl_xor(tot[i], off, 64);
+                below[i] += __shfl_xor(below[i], off, 64);
+            }
+        }
+        if (lane < E / 4 || E >= 256) {
+            const int e = (4 * tid) % E;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                if (tot[i]) atomicAdd(&s_tot[e + i], tot[i]);
+                if (below[i]) atomicAdd(&s_next[e + i], below[i]);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int u = 0; u < kPackPrefixLoads; ++u) {
+            const int q = tid + 256 * u;
+            if (q < nq) {
+                const int cc = 4 * q / E, e = 4 * q - cc * E;
+                const int a[4] = {(int)v[u].x, (int)v[u].y, (int)v[u].z, (int)v[u].w};
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    if (a[i] == 0) continue;
+                    atomicAdd(&s_tot[e + i], a[i]);
+                    if (cc < c) atomicAdd(&s_next[e + i], a[i]);
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // exclusive scan of the totals over experts: each thread a contiguous run
+    const int per = (E + 255) / 256;
+    const int e0 = tid * per, e1 = e0 + per < E ? e0 + per : E;
+    int local = 0;
+    for (int e = e0; e < e1; ++e) local += s_tot[e];
+    int x = local;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
+    }
+    if (lane == 63) s_wave[w] = x;
+    __syncthreads();
+    int run = x - local;
+    for (int q = 0; q < w; ++q) run += s_wave[q];
+    for (int e = e0; e < e1; ++e) {
+        const int t = s_tot[e];
+        if (c == 0) offsets[e] = run;
+        s_next[e] += run;
+        run += t;
+    }
+    if (c == 0 && tid == 0) offsets[E] = (int32_t)n;
+    __syncthreads();
+    if (w != 0) return;
+    int nbits = 0;
+    while ((1 << nbits) < E) ++nbits;
+    const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+    const int64_t c0 = (int64_t)c * kPackChunk;
+    int ev[kPackChunk / 64];                               // all ids of the chunk in flight
+#pragma unroll
+    for (int it = 0; it < kPackChunk / 64; ++it) {
+        const int64_t idx = c0 + it * 64 + lane;
+        ev[it] = idx < n ? ids[idx] : -1;
+    }
+#pragma unroll
+    for (int it = 0; it < kPackChunk / 64; ++it) {
+        const int64_t idx = c0 + it * 64 + lane;
+        int e = ev[it];
+        if (e < 0 || e >= E) e = -1;
+        uint64_t peers = __ballot(e >= 0);
+        for (int b = 0; b < nbits; ++b) {
+            const uint64_t m = __ballot(e >= 0 && ((e >> b) & 1));
+            peers &= (e >= 0 && ((e >> b) & 1)) ? m : ~m;
+        }
+        int rank = 0, p = 0;
+        if (e >= 0) {
+            rank = __popcll(peers & lt);
+            p = s_next[e] + rank;
+        }
+        // every lane has read its expert's next row before the first peer moves it
+        __builtin_amdgcn_wave_barrier();
+        if (e >= 0) {
+            row_token[p] = (int32_t)(idx / topk);
+            pos[idx] = p;
+            if (rank == 0) s_next[e] += __popcll(peers);
+        }
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 // Small inputs (n <= kPackOneMaxN entries, E <= kPackOneMaxE) in one
 // work-group of 16 waves and one launch.  Wave w owns the contiguous entries
 // [w S, w S + S) (S a multiple of 64, at most 4 steps of 64, all ids held in
@@ -337,6 +480,12 @@ extern "C" int quads_moe_pack(const int32_t* topk_ids, int64_t T, int32_t topk, 
     if (nchunks > 0) {
         hipLaunchKernelGGL(k_pack_count, dim3(nchunks), dim3(256), 0, s, topk_ids, n, (int)E, cnt);
         QUADS_CHECK_LAUNCH();
+    }
+    if (nchunks > 0 && (int64_t)nchunks * E <= kPackPrefixMax && E % 4 == 0) {
+        hipLaunchKernelGGL(k_pack_scatter_prefix, dim3(nchunks), dim3(256), 0, s, topk_ids, n,
+                           (int)topk, (int)E, nchunks, cnt, offsets, row_token, pos);
+        QUADS_CHECK_LAUNCH();
+        return QUADS_OK;
     }
     hipLaunchKernelGGL(k_pack_scan, dim3(1), dim3(1024), 0, s, cnt, nchunks, (int)E, n, offsets);
     QUADS_CHECK_LAUNCH();

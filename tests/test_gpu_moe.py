@@ -36,11 +36,15 @@ def test_pack_configs(Q, cfg):
 
 
 @pytest.mark.parametrize("t,e,topk", [(1, 1, 1), (3, 5, 2), (1000, 7, 3), (513, 4096, 8),
-                                      (2000, 1, 1), (512, 128, 8), (455, 300, 9), (513, 128, 8)])
+                                      (2000, 1, 1), (512, 128, 8), (455, 300, 9), (513, 128, 8),
+                                      (4000, 256, 4), (65536, 4, 2), (4100, 6, 2)])
 def test_pack_small_and_edge(Q, t, e, topk):
-    """Both packing paths: one work-group up to 4096 pairs and 512 experts
-    (512 x 8 is the largest such case, 455 x 9 has 300 experts), three
-    launches above (513 x 8; 4096 experts)."""
+    """Every packing path: one work-group up to 4096 pairs and 512 experts
+    (512 x 8 is the largest such case, 455 x 9 has 300 experts); the count
+    and the scatter that sums the counts itself for up to 16384 per-chunk
+    counts with E % 4 == 0 (513 x 8 over 128 experts with a ragged last
+    chunk, 4000 x 4 over 256, 65536 x 2 over 4 experts: 512 chunks); three
+    launches otherwise (4096 experts; 6 experts)."""
     rng = np.random.default_rng(t + e)
     ids = np.stack([rng.choice(e, topk, replace=False) for _ in range(t)]).astype(np.int32)
     _pack_check(Q, ids, e)
