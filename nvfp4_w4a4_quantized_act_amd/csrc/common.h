@@ -186,13 +186,38 @@ __device__ __forceinline__ uint32_t bf16_rne_from_f32(float f) {
 }
 
 // Wave64 reductions.
+// Maximum over the 64 lanes of a wave (every lane active), returned to all:
+// DPP moves within each row of 16 lanes (quad permutations, then rotations
+// by 4 and 8), then the four row maxima read as scalars -- no LDS round
+// trips, unlike lane shuffles.
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        uint32_t o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    uint32_t o;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);   // quad 1,0,3,2
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);   // quad 2,3,0,1
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x124, 0xF, 0xF, false);  // row_ror:4
+    v = o > v ? o : v;
+    o = (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x128, 0xF, 0xF, false);  // row_ror:8
+    v = o > v ? o : v;
+    const uint32_t a = __builtin_amdgcn_readlane(v, 15), b = __builtin_amdgcn_readlane(v, 31);
+    const uint32_t c = __builtin_amdgcn_readlane(v, 47), d = __builtin_amdgcn_readlane(v, 63);
+    const uint32_t ab = a > b ? a : b, cd = c > d ? c : d;
+    return ab > cd ? ab : cd;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (every lane active), by
+// DPP: shifts by 1, 2, 4 and 8 within each row of 16 lanes, then the last
+// lane of row 0 and 2 broadcast into rows 1 and 3, and of rows 0-1 into rows
+// 2 and 3.
+__device__ __forceinline__ int wave_incl_add(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);   // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);   // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);   // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);   // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);   // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);   // row_bcast:31
+    return x;
 }
 
 typedef unsigned short us2 __attribute__((ext_vector_type(2)));

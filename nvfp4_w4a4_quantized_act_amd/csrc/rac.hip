@@ -172,163 +172,179 @@ __global__ __launch_bounds__(256) void k_tree_level(const double* __restrict__ i
 }
 
 // ----------------------------------------------------------------- select --
-// Exclusive scan of one value per thread over a 1024-thread work-group.
-__device__ __forceinline__ int block_excl_scan_1024(int v, int* s_tmp, int* total) {
+// Exclusive scan of one value per thread over a work-group of kT threads
+// with one barrier: DPP wave scans, the wave totals through s_tmp[0 .. kT/64)
+// (its own buffer), and every wave adds up the totals before it itself.
+template <int kT>
+__device__ __forceinline__ int block_excl_scan_dpp(int v, int* s_tmp, int* total) {
+    constexpr int kW = kT / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
+    const int x = wave_incl_add(v);
     if (lane == 63) s_tmp[wid] = x;
     __syncthreads();
-    if (threadIdx.x < 16) {
-        int w = s_tmp[threadIdx.x];
-        int sum = w;
-        for (int off = 1; off < 16; off <<= 1) {
-            int y = __shfl_up(sum, off, 16);
-            if ((int)threadIdx.x >= off) sum += y;
-        }
-        s_tmp[16 + threadIdx.x] = sum - w;       // exclusive wave offsets
-        if (threadIdx.x == 15) s_tmp[32] = sum;
-    }
-    __syncthreads();
-    const int res = x - v + s_tmp[16 + wid];
-    *total = s_tmp[32];
-    __syncthreads();
-    return res;
+    const int w = lane < kW ? s_tmp[lane] : 0;
+    const int incl = wave_incl_add(w);                  // over the wave totals
+    *total = __builtin_amdgcn_readlane(incl, kW - 1);
+    const int before = wid > 0 ? __builtin_amdgcn_readlane(incl, wid - 1) : 0;
+    return x - v + before;
 }
 
-// Radix select of the k largest of K keys held in LDS (fp64 scores as bit
-// patterns; ties to the lower index), by a 1024-thread work-group: S into
-// sel (ascending), and the tensor scale of the gathered residual, from the
-// selected channels' maxima s_cmax, into *s_rts (LDS).
+// Radix select of the k largest of K keys (K <= 8192; fp64 scores as bit
+// patterns in LDS; ties to the lower index), by a work-group of kT threads: S
+// into sel (ascending), and the tensor scale of the gathered residual, from
+// the selected channels' maxima s_cmax, into *s_rts (LDS).
+//
+// Thread t holds keys t * per .. t * per + per - 1 in registers.  MSB-first
+// passes of 8-bit digits: the histogram of the digit among the keys under
+// the prefix chosen so far, then every wave reads the histogram and finds
+// the digit where the count from the top reaches the number still needed,
+// so the selection state stays in registers and a pass costs one barrier
+// (three histogram buffers in turn: a pass clears the next pass's buffer,
+// which every wave last read two passes ago, before the barrier it has
+// passed since).  It stops once every key under the chosen prefix is
+// needed (the selected set is then the keys whose prefix is greater plus
+// all keys with that prefix), or once all 64 bits are chosen.  Of the keys
+// equal to the prefix the first ones in index order are taken; when all of
+// them are needed (the usual case) one scan of the per-thread selection
+// counts places S, otherwise a scan of the equal keys comes first.  Scans
+// and wave reductions run on DPP moves and scalar lane reads: the
+// work-group's time is its chain of dependent steps.
+template <int kT>
 __device__ void select_keys(const unsigned long long* s_key, const uint32_t* s_cmax, int K, int k,
                             int32_t* __restrict__ sel, float* s_rts) {
-    __shared__ int s_hist[256];
-    __shared__ int s_tmp[40];
-    __shared__ unsigned long long s_prefix;
-    __shared__ int s_need;
-    __shared__ int s_done;
+    constexpr int kSelPer = kRacMaxK / kT;
+    constexpr int kW = kT / 64;
+    __shared__ int s_hist[3][256];
+    __shared__ int s_tmp[2][16];
     __shared__ uint32_t s_amax[16];
-    const int tid = threadIdx.x;
-    if (tid == 0) { s_prefix = 0ull; s_need = k; s_done = k == 0; }
-    __syncthreads();
-    // MSB-first radix select of the k-th largest key, 8 bits per pass.  It
-    // stops early once every key under the chosen prefix is needed: the
-    // selected set is then the keys whose prefix is greater, plus all keys
-    // with that prefix (the tie rule below takes all of them).
-    unsigned long long mask = 0ull;
-    for (int shift = 56; shift >= 0 && !s_done; shift -= 8) {
-        if (tid < 256) s_hist[tid] = 0;
-        __syncthreads();
-        const unsigned long long prefix = s_prefix;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int per = (K + kT - 1) / kT;
+    const int j0 = tid * per;
+    for (int i = tid; i < 256; i += kT) {
+        s_hist[0][i] = 0;
+        s_hist[1][i] = 0;
+    }
+    __syncthreads();                            // s_key (the caller's) and the histograms
+    unsigned long long key[kSelPer];
+#pragma unroll
+    for (int u = 0; u < kSelPer; ++u) key[u] = u < per && j0 + u < K ? s_key[j0 + u] : 0ull;
+    unsigned long long prefix = 0ull, mask = 0ull;
+    int need = k, eq = K, shift = 56, buf = 0;
+    bool done = k == 0;
+    while (!done) {                                            // uniform
         // histogram of the digit under the prefix.  The keys are scores of
-        // one tensor, so the first digits of most of them agree and plain LDS
-        // atomics would queue on one or two bins: lanes of a wave that share
-        // a bin add their count once (up to four distinct bins per wave),
-        // the rest one by one.
-        const int lane = tid & 63;
-        for (int j0 = 0; j0 < K; j0 += 1024) {
-            const int j = j0 + tid;
-            const unsigned long long key = j < K ? s_key[j] : 0ull;
-            const bool in = j < K && (key & mask) == prefix;
-            const int bin = (int)((key >> shift) & 0xFF);
-            unsigned long long pend = __ballot(in);
-            for (int it = 0; it < 4 && pend != 0ull; ++it) {
-                const int leader = __ffsll((long long)pend) - 1;
-                const int lb = __shfl(bin, leader, 64);
-                const unsigned long long same = __ballot(in && bin == lb) & pend;
-                if (lane == leader) atomicAdd(&s_hist[lb], __popcll(same));
-                pend &= ~same;
-            }
-            if ((pend >> lane) & 1ull) atomicAdd(&s_hist[bin], 1);
-        }
-        __syncthreads();
-        if (tid < 64) {
-            // lane l owns bins 255-4l .. 252-4l (descending); find the bin where
-            // the count from the top first reaches `need`
-            const int need = s_need;
-            int h[4], own = 0;
+        // one tensor, so in the first passes whole waves share one digit,
+        // and LDS atomics on one bin would queue: such a wave adds its count
+        // once; other waves add per lane.
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                h[q] = s_hist[255 - 4 * tid - q];
-                own += h[q];
-            }
-            int incl = own;                                   // inclusive scan over lanes
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const int y = __shfl_up(incl, off, 64);
-                if (tid >= off) incl += y;
-            }
-            const int above = incl - own;                     // count in higher bins
-            if (above < need && incl >= need) {               // exactly one lane
-                int rem = need - above, d = 255 - 4 * tid, hd = h[0];
-#pragma unroll
-                for (int q = 0; q < 3; ++q) {
-                    if (h[q] >= rem) { hd = h[q]; break; }
-                    rem -= h[q];
-                    --d;
-                    hd = h[q + 1];
+        for (int u = 0; u < kSelPer; ++u) {
+            if (u >= per) break;                               // uniform
+            const bool in = j0 + u < K && (key[u] & mask) == prefix;
+            const int bin = (int)((key[u] >> shift) & 0xFF);
+            const unsigned long long inb = __ballot(in);
+            if (inb != 0ull) {
+                const int leader = __ffsll((long long)inb) - 1;
+                const int lb = __builtin_amdgcn_readlane(bin, leader);
+                if (__ballot(in && bin == lb) == inb) {
+                    if (lane == leader) atomicAdd(&s_hist[buf][lb], __popcll(inb));
+                } else if (in) {
+                    atomicAdd(&s_hist[buf][bin], 1);
                 }
-                s_need = rem;
-                s_prefix = prefix | ((unsigned long long)d << shift);
-                s_done = hd == rem;
             }
         }
-        mask |= 0xFFull << shift;
+        for (int i = tid; i < 256; i += kT) s_hist[buf == 2 ? 0 : buf + 1][i] = 0;   // next
         __syncthreads();
+        // lane l owns bins 255-4l .. 252-4l (descending); the lane where the
+        // count from the top first reaches `need` finds the digit
+        int h[4], own = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            h[q] = s_hist[buf][255 - 4 * lane - q];
+            own += h[q];
+        }
+        const int incl = wave_incl_add(own);
+        const int above = incl - own;                         // count in higher bins
+        int rem = need - above, d = 255 - 4 * lane, hd = h[0];
+#pragma unroll
+        for (int q = 0; q < 3; ++q) {
+            if (h[q] >= rem) break;
+            rem -= h[q];
+            --d;
+            hd = h[q + 1];
+        }
+        const int src = __ffsll((long long)__ballot(above < need && incl >= need)) - 1;
+        rem = __builtin_amdgcn_readlane(rem, src);
+        d = __builtin_amdgcn_readlane(d, src);
+        hd = __builtin_amdgcn_readlane(hd, src);
+        need = rem;
+        eq = hd;
+        prefix |= (unsigned long long)d << shift;
+        mask |= 0xFFull << shift;
+        done = hd == rem || shift == 0;
+        shift -= 8;
+        buf = buf == 2 ? 0 : buf + 1;
     }
     // keys compare on the bits resolved so far (all 64 unless stopped early)
-    const unsigned long long thr = s_prefix;    // the k-th largest key (under mask)
-    const int need_ties = s_need;               // how many keys equal to thr to take
-    // ties at thr in index order: rank among equal keys via a chunked scan
-    const int per = (K + 1023) / 1024;
-    const int j0 = tid * per;
-    const int j1 = j0 + per < K ? j0 + per : K;
-    int n_eq = 0;
-    for (int j = j0; j < j1; ++j) n_eq += (s_key[j] & mask) == thr;
-    int total;
-    int eq_before = block_excl_scan_1024(n_eq, s_tmp, &total);
+    const unsigned long long thr = prefix;      // the k-th largest key (under mask)
+    const int need_ties = need;                 // how many keys equal to thr to take
+    const bool all_ties = need_ties == eq;      // uniform
+    int eq_before = 0, total;
+    if (!all_ties) {                            // rank the equal keys by index
+        int n_eq = 0;
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u)
+            n_eq += u < per && j0 + u < K && (key[u] & mask) == thr;
+        eq_before = block_excl_scan_dpp<kT>(n_eq, s_tmp[0], &total);
+    }
+    bool take[kSelPer];
     int n_sel = 0;
     {
         int e = eq_before;
-        for (int j = j0; j < j1; ++j) {
-            const unsigned long long key = s_key[j] & mask;
-            if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) ++n_sel;
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            const unsigned long long kv = key[u] & mask;
+            take[u] = k > 0 && u < per && j0 + u < K &&
+                      (kv > thr || (kv == thr && (all_ties || e < need_ties)));
+            if (u < per && j0 + u < K && kv == thr) ++e;
+            n_sel += take[u];
         }
     }
-    int sel_before = block_excl_scan_1024(n_sel, s_tmp, &total);
+    const int sel_before = block_excl_scan_dpp<kT>(n_sel, s_tmp[1], &total);
     uint32_t am = 0;
     {
-        int e = eq_before, o = sel_before;
-        for (int j = j0; j < j1; ++j) {
-            const unsigned long long key = s_key[j] & mask;
-            if (k > 0 && (key > thr || (key == thr && e++ < need_ties))) {
-                sel[o++] = j;
-                am = s_cmax[j] > am ? s_cmax[j] : am;
+        int o = sel_before;
+#pragma unroll
+        for (int u = 0; u < kSelPer; ++u) {
+            if (take[u]) {
+                sel[o++] = j0 + u;
+                am = s_cmax[j0 + u] > am ? s_cmax[j0 + u] : am;
             }
         }
     }
     am = wave_max_u32(am);
-    if ((tid & 63) == 0) s_amax[tid >> 6] = am;
+    if (lane == 0) s_amax[tid >> 6] = am;
     __syncthreads();
     if (tid == 0) {
         uint32_t m = 0;
-        for (int i = 0; i < 16; ++i) m = s_amax[i] > m ? s_amax[i] : m;
+        for (int i = 0; i < kW; ++i) m = s_amax[i] > m ? s_amax[i] : m;
         *s_rts = tensor_scale_from_amax(__uint_as_float(m));
     }
     __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ score,
-                                                     const uint32_t* __restrict__ colmax,
-                                                     int nrows, int K,
-                                                     int k, int32_t* __restrict__ sel,
-                                                     float* __restrict__ r_ts,
-                                                     double* __restrict__ score_out,
-                                                     uint32_t* __restrict__ r_table) {
+// Threads of the select kernel (measured at 2048 keys: four waves take
+// twice as long as sixteen, the per-thread share of the keys being the
+// longer chain).
+constexpr int kSelThreads = 1024;
+constexpr int kSelRowBatch = 4;            // partial rows loaded together
+
+__global__ __launch_bounds__(kSelThreads) void k_rac_select(const double* __restrict__ score,
+                                                            const uint32_t* __restrict__ colmax,
+                                                            int nrows, int K,
+                                                            int k, int32_t* __restrict__ sel,
+                                                            float* __restrict__ r_ts,
+                                                            double* __restrict__ score_out,
+                                                            uint32_t* __restrict__ r_table) {
     __shared__ unsigned long long s_key[kRacMaxK];
     __shared__ uint32_t s_cmax[kRacMaxK];          // per-channel max |r| over the rows
     __shared__ float s_rts;
@@ -343,20 +359,33 @@ __global__ __launch_bounds__(1024) void k_rac_select(const double* __restrict__ 
         r_table += b * 1024;
     }
     // the last level of the fixed-order tree: nrows (<= kSelectFold) partial
-    // rows summed in order from +0
-    for (int j = tid; j < K; j += 1024) {
+    // rows summed in order from +0, kSelRowBatch rows of a channel requested
+    // together
+    for (int j = tid; j < K; j += kSelThreads) {
         double v = 0.0;
         uint32_t cm = 0;
-        for (int r = 0; r < nrows; ++r) {
-            v = v + score[(int64_t)r * K + j];
-            const uint32_t c = colmax[(int64_t)r * K + j];
-            cm = c > cm ? c : cm;
+        for (int r0 = 0; r0 < nrows; r0 += kSelRowBatch) {
+            double sv[kSelRowBatch];
+            uint32_t cv[kSelRowBatch];
+#pragma unroll
+            for (int q = 0; q < kSelRowBatch; ++q) {
+                const int r = r0 + q < nrows ? r0 + q : nrows - 1;
+                sv[q] = score[(int64_t)r * K + j];
+                cv[q] = colmax[(int64_t)r * K + j];
+            }
+#pragma unroll
+            for (int q = 0; q < kSelRowBatch; ++q) {
+                if (r0 + q < nrows) {
+                    v = v + sv[q];
+                    cm = cv[q] > cm ? cv[q] : cm;
+                }
+            }
         }
         s_key[j] = (unsigned long long)__double_as_longlong(v);   // v >= +0: bits order
         s_cmax[j] = cm;
         if (score_out) score_out[j] = v;
     }
-    select_keys(s_key, s_cmax, K, k, sel, &s_rts);
+    select_keys<kSelThreads>(s_key, s_cmax, K, k, sel, &s_rts);
     if (tid == 0) r_ts[0] = s_rts;
     build_threshold_table(s_rts, reinterpret_cast<uint32_t(*)[8]>(r_table), false);
 }
@@ -523,7 +552,7 @@ __global__ __launch_bounds__(1024) void k_rac_small(
     __syncthreads();
 
     // 3. selection, the residual's tensor scale and code table
-    select_keys(s_key, s_cmax, K, k, sel, &s_rts);
+    select_keys<1024>(s_key, s_cmax, K, k, sel, &s_rts);
     const float s_tr = s_rts;
     if (tid == 0) r_ts[0] = s_tr;
     build_threshold_table(s_tr, s_tab, false);
@@ -1037,8 +1066,8 @@ static int rac_run(const uint16_t* x, int64_t M, int64_t K, int32_t k, uint8_t* 
         double* tp = pin; pin = pout; pout = tp;
         uint32_t* tc = cin; cin = cout; cout = tc;
     }
-    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)n, (int)K, (int)k,
-                       sel, r_ts, score_out, w.r_table);
+    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(kSelThreads), 0, s, pin, cin, (int)n, (int)K,
+                       (int)k, sel, r_ts, score_out, w.r_table);
     QUADS_CHECK_LAUNCH();
     if (k > 0) {
         const int64_t nel = M * (int64_t)k;
@@ -1211,7 +1240,7 @@ extern "C" int quads_rac_quantize_experts(const uint16_t* x, int64_t M, int64_t 
     hipLaunchKernelGGL(k_rac_expert_scores, dim3((unsigned)ctiles, (unsigned)E), dim3(256), 0, s,
                        w.part, w.pmax, w.chunk_start, (int)K, w.score, w.cmax);
     QUADS_CHECK_LAUNCH();
-    hipLaunchKernelGGL(k_rac_select, dim3((unsigned)E), dim3(1024), 0, s, w.score, w.cmax, 1,
+    hipLaunchKernelGGL(k_rac_select, dim3((unsigned)E), dim3(kSelThreads), 0, s, w.score, w.cmax, 1,
                        (int)K, (int)k, sel, r_ts, score_out, w.tables);
     QUADS_CHECK_LAUNCH();
     if (k > 0) {
@@ -1275,8 +1304,8 @@ extern "C" int quads_mx_rac_quantize(const uint16_t* x, int64_t M, int64_t K, in
         double* tp = pin; pin = pout; pout = tp;
         uint32_t* tc = cin; cin = cout; cout = tc;
     }
-    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(1024), 0, s, pin, cin, (int)n, (int)K, (int)k,
-                       sel, reinterpret_cast<float*>(w.partial), score_out, w.r_table);
+    hipLaunchKernelGGL(k_rac_select, dim3(1), dim3(kSelThreads), 0, s, pin, cin, (int)n, (int)K,
+                       (int)k, sel, reinterpret_cast<float*>(w.partial), score_out, w.r_table);
     QUADS_CHECK_LAUNCH();
     if (k > 0) {
         const int64_t threads = M * (int64_t)(k / 8);
