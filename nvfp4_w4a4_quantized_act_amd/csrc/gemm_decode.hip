@@ -211,12 +211,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_w4a4_decode(GemmArgs g) {
             const int n = decode_rows(g, g.offsets[x + 1] - g.offsets[x]);
             na += (n + kDecodeMaxRows - 1) / kDecodeMaxRows;
         }
-        int inc = na;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const int y = __shfl_up(inc, off, 64);
-            if (lane >= off) inc += y;
-        }
+        const int inc = wave_incl_add(na);
         if (rank >= __builtin_amdgcn_readlane(inc, 63)) {         // uniform: past the last
             if (g.amax) amax_group_none(g);
             return;

@@ -168,13 +168,10 @@ __device__ __forceinline__ int tile_height(int n, int bm, int* t_out) {
     return t > 0 ? ((n + t - 1) / t + 31) / 32 : 0;          // in 32-row blocks
 }
 
+// Inclusive prefix sum over the wave (every lane active).
 __device__ __forceinline__ int wave_scan(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    return x;
+    (void)lane;
+    return wave_incl_add(x);
 }
 
 // Rows of expert e the tiled kernel takes: none for an expert of at most
@@ -183,6 +180,8 @@ __device__ __forceinline__ int rows_of(const int32_t* offsets, int e, int skip, 
     const int n = offsets[e + 1] - offsets[e];
     return n > skip ? n - expert_tail(n, tail_rows) : 0;
 }
+
+constexpr int kTileCache = 4;    // experts per lane whose offsets the tile lookup keeps
 
 template <int BMT>
 __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, int64_t rows, int tile, int* e_out,
@@ -202,6 +201,56 @@ __device__ __forceinline__ bool find_tile_wave(const int32_t* offsets, int E, in
     int cnt[kH];                                  // this lane's tiles of each height
 #pragma unroll
     for (int q = 0; q < kH; ++q) cnt[q] = 0;
+    if (per <= kTileCache) {
+        // up to 256 experts: the lane's offsets loaded together once, and the
+        // tile found from registers
+        int o[kTileCache + 1], n[kTileCache];
+#pragma unroll
+        for (int u = 0; u <= kTileCache; ++u) o[u] = e0 + u <= e1 ? offsets[e0 + u] : 0;
+#pragma unroll
+        for (int u = 0; u < kTileCache; ++u) {
+            const int r = e0 + u < e1 ? o[u + 1] - o[u] : 0;
+            n[u] = r > skip ? r - expert_tail(r, tail_rows) : 0;
+            int t;
+            const int hgt = tile_height(n[u], BMT, &t);
+#pragma unroll
+            for (int q = 0; q < kH; ++q) cnt[q] += hgt == q + 1 ? t : 0;
+        }
+        int all = 0;
+#pragma unroll
+        for (int q = 0; q < kH; ++q) all += cnt[q];
+        if (tile >= __builtin_amdgcn_readlane(wave_incl_add(all), 63)) return false;
+        int base = 0;
+#pragma unroll
+        for (int q = kH - 1; q >= 0; --q) {
+            const int hgt = q + 1;
+            const int x = wave_incl_add(cnt[q]);
+            const int total = __builtin_amdgcn_readlane(x, 63);   // uniform: scalar branches
+            if (tile < base + total) {
+                int run = base + x - cnt[q], fe = -1, fm0 = 0, fme = 0;
+                if (tile >= run && tile < run + cnt[q]) {
+#pragma unroll
+                    for (int u = 0; u < kTileCache; ++u) {
+                        int t;
+                        if (fe >= 0 || tile_height(n[u], BMT, &t) != hgt) continue;
+                        if (tile < run + t) {
+                            fe = e0 + u;
+                            fm0 = o[u] + (tile - run) * hgt * 32;
+                            fme = fm0 + hgt * 32 < o[u] + n[u] ? fm0 + hgt * 32 : o[u] + n[u];
+                        }
+                        run += t;
+                    }
+                }
+                const int src = __ffsll(__ballot(fe >= 0)) - 1;
+                *e_out = __builtin_amdgcn_readlane(fe, src);
+                *m0_out = __builtin_amdgcn_readlane(fm0, src);
+                *mend_out = __builtin_amdgcn_readlane(fme, src);
+                return true;
+            }
+            base += total;
+        }
+        return false;
+    }
     for (int e = e0; e < e1; ++e) {
         int t;
         const int hgt = tile_height(rows_of(offsets, e, skip, tail_rows), BMT, &t);
