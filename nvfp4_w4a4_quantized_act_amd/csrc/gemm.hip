@@ -813,6 +813,7 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     if (E < 1 || E > kGemmMaxE || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
     if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
     if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (rows == 0) return QUADS_OK;                   // size 0: a no-op, whatever the pointers
     if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
     if (!ok_ptr(a_nib) || !ok_ptr(a_scale) || !ok_ptr(a_ts) || !ok_ptr(w_nib) ||
         !ok_ptr(w_scale) || !ok_ptr(w_ts) || !ok_ptr(out))
@@ -823,7 +824,6 @@ static int gemm_w4a4(const uint8_t* a_nib, const uint8_t* a_scale, const float* 
     if (ws_bytes < need || (need > 0 && !ok_ptr(ws))) return QUADS_EWORKSPACE;
     if (amax != nullptr && (epilogue != QUADS_EPI_SWIGLU || !ok_ptr4(amax) || amax_groups < 1))
         return QUADS_EINVAL;
-    if (rows == 0) return QUADS_OK;
     GemmArgs g{a_nib, a_scale, a_ts, row_token, rows, (int)K, r_nib, r_scale, r_ts, sel, (int)k,
                w_nib, w_scale, w_ts, offsets, (int)E, (int)N, epilogue,
                out_dtype == QUADS_OUT_BF16, out, 0, a_ts_rows, sel_per_expert};
@@ -892,7 +892,7 @@ extern "C" int quads_moe_w4a4_gemm_amax(const uint8_t* a_nib, const uint8_t* a_s
                                         int64_t N, void* out, uint32_t* amax_part,
                                         int64_t amax_groups, void* ws, size_t ws_bytes,
                                         void* stream) {
-    if (!ok_ptr4(amax_part)) return QUADS_EINVAL;
+    if (rows > 0 && !ok_ptr4(amax_part)) return QUADS_EINVAL;
     return gemm_w4a4(a_nib, a_scale, a_ts, nullptr, 0, row_token, rows, K, r_nib, r_scale, r_ts,
                      sel, k, w_nib, w_scale, w_ts, offsets, E, N, QUADS_EPI_SWIGLU,
                      QUADS_OUT_BF16, out, amax_part, amax_groups, ws, ws_bytes, stream);
@@ -905,7 +905,7 @@ extern "C" int quads_moe_w4a4_gemm_rowscale(const uint8_t* a_nib, const uint8_t*
                                             const int32_t* offsets, int32_t E, int64_t N,
                                             int epilogue, int out_dtype, void* out, void* ws,
                                             size_t ws_bytes, void* stream) {
-    if (!ok_ptr(a_ts_rows)) return QUADS_EINVAL;
+    if (rows > 0 && !ok_ptr(a_ts_rows)) return QUADS_EINVAL;
     return gemm_w4a4(a_nib, a_scale, a_ts_rows, a_ts_rows, 0, row_token, rows, K, nullptr, nullptr,
                      nullptr, nullptr, 0, w_nib, w_scale, w_ts, offsets, E, N, epilogue,
                      out_dtype, out, nullptr, 0, ws, ws_bytes, stream);

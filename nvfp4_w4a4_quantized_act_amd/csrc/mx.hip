@@ -435,11 +435,11 @@ extern "C" int quads_moe_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scale,
     if (E < 1 || E > 4096 || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
     if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
     if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (rows == 0) return QUADS_OK;                   // size 0: a no-op, whatever the pointers
     if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
     if (!ok_ptr(a_codes) || !ok_ptr(a_scale) || !ok_ptr(w_codes) || !ok_ptr(w_scale) ||
         !ok_ptr(out))
         return QUADS_EINVAL;
-    if (rows == 0) return QUADS_OK;
     mx::MxArgs g{a_codes, a_scale, row_token, rows, (int)K, w_codes, w_scale, offsets, (int)E,
                  (int)N, epilogue, out_dtype == QUADS_OUT_BF16, out};
     const int64_t nt_n = epilogue == QUADS_EPI_SWIGLU ? (N / 2 + mx::BN / 2 - 1) / (mx::BN / 2)
@@ -473,7 +473,8 @@ extern "C" int quads_moe_mx_rac_gemm(const uint8_t* a_codes, const uint8_t* a_sc
                                      int64_t N, int epilogue, int out_dtype, void* out, void* ws,
                                      size_t ws_bytes, void* stream) {
     if (k < 0 || k % 32 || k > K) return QUADS_ESHAPE;
-    if (k > 0 && (!ok_ptr(r_codes) || !ok_ptr(r_scale) || !ok_ptr(sel))) return QUADS_EINVAL;
+    if (rows > 0 && k > 0 && (!ok_ptr(r_codes) || !ok_ptr(r_scale) || !ok_ptr(sel)))
+        return QUADS_EINVAL;
     if (k == 0)
         return quads_moe_mx_gemm(a_codes, a_scale, row_token, rows, K, w_codes, w_scale, offsets,
                                  E, N, QUADS_MX_FP4, epilogue, out_dtype, out, stream);
@@ -485,12 +486,12 @@ extern "C" int quads_moe_mx_rac_gemm(const uint8_t* a_codes, const uint8_t* a_sc
     if (E < 1 || E > 4096 || N < 1 || N >= ((int64_t)1 << 30)) return QUADS_ESHAPE;
     if (epilogue == QUADS_EPI_SWIGLU && N % 2) return QUADS_ESHAPE;
     if (offsets == nullptr && E != 1) return QUADS_EINVAL;
+    if (rows == 0) return QUADS_OK;                   // size 0: a no-op, whatever the pointers
     if (!ok_opt_ptr(offsets) || !ok_opt_ptr(row_token)) return QUADS_EINVAL;
     if (!ok_ptr(a_codes) || !ok_ptr(a_scale) || !ok_ptr(w_codes) || !ok_ptr(w_scale) ||
         !ok_ptr(out))
         return QUADS_EINVAL;
     if (ws_bytes < quads_moe_mx_rac_gemm_ws(E, N, k) || !ok_ptr(ws)) return QUADS_EWORKSPACE;
-    if (rows == 0) return QUADS_OK;
     hipStream_t s = (hipStream_t)stream;
     const int64_t nrows = (int64_t)E * N, threads = nrows * (k / 8);
     hipLaunchKernelGGL(mx::k_mx_gather_wsel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,

@@ -167,6 +167,31 @@ def test_gemm_validation():
     assert call(out=MIS) == -1
 
 
+def test_empty_gemm_calls_are_no_ops():
+    """rows = 0 returns QUADS_OK before any row-sized pointer is looked at, as the
+    header promises for size-0 inputs (a size-0 torch tensor has a null data
+    pointer), on every grouped-GEMM entry point and the combine."""
+    lib = Q.lib()
+    n0 = None
+    assert lib.quads_moe_w4a4_gemm(n0, n0, n0, n0, 0, 256, n0, n0, n0, n0, 16, n0, n0, n0, n0,
+                                   1, 64, 0, 0, n0, n0, 0, n0) == 0
+    assert lib.quads_moe_w4a4_gemm_amax(n0, n0, n0, n0, 0, 256, n0, n0, n0, n0, 16, n0, n0, n0,
+                                        n0, 1, 64, n0, n0, 0, n0, 0, n0) == 0
+    assert lib.quads_moe_w4a4_gemm_rowscale(n0, n0, n0, n0, 0, 256, n0, n0, n0, n0, 1, 64, 0, 0,
+                                            n0, n0, 0, n0) == 0
+    assert lib.quads_moe_w4a4_gemm_sel_experts(n0, n0, n0, 0, 256, n0, n0, FAKE, n0, 16, n0, n0,
+                                               n0, FAKE, 4, 64, 0, 0, n0, n0, 0, n0) == 0
+    assert lib.quads_moe_mx_gemm(n0, n0, n0, 0, 256, n0, n0, n0, 1, 64, 0, 0, 0, n0, n0) == 0
+    assert lib.quads_moe_mx_rac_gemm(n0, n0, n0, 0, 256, n0, n0, n0, 32, n0, n0, n0, 1, 64, 0, 0,
+                                     n0, n0, 0, n0) == 0
+    assert lib.quads_moe_combine(n0, 0, n0, n0, 0, 8, 16, n0, n0) == 0
+    # the shape and enum checks still come first
+    assert lib.quads_moe_w4a4_gemm(n0, n0, n0, n0, 0, 250, n0, n0, n0, n0, 16, n0, n0, n0, n0,
+                                   1, 64, 0, 0, n0, n0, 0, n0) == -2
+    assert lib.quads_moe_w4a4_gemm(n0, n0, n0, n0, 0, 256, n0, n0, n0, n0, 16, n0, n0, n0, n0,
+                                   1, 64, 7, 0, n0, n0, 0, n0) == -1
+
+
 def test_gemm_amax_slots():
     """Slot count of the SwiGLU GEMM with partial maxima: the work-groups of its launches,
     worked out here from the launch rules (host logic only)."""

@@ -80,3 +80,28 @@ def test_combine(Q, bf16):
     bound = OM.combine(np.abs(y), OM.pack_routes(ids, 128)[2], np.abs(w), 512, 8)
     err = np.abs(out.cpu().numpy() - exp)
     assert np.all(err <= 8 * 2.0 ** -24 * bound + 1e-30)
+
+
+def test_empty_layer_calls(Q):
+    """Size-0 inputs through the bindings (null data pointers): a GEMM over no
+    rows, the SwiGLU GEMM with partial maxima, and a combine over no tokens
+    return empty outputs without error."""
+    dev = "cuda:0"
+    e, n, kd = 4, 64, 256
+    rng = np.random.default_rng(3)
+    w = (torch.from_numpy(rng.integers(0, 256, (e, n, kd // 2), dtype=np.uint8)).to(dev),
+         torch.from_numpy(rng.integers(40, 71, (e, n, kd // 16), dtype=np.uint8)).to(dev),
+         torch.full((e,), 2.0 ** -6, dtype=torch.float32, device=dev))
+    a = (torch.empty((0, kd // 2), dtype=torch.uint8, device=dev),
+         torch.empty((0, kd // 16), dtype=torch.uint8, device=dev),
+         torch.ones(1, dtype=torch.float32, device=dev))
+    off = torch.zeros(e + 1, dtype=torch.int32, device=dev)
+    rt = torch.empty(0, dtype=torch.int32, device=dev)
+    y = Q.quads_moe_w4a4_gemm(a, w, n, rows=0, offsets=off, row_token=rt)
+    h, part = Q.quads_moe_w4a4_gemm_amax(a, w, n, rows=0, offsets=off, row_token=rt)
+    out = Q.quads_moe_combine(torch.empty((0, n), dtype=torch.float32, device=dev),
+                              torch.empty((0, 2), dtype=torch.int32, device=dev),
+                              torch.empty((0, 2), dtype=torch.float32, device=dev))
+    torch.cuda.synchronize()
+    assert tuple(y.shape) == (0, n) and tuple(h.shape) == (0, n // 2)
+    assert tuple(out.shape) == (0, n)
