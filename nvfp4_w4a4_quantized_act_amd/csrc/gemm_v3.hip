@@ -726,32 +726,120 @@ bool gemm_v3_fits(const GemmArgs& g) {
 namespace v3 {
 
 // W[:, S] of every weight row as exact fp16 values (v * s_b: at most 6
-// significant bits, magnitude in [2^-10, 2688]), [E * N, k] row-major: a
-// thread writes 8 consecutive selected channels of one row.
+// significant bits, magnitude in [2^-10, 2688]), [E * N, k] row-major.  A
+// thread takes 8 consecutive selected channels (sel[j0 .. j0 + 7]) of
+// kGatherRows consecutive rows: the channel offsets are worked out once and
+// serve every row, whose loads are all issued before the first is used.  sel is strictly ascending, so when the 8 channels fit the
+// two 32-channel pieces starting at sel[j0]'s piece (always, once a quarter or
+// more of the channels are selected, bar clustered choices) a row costs two
+// 16-byte code loads and two 2-byte scale loads, the codes picked out of
+// registers; otherwise each channel's code byte and scale are read on their
+// own.  Both give the same values.
+constexpr int kGatherRows = 4;
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ uint32_t pick_word(const uint4& lo, const uint4& hi, int w) {
+    const uint4 q = w < 4 ? lo : hi;
+    const int i = w & 3;
+    return i == 0 ? q.x : (i == 1 ? q.y : (i == 2 ? q.z : q.w));
+}
+
+// two codes (bits 0-3, 4-7) and their two block scales (bits 0-7, 8-15) to
+// the two fp16 values code * scale
+__device__ __forceinline__ f16x2 dq_pair(uint32_t codes, uint32_t scales) {
+    const f16x2 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0);
+    const f16x2 s = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(scales, 1.0f, false);
+    return e * s;
+}
+
+// NR rows from row0 on, window case: every load of the NR rows is issued
+// before the first value is formed, so they are in flight together
+template <int NR>
+__device__ __forceinline__ void gather_window_rows(const uint8_t* __restrict__ w_nib,
+                                                   const uint8_t* __restrict__ w_scale,
+                                                   const int (&c)[8], int base, bool two, int K,
+                                                   int k, int j0, int64_t row0,
+                                                   _Float16* __restrict__ out) {
+    uint4 lo[NR], hi[NR];
+    uint32_t sc[NR];
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        const uint8_t* nrow = w_nib + (row0 + r) * (K / 2) + base / 2;
+        const uint8_t* srow = w_scale + (row0 + r) * (K / kBlock) + base / kBlock;
+        lo[r] = *reinterpret_cast<const uint4*>(nrow);
+        hi[r] = make_uint4(0u, 0u, 0u, 0u);
+        sc[r] = *reinterpret_cast<const uint16_t*>(srow);
+        if (two) {
+            hi[r] = *reinterpret_cast<const uint4*>(nrow + 16);
+            sc[r] |= (uint32_t)*reinterpret_cast<const uint16_t*>(srow + 2) << 16;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+        f16x2 v[4];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+            const int oa = c[2 * p] - base, ob = c[2 * p + 1] - base;
+            const uint32_t ca = (pick_word(lo[r], hi[r], oa >> 3) >> (4 * (oa & 7))) & 15u;
+            const uint32_t cb = (pick_word(lo[r], hi[r], ob >> 3) >> (4 * (ob & 7))) & 15u;
+            const uint32_t sa8 = (sc[r] >> (8 * (oa >> 4))) & 255u;
+            const uint32_t sb8 = (sc[r] >> (8 * (ob >> 4))) & 255u;
+            v[p] = dq_pair(ca | (cb << 4), sa8 | (sb8 << 8));
+        }
+        *reinterpret_cast<f16x8*>(out + (row0 + r) * k + j0) =
+            (f16x8){v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+    }
+}
+
 __global__ __launch_bounds__(256) void k_gather_wsel(const uint8_t* __restrict__ w_nib,
                                                      const uint8_t* __restrict__ w_scale,
                                                      const int32_t* __restrict__ sel, int K, int k,
                                                      int64_t nrows, _Float16* __restrict__ out) {
-    const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    const int per_row = k / 8;
-    if (t >= nrows * per_row) return;
-    const int64_t row = t / per_row;
-    const int j0 = (int)(t - row * per_row) * 8;
-    const uint8_t* nrow = w_nib + row * (K / 2);
-    const uint8_t* srow = w_scale + row * (K / kBlock);
-    _Float16 v[8];
+    const uint32_t per_row = (uint32_t)(k / 8);
+    const uint32_t t = blockIdx.x * 256u + threadIdx.x;
+    const uint32_t groups = (uint32_t)((nrows + kGatherRows - 1) / kGatherRows);
+    if (t >= groups * per_row) return;
+    const uint32_t rg = t / per_row;
+    const int j0 = (int)(t - rg * per_row) * 8;
+    const int4 sa = *reinterpret_cast<const int4*>(sel + j0);
+    const int4 sb = *reinterpret_cast<const int4*>(sel + j0 + 4);
+    int c[8] = {sa.x, sa.y, sa.z, sa.w, sb.x, sb.y, sb.z, sb.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) c[i] = c[i] < 0 ? 0 : (c[i] >= K ? K - 1 : c[i]);  // bounds only
+    const int base = c[0] & ~31;
+    bool window = true, two = false;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        int c = sel[j0 + i];
-        c = c < 0 ? 0 : (c >= K ? K - 1 : c);                // bounds only: sel < K
-        const uint32_t code = (nrow[c >> 1] >> (4 * (c & 1))) & 15u;
-        const _Float16 e = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0)[0];
-        const _Float16 sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(srow[c / kBlock], 1.0f,
-                                                                     false)[0];
-        v[i] = e * sb;
+        window = window && c[i] >= base && c[i] - base < 64;
+        two = two || c[i] - base >= 32;  // the second piece then ends inside the row (K % 32 == 0)
     }
-    *reinterpret_cast<f16x8*>(out + row * k + j0) = (f16x8){v[0], v[1], v[2], v[3], v[4], v[5],
-                                                             v[6], v[7]};
+    const int64_t row0 = (int64_t)rg * kGatherRows;
+    const int nr = (int)(nrows - row0 < kGatherRows ? nrows - row0 : kGatherRows);
+    if (window) {
+        if (nr == kGatherRows)
+            gather_window_rows<kGatherRows>(w_nib, w_scale, c, base, two, K, k, j0, row0, out);
+        else
+            for (int r = 0; r < nr; ++r)
+                gather_window_rows<1>(w_nib, w_scale, c, base, two, K, k, j0, row0 + r, out);
+    } else {
+        for (int r = 0; r < nr; ++r) {
+            const int64_t row = row0 + r;
+            const uint8_t* nrow = w_nib + row * (K / 2);
+            const uint8_t* srow = w_scale + row * (K / kBlock);
+            f16x2 v[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const int ca = c[2 * p], cb = c[2 * p + 1];
+                const uint32_t na = (nrow[ca >> 1] >> (4 * (ca & 1))) & 15u;
+                const uint32_t nb = (nrow[cb >> 1] >> (4 * (cb & 1))) & 15u;
+                v[p] = dq_pair(na | (nb << 4),
+                               (uint32_t)srow[ca / kBlock] | ((uint32_t)srow[cb / kBlock] << 8));
+            }
+            *reinterpret_cast<f16x8*>(out + row * k + j0) =
+                (f16x8){v[0][0], v[0][1], v[1][0], v[1][1], v[2][0], v[2][1], v[3][0], v[3][1]};
+        }
+    }
 }
 
 template <bool kGather>
@@ -789,7 +877,8 @@ int launch_gemm_v3(GemmArgs g, hipStream_t st, LaunchPlan* lp) {
 size_t gemm_v3_gather_ws(int64_t K, int64_t k, int64_t E, int64_t N) {
     const bool shape = K % v3::BK == 0 && K <= v3::BK * v3::kMaxChunksV3 && k > kCapMaxV3 &&
                        k % v3::BK == 0 && k <= K && K + k > kSingleChainMax &&
-                       N * K / 2 < ((int64_t)1 << 31) && E > 0 && N > 0;
+                       N * K / 2 < ((int64_t)1 << 31) && E > 0 && N > 0 &&
+                       (E * N + 3) / 4 * (k / 8) < ((int64_t)1 << 31);  // gather's thread index
     return shape ? align_up((size_t)E * (size_t)N * (size_t)k * 2, 256) : 0;
 }
 
@@ -800,7 +889,8 @@ bool gemm_v3_gather_fits(const GemmArgs& g) {
 
 int launch_gemm_v3_gather(GemmArgs g, void* ws, hipStream_t st, LaunchPlan* lp) {
     const int64_t nrows = (int64_t)g.E * g.N;
-    const int64_t threads = nrows * (g.k / 8);
+    const int64_t threads = (nrows + v3::kGatherRows - 1) / v3::kGatherRows * (g.k / 8);
+    if (threads >= ((int64_t)1 << 31)) return QUADS_EINVAL;  // 32-bit thread index
     if (lp->dry) return v3::launch_tiles<true>(g, st, lp);
     hipLaunchKernelGGL(v3::k_gather_wsel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st,
                        g.w_nib, g.w_scale, g.sel, g.K, g.k, nrows, static_cast<_Float16*>(ws));
