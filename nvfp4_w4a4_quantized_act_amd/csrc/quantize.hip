@@ -81,7 +81,11 @@ __global__ __launch_bounds__(128) void k_scale_finalize(const uint32_t* __restri
                           true);
 }
 
-constexpr int kQuantUnroll = 4;                 // half-blocks per batch per lane (two batches in flight)
+// half-blocks per batch per lane (two batches in flight).  Given-scale pass,
+// us at 16384 x 4096 / 131072 x 1536, grid at the resident count: 1: 33.6 /
+// 90.2, 2: 33.0 / 88.1, 3: 34.7 / 91.4, 4: 35.7 / 94.3, 8: 35.4 / 91.6; at 2,
+// half or a quarter of that grid is slower
+constexpr int kQuantUnroll = 2;
 
 // Half-block h (8 elements) of a segment, the other half on the neighbouring
 // lane (h ^ 1): block maximum by one shuffle, then codes (4 bytes), the
